@@ -1,0 +1,212 @@
+/*
+ * spec.h -- C ABI of libspec, an MI355X (gfx950) library for the hot path of
+ * speculative decoding: one target forward pass over K+1 positions with the
+ * weights streamed from HBM once, followed by the accept/reject rule, fed by
+ * a draft-model loop.  All device work is hand-written HIP.
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [zh]  "在神諭塔當見習抄寫刺蝟…：推測解碼入門" (gu-log Lv-19, zh-tw)
+ *   [en]  "Apprentice Scribe Hedgehog at the Oracle Tower … Speculative
+ *          Decoding 101" (gu-log Lv-19, English)
+ *   [int] "Speculative decoding internals" (tarrragon LLM notes, module 3)
+ *
+ * General conventions
+ *   Return codes: every call returns SPEC_OK (0) or a negative SPEC_ERR_*.
+ *   Argument errors are detected synchronously, before anything is enqueued.
+ *   Device work is enqueued on the context's stream and the call returns
+ *   without waiting; outputs are valid once that stream has drained
+ *   (spec_sync, or any later call that synchronises).  A failed HIP call is
+ *   reported as SPEC_ERR_HIP with its text in spec_last_error().
+ *   No C++ exception crosses this interface.
+ *
+ *   Pointers: every *_dev argument is device memory owned by the caller; it
+ *   must stay valid until the work that uses it has run.  The context owns
+ *   the packed weights, KV caches, workspaces and graphs it creates.
+ *   Host pointers are read before the call returns.
+ *
+ *   Layouts are row-major.  Token ids are int32 in [0, vocab).  Probability
+ *   rows are fp32.  Weights are bf16, [out_features][in_features], stacked
+ *   over layers.
+ *
+ *   Threading: one context per stream; a context is not thread-safe.
+ *   Determinism: results depend only on weights, prompt, K and seed; device
+ *   reductions use fixed orders (no floating-point atomics).
+ */
+#ifndef SPEC_H
+#define SPEC_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_OK 0
+#define SPEC_ERR_ARG (-1)        /* null pointer, bad size, unsupported shape */
+#define SPEC_ERR_CAPACITY (-2)   /* a pass would write beyond max_seq */
+#define SPEC_ERR_STATE (-3)      /* call out of order (e.g. commit with no verify) */
+#define SPEC_ERR_OOM (-4)        /* device allocation failed */
+#define SPEC_ERR_HIP (-5)        /* HIP runtime error; text in spec_last_error */
+
+/* Largest K (drafted tokens per round) the model path supports: K+1 rows of
+ * activations are carried as bf16 high and low halves in one 16-row MFMA
+ * tile. */
+#define SPEC_K_MAX 7
+/* Largest K of the stateless accept/reject entry point. */
+#define SPEC_AR_K_MAX 63
+
+/* A Llama-style decoder: pre-norm RMSNorm blocks with rotate-half RoPE,
+ * grouped-query causal attention and a SwiGLU feed-forward, final RMSNorm and
+ * an LM head; the next-token distribution at every position is the softmax
+ * of the logits at temperature 1 ([en] Floor 3: one pass scores every
+ * position).  The pages fix no architecture; this is the one the workloads
+ * name.
+ * Shape rules: d_model % 64 == 0, d_ffn % 32 == 0, vocab % 16 == 0,
+ * head_dim even, n_heads % n_kv_heads == 0, (n_heads*head_dim/2) % 8 == 0,
+ * (n_kv_heads*head_dim/2) % 8 == 0, head_dim <= 256,
+ * n_heads/n_kv_heads*(SPEC_K_MAX+1) <= 64. */
+typedef struct spec_model_desc {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rope_theta, rms_eps;
+  /* Device pointers to bf16 weights.  They are only read during spec_init
+   * (copied and repacked into context-owned memory); the caller may free
+   * them afterwards.  A draft whose embed or lm_head pointer equals the
+   * target's shares the target's packed copy. */
+  const void* embed;      /* [vocab][d_model] */
+  const void* attn_norm;  /* [n_layers][d_model] */
+  const void* wq;         /* [n_layers][n_heads*head_dim][d_model] */
+  const void* wk;         /* [n_layers][n_kv_heads*head_dim][d_model] */
+  const void* wv;         /* [n_layers][n_kv_heads*head_dim][d_model] */
+  const void* wo;         /* [n_layers][d_model][n_heads*head_dim] */
+  const void* ffn_norm;   /* [n_layers][d_model] */
+  const void* wg;         /* [n_layers][d_ffn][d_model] */
+  const void* wu;         /* [n_layers][d_ffn][d_model] */
+  const void* wd;         /* [n_layers][d_model][d_ffn] */
+  const void* final_norm; /* [d_model] */
+  const void* lm_head;    /* [vocab][d_model] */
+} spec_model_desc;
+
+typedef struct spec_init_params {
+  spec_model_desc target;
+  spec_model_desc draft;     /* must have target.vocab ([en] Floor 6: shared vocabulary) */
+  int32_t k_max;             /* 1..SPEC_K_MAX: largest K later calls may use */
+  int32_t max_seq;           /* token capacity of each KV cache (>= n_prompt + k_max + 1) */
+  int32_t greedy;            /* 1: greedy checking ([en] Floor 4); 0: sampling at T = 1 (Floor 5) */
+  int32_t use_graphs;        /* 1: replay draft/verify from captured hipGraphs; 0: plain launches */
+  int32_t profile_kernels;   /* 1: record hipEvents around every launch of the feed-forward
+                                gate/up GEMM (see spec_kernel_times) */
+  uint64_t stream_id;        /* Philox counter word c (0 in normal use) */
+  void* hip_stream;          /* hipStream_t to enqueue on; NULL: the context creates one */
+} spec_init_params;
+
+typedef struct spec_ctx spec_ctx;
+
+/* Creates a context: validates shapes, copies and packs the weights,
+ * allocates the paged KV caches (block size 16) and workspaces, and runs the
+ * prompt through both models.  prompt_host[0..n_prompt-2] is written into
+ * the caches; prompt_host[n_prompt-1] becomes the pending token (emitted but
+ * not yet in the target cache).  Synchronises before returning.
+ * Errors: SPEC_ERR_ARG (shapes, n_prompt < 1, token ids), SPEC_ERR_CAPACITY,
+ * SPEC_ERR_OOM, SPEC_ERR_HIP.  On error *out is NULL. */
+int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_prompt,
+              spec_ctx** out);
+
+/* Draft loop ([int] algorithm core, Step 1; [en] Floor 4 item 1): K
+ * autoregressive draft-model steps.  Step s feeds the tokens the draft cache
+ * lacks (the pending token, plus the last accepted draft after a round that
+ * accepted all K) or d_s, and ends with the draft's softmax row D_{s+1}
+ * written to D_dev[s] and its token d_{s+1} written to d_dev[s]: inverse CDF
+ * on the 2^-40 grid with Philox word w0 at that token's position (seed,
+ * stream_id), or the top token in greedy mode.
+ *   d_dev: int32 [K];  D_dev: fp32 [K][vocab].
+ * Errors: SPEC_ERR_ARG (K outside 1..k_max, null pointers), SPEC_ERR_CAPACITY,
+ * SPEC_ERR_STATE (the draft cache lags by more than 7 tokens). */
+int spec_draft(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev);
+
+/* Verify pass plus accept/reject ([int] algorithm core, Steps 2-4; [en]
+ * Floors 3-5).  One target pass over the K+1 rows [pending, d_1..d_K] at
+ * positions L..L+K gives T_1..T_{K+1}; their keys/values are appended to the
+ * target cache.  Then, sampling mode: draft i is accepted iff
+ * r_i * D_i(d_i) < T_i(d_i) (r_i from Philox word w1 at the draft's
+ * position); at the first reject the replacement is drawn from
+ * max(0, fix(T_i) - fix(D_i)) by inverse CDF with word w2 (falling back to
+ * T_i, then its argmax, if that residual is empty); if all K pass the bonus
+ * token is drawn from T_{K+1} with w2.  Greedy mode: a draft passes iff it is
+ * the lowest-index argmax of T_i; the first mismatch emits that argmax; the
+ * bonus is the argmax of T_{K+1}.  Drafts may come from any source: D rows
+ * are only read in sampling mode (one-hot rows describe a deterministic
+ * drafter).
+ *   d_dev: int32 [K]; D_dev: fp32 [K][vocab] (may be NULL in greedy mode);
+ *   out_dev: int32 [K+1] receives the n_acc+1 emitted tokens, -1 after them;
+ *   n_acc_dev: int32 [1] receives n_acc in 0..K, or -1 if an input that the
+ *   rule read was invalid (a probability outside [0,1] or non-finite, or a
+ *   draft id outside [0, vocab)) -- then out_dev is all -1;
+ *   T_dev (nullable): fp32 [K+1][vocab] receives the target rows;
+ *   logits_dev (nullable): fp32 [K+1][vocab] receives the target logits.
+ * Errors: SPEC_ERR_ARG, SPEC_ERR_CAPACITY (L+K+1 > max_seq), SPEC_ERR_STATE
+ * (a verify is already awaiting its commit). */
+int spec_verify(spec_ctx* ctx, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
+                int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev);
+
+/* Commit ([en] Floor 4: slips after a reject are torn up).  On the device:
+ * the emitted tokens are appended to the committed history, the target
+ * length advances by n_acc+1 (keys/values of the rejected rows stay in place
+ * and are overwritten later), the last emitted token becomes the pending one,
+ * and the draft length keeps only rows whose tokens were committed.  No host
+ * synchronisation.  out_dev / n_acc_dev are the buffers given to the
+ * preceding spec_verify (or equivalent values).  n_acc = -1 leaves the state
+ * unchanged.  Errors: SPEC_ERR_ARG, SPEC_ERR_STATE (no verify pending). */
+int spec_commit(spec_ctx* ctx, const int32_t* out_dev, const int32_t* n_acc_dev);
+
+/* Releases everything the context owns.  NULL is accepted. */
+int spec_destroy(spec_ctx* ctx);
+
+/* Text of the last failure on ctx (or of the last failed spec_init /
+ * stateless call on this thread when ctx is NULL).  Never NULL. */
+const char* spec_last_error(const spec_ctx* ctx);
+
+/* Waits for the context's stream. */
+int spec_sync(spec_ctx* ctx);
+
+/* The hipStream_t the context enqueues on. */
+void* spec_stream(const spec_ctx* ctx);
+
+typedef struct spec_state {
+  int32_t target_len;   /* tokens in the target KV cache (pending token at this position) */
+  int32_t draft_len;    /* tokens in the draft KV cache */
+  int32_t pending;      /* pending token id */
+  int32_t device_error; /* sticky device-side error bits (0 = none) */
+} spec_state;
+
+/* Synchronises and reads the device-side state. */
+int spec_get_state(spec_ctx* ctx, spec_state* out);
+
+/* Synchronises and copies committed tokens [0, n) (prompt included) to host. */
+int spec_get_history(spec_ctx* ctx, int32_t* host_out, int32_t n);
+
+/* With profile_kernels = 1: durations in ms of the feed-forward gate/up GEMM
+ * launches of the most recent spec_draft and spec_verify calls, in launch
+ * order (draft launches first).  Synchronises.  *n_out = count written. */
+int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out);
+
+/* Stateless accept/reject over a batch of independent sequences (the rule of
+ * spec_verify without the forward pass).
+ *   T_dev: fp32 [B][K+1][V]; D_dev: fp32 [B][K][V] (unused if greedy);
+ *   d_dev: int32 [B][K]; pos_dev: uint64 [B], position of d_1 of each
+ *   sequence; sequence b draws uniforms with counter (p, b, stream_id, 0);
+ *   out_dev: int32 [B][K+1]; n_acc_dev: int32 [B] (-1 marks invalid input,
+ *   as in spec_verify).
+ *   hip_stream: hipStream_t (NULL = default stream).
+ * Uses a library-owned workspace, allocated on first use and grown when a
+ * larger B*V arrives (that call allocates).  Calls that overlap on one device
+ * must not share it: serialise them on one stream.
+ * Errors: SPEC_ERR_ARG (B < 0, K outside 1..SPEC_AR_K_MAX, V < 1, null
+ * pointers), SPEC_ERR_OOM, SPEC_ERR_HIP. */
+int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_dev, int32_t B,
+                       int32_t K, int32_t V, uint64_t seed, const uint64_t* pos_dev,
+                       uint64_t stream_id, int32_t greedy, int32_t* out_dev, int32_t* n_acc_dev,
+                       void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_H */

@@ -264,9 +264,12 @@ class KV:
         self.model = model
 
     def __del__(self):
-        if getattr(self, "_h", None):
-            lib().orc_kv_free(self._h)
-            self._h = None
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            try:
+                _lib.orc_kv_free(h)
+            except Exception:  # interpreter shutdown
+                pass
 
 
 def forward(model: Model, kv: KV, tokens, pos0: int, want_logits: bool = True):

@@ -1,0 +1,210 @@
+"""ctypes binding of libspec (include/spec.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of libspec.so; torch is used only
+to own device memory (tensor.data_ptr()) and streams.  If the library is not
+built, importing the functions raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Mapping, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libspec.so")
+
+SPEC_OK = 0
+SPEC_ERR_ARG = -1
+SPEC_ERR_CAPACITY = -2
+SPEC_ERR_STATE = -3
+SPEC_ERR_OOM = -4
+SPEC_ERR_HIP = -5
+SPEC_K_MAX = 7
+SPEC_AR_K_MAX = 63
+
+_p = C.c_void_p
+_i32 = C.c_int32
+_u64 = C.c_uint64
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libspec error {code}: {msg}")
+        self.code = code
+
+
+class SpecModelDesc(C.Structure):
+    _fields_ = [
+        ("n_layers", _i32), ("d_model", _i32), ("n_heads", _i32), ("n_kv_heads", _i32),
+        ("head_dim", _i32), ("d_ffn", _i32), ("vocab", _i32),
+        ("rope_theta", C.c_float), ("rms_eps", C.c_float),
+        ("embed", _p), ("attn_norm", _p), ("wq", _p), ("wk", _p), ("wv", _p), ("wo", _p),
+        ("ffn_norm", _p), ("wg", _p), ("wu", _p), ("wd", _p), ("final_norm", _p), ("lm_head", _p),
+    ]
+
+
+class SpecInitParams(C.Structure):
+    _fields_ = [
+        ("target", SpecModelDesc), ("draft", SpecModelDesc),
+        ("k_max", _i32), ("max_seq", _i32), ("greedy", _i32), ("use_graphs", _i32),
+        ("profile_kernels", _i32), ("stream_id", _u64), ("hip_stream", _p),
+    ]
+
+
+class SpecState(C.Structure):
+    _fields_ = [("target_len", _i32), ("draft_len", _i32), ("pending", _i32),
+                ("device_error", _i32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBPATH):
+            raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() first")
+        L = C.CDLL(LIBPATH)
+        L.spec_init.argtypes = [C.POINTER(SpecInitParams), _p, _i32, C.POINTER(_p)]
+        L.spec_draft.argtypes = [_p, _i32, _u64, _p, _p]
+        L.spec_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
+        L.spec_commit.argtypes = [_p, _p, _p]
+        L.spec_destroy.argtypes = [_p]
+        L.spec_last_error.argtypes = [_p]
+        L.spec_last_error.restype = C.c_char_p
+        L.spec_sync.argtypes = [_p]
+        L.spec_stream.argtypes = [_p]
+        L.spec_stream.restype = _p
+        L.spec_get_state.argtypes = [_p, C.POINTER(SpecState)]
+        L.spec_get_history.argtypes = [_p, _p, _i32]
+        L.spec_kernel_times.argtypes = [_p, _p, _i32, C.POINTER(_i32)]
+        L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
+                                         _p, _p]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("spec_init", "spec_draft", "spec_verify", "spec_commit", "spec_destroy",
+            "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
+            "spec_kernel_times", "spec_accept_reject")
+
+
+def _check(rc: int, ctx=None):
+    if rc != SPEC_OK:
+        raise SpecError(rc, spec_last_error(ctx))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+WEIGHT_NAMES = ("embed", "attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd",
+                "final_norm", "lm_head")
+
+
+def model_desc(cfg, weights: Mapping[str, "object"]) -> SpecModelDesc:
+    """cfg: any object with n_layers, d_model, n_heads, n_kv_heads, head_dim,
+    d_ffn, vocab, rope_theta, rms_eps; weights: contiguous bf16 device tensors."""
+    import torch
+    m = SpecModelDesc()
+    m.n_layers = cfg.n_layers; m.d_model = cfg.d_model; m.n_heads = cfg.n_heads
+    m.n_kv_heads = cfg.n_kv_heads; m.head_dim = cfg.head_dim; m.d_ffn = cfg.d_ffn
+    m.vocab = cfg.vocab; m.rope_theta = float(cfg.rope_theta); m.rms_eps = float(cfg.rms_eps)
+    for k in WEIGHT_NAMES:
+        t = weights[k]
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"weight {k} must be a contiguous bf16 device tensor")
+        setattr(m, k, t.data_ptr())
+    return m
+
+
+class Ctx:
+    """Owns a spec_ctx* handle."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib().spec_destroy(self.handle)
+            self.handle = None
+
+
+def spec_init(target_cfg, target_w, draft_cfg, draft_w, prompt, *, k_max: int, max_seq: int,
+              greedy: bool, use_graphs: bool = True, profile_kernels: bool = False,
+              stream_id: int = 0, stream: int = 0) -> Ctx:
+    p = SpecInitParams()
+    p.target = model_desc(target_cfg, target_w)
+    p.draft = model_desc(draft_cfg, draft_w)
+    p.k_max = k_max; p.max_seq = max_seq; p.greedy = int(bool(greedy))
+    p.use_graphs = int(bool(use_graphs)); p.profile_kernels = int(bool(profile_kernels))
+    p.stream_id = stream_id; p.hip_stream = stream or None
+    pr = np.ascontiguousarray(prompt, dtype=np.int32)
+    h = _p()
+    rc = lib().spec_init(C.byref(p), pr.ctypes.data, len(pr), C.byref(h))
+    _check(rc)
+    return Ctx(h.value)
+
+
+def spec_draft(ctx: Ctx, K: int, seed: int, d, D) -> None:
+    _check(lib().spec_draft(ctx.handle, K, seed, _ptr(d), _ptr(D)), ctx)
+
+
+def spec_verify(ctx: Ctx, K: int, seed: int, d, D, out, n_acc, T=None, logits=None) -> None:
+    _check(lib().spec_verify(ctx.handle, K, seed, _ptr(d), _ptr(D), _ptr(out), _ptr(n_acc),
+                             _ptr(T), _ptr(logits)), ctx)
+
+
+def spec_commit(ctx: Ctx, out, n_acc) -> None:
+    _check(lib().spec_commit(ctx.handle, _ptr(out), _ptr(n_acc)), ctx)
+
+
+def spec_destroy(ctx: Ctx) -> None:
+    if ctx.handle:
+        lib().spec_destroy(ctx.handle)
+        ctx.handle = None
+
+
+def spec_last_error(ctx: Optional[Ctx] = None) -> str:
+    h = ctx.handle if isinstance(ctx, Ctx) else None
+    return lib().spec_last_error(h).decode(errors="replace")
+
+
+def spec_sync(ctx: Ctx) -> None:
+    _check(lib().spec_sync(ctx.handle), ctx)
+
+
+def spec_stream(ctx: Ctx) -> int:
+    return int(lib().spec_stream(ctx.handle) or 0)
+
+
+def spec_get_state(ctx: Ctx) -> dict:
+    s = SpecState()
+    _check(lib().spec_get_state(ctx.handle, C.byref(s)), ctx)
+    return {"target_len": s.target_len, "draft_len": s.draft_len, "pending": s.pending,
+            "device_error": s.device_error}
+
+
+def spec_get_history(ctx: Ctx, n: int) -> np.ndarray:
+    out = np.zeros(n, np.int32)
+    _check(lib().spec_get_history(ctx.handle, out.ctypes.data, n), ctx)
+    return out
+
+
+def spec_kernel_times(ctx: Ctx, cap: int = 4096) -> np.ndarray:
+    buf = np.zeros(cap, np.float32)
+    n = _i32()
+    _check(lib().spec_kernel_times(ctx.handle, buf.ctypes.data, cap, C.byref(n)), ctx)
+    return buf[: n.value].copy()
+
+
+def spec_accept_reject(T, D, d, seed: int, pos, stream_id: int, greedy: bool, out, n_acc,
+                       stream: int = 0) -> None:
+    """T [B][K+1][V] f32, D [B][K][V] f32, d [B][K] i32, pos [B] i64 (read as
+    uint64), out [B][K+1] i32, n_acc [B] i32: all device tensors."""
+    B, K1, V = T.shape
+    _check(lib().spec_accept_reject(_ptr(T), _ptr(D), _ptr(d), B, K1 - 1, V, seed, _ptr(pos),
+                                    stream_id, int(bool(greedy)), _ptr(out), _ptr(n_acc),
+                                    stream or None))

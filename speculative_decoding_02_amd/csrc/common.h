@@ -1,0 +1,174 @@
+// common.h -- device helpers and launch-argument structs shared by the HIP
+// kernels of libspec (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SPEC_DEVICE __device__ __forceinline__
+
+namespace spec {
+
+constexpr int kWave = 64;
+constexpr int kMaxRows = 8;       // activation rows per pass (K+1 <= 8)
+constexpr int kBlock = 16;        // KV-cache block size in tokens
+
+// ---------------------------------------------------------------- errors --
+// Sticky device-side error bits (DevState::err).
+enum : int32_t {
+  kErrBadToken = 1,       // a token id outside [0, vocab) reached the embedding
+  kErrLag = 2,            // draft cache lag larger than kMaxRows - 1
+  kErrCapacity = 4,       // a position at or beyond max_seq
+};
+
+// Device-resident decoding state (one per context).
+struct DevState {
+  int32_t LT;        // tokens in the target cache; hist[LT] is the pending token
+  int32_t LD;        // tokens in the draft cache
+  int32_t err;       // sticky error bits
+  int32_t pad;
+};
+
+// Row descriptor of one forward pass, written by the embedding kernel and
+// read by every later kernel of the pass.
+struct PassRows {
+  int32_t n_rows;    // 1..kMaxRows
+  int32_t pos0;      // absolute position of row 0 (row r is at pos0 + r)
+  int32_t tok[kMaxRows];
+};
+
+// ------------------------------------------------------------------ bf16 --
+SPEC_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays a quiet NaN).
+SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- Philox --
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 64x64->128-bit multiplies, key bumped by two Weyl constants between rounds.
+struct U64x4 {
+  uint64_t w[4];
+};
+
+SPEC_DEVICE U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  U64x4 o;
+  o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
+  return o;
+}
+
+// Uniform word `word` (0: draft sample, 1: accept test, 2: target sample) for
+// the token decided at absolute position p of sequence s, stream c.  Returns
+// its top 24 bits: r = u24 * 2^-24 in [0, 1).
+SPEC_DEVICE uint32_t uniform_u24(uint64_t seed, uint64_t p, uint64_t s, uint64_t c, int word) {
+  const U64x4 w = philox4x64_10(p, s, c, 0, seed, 0);
+  return (uint32_t)(w.w[word] >> 40);
+}
+
+// -------------------------------------------------------- probabilities --
+SPEC_DEVICE bool prob_valid(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
+
+// floor(x * 2^40) for a valid probability (exact: power-of-two scaling of an
+// fp32 value, then truncation of a non-negative double).
+SPEC_DEVICE uint64_t fix40(float x) { return (uint64_t)((double)x * 1099511627776.0); }
+
+// Needle of the inverse CDF: floor(u24 * Z / 2^24) without 128-bit products.
+SPEC_DEVICE uint64_t icdf_needle(uint32_t u24, uint64_t Z) {
+  return (uint64_t)u24 * (Z >> 24) + (((uint64_t)u24 * (Z & 0xFFFFFFull)) >> 24);
+}
+
+// Key whose unsigned maximum is the largest fp32 value, ties to the lowest
+// index.  Inputs are validated probabilities (>= 0); -0.0 is folded to +0.
+SPEC_DEVICE uint64_t argmax_key(float x, uint32_t idx) {
+  const uint32_t b = __float_as_uint(x == 0.0f ? 0.0f : x);
+  return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+SPEC_DEVICE uint32_t argmax_key_index(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
+
+// ------------------------------------------------------ wave reductions --
+SPEC_DEVICE uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+SPEC_DEVICE uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
+  return v;
+}
+SPEC_DEVICE uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+SPEC_DEVICE float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+SPEC_DEVICE float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Block-wide reductions through LDS (blockDim.x a multiple of 64, <= 1024).
+// Fixed combination order: deterministic.
+template <typename T, typename Op>
+SPEC_DEVICE T block_reduce(T v, T* lds /* >= 16 */, Op op) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = op(v, __shfl_xor(v, m));
+  if (lane == 0) lds[wid] = v;
+  __syncthreads();
+  T r = lds[0];
+  for (int i = 1; i < nw; ++i) r = op(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// "Last block done" protocol for reductions across the blocks of one kernel:
+// every block publishes its partial, then counts itself in; the block that
+// brings the count to `expected` sees all partials and resets the counter
+// for the next launch.  Returns true in every thread of the last block.
+SPEC_DEVICE bool arrive_last(int32_t* counter, int32_t expected, int32_t* lds_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int32_t old = atomicAdd(counter, 1);
+    const bool last = (old == expected - 1);
+    if (last) {
+      __threadfence();
+      *counter = 0;
+    }
+    *lds_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *lds_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace spec

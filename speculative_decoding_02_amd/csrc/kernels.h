@@ -1,0 +1,144 @@
+// kernels.h -- launch-argument structs and host-side launchers of the HIP
+// kernels (one translation unit per kernel family).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace spec {
+
+// ------------------------------------------------------------------ GEMM --
+// Epilogue kinds of the skinny GEMM Y[m][n] = sum_k A[m][k] W[n][k].
+enum Epi : int {
+  EPI_STORE = 0,   // out[m][n] = y
+  EPI_RESID = 1,   // resid[m][n] += y; per-64-column sums of squares for the next RMSNorm
+  EPI_SILU = 2,    // out[m][f] = silu(gate) * up   (NB = 2: gate block, up block)
+  EPI_QKV = 3,     // RoPE on q/k, q -> out, k/v -> paged KV cache
+  EPI_LOGITS = 4,  // out[m][n] = logit; per-64-column (max, sum exp) partials
+};
+
+struct GemmArgs {
+  // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16]
+  const uint16_t* Wp;
+  int n_groups;      // groups of NB 16-column blocks
+  int Kb;            // K / 32
+  int kcb;           // k-blocks staged per workgroup
+  int splits;        // workgroups along K per column group
+  // A operand: fp32 rows [n_rows][K] with row stride ldx, optional RMSNorm
+  const float* X;
+  int ldx;
+  const float* ssq;  // [ssq_groups][8] partial sums of squares, or null (no norm)
+  int ssq_groups;
+  const uint16_t* gain;  // [K] bf16 norm gain (with ssq)
+  float eps;
+  int K;
+  const PassRows* rows;
+  int last_row_only;  // use only row n_rows-1 (written as output row 0)
+  // split-K workspace
+  float* ws;
+  int32_t* counters;
+  // epilogue
+  float* out;
+  int ldo;
+  float* resid;
+  int ldr;
+  float* ssq_out;
+  float2* lm_part;   // EPI_LOGITS partials [n_wgg][8]
+  int n_valid;       // EPI_LOGITS: valid columns (vocab)
+  // EPI_QKV
+  int q_dim, kv_dim, head_dim, n_kv;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* block_table;
+  const double* inv_freq;  // [head_dim/2]
+  int max_seq;
+};
+
+// Dynamic LDS bytes the GEMM needs for a given kcb.
+inline size_t gemm_lds_bytes(int kcb) { return (size_t)kcb * 64 * 16; }
+hipError_t launch_gemm(int nb, int epi, const GemmArgs& a, hipStream_t s);
+
+// Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
+// layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
+hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, uint16_t* out,
+                       hipStream_t s);
+
+// ------------------------------------------------------------- attention --
+struct AttnArgs {
+  const float* q;            // [n_rows][n_q*hd]
+  const uint16_t* k_cache;   // [n_blocks][n_kv][16][hd]
+  const uint16_t* v_cache;
+  const int32_t* block_table;
+  const PassRows* rows;
+  int n_q, n_kv, hd;
+  int max_chunks;            // grid.x; chunks of kAttnChunk keys
+  float* o;                  // [n_rows][n_q*hd]
+  float* ws;                 // [n_kv][max_chunks][qg_max][hd+2]
+  int32_t* counters;         // [n_kv]
+  int qg_max;                // (n_q/n_kv) * kMaxRows
+};
+constexpr int kAttnChunk = 64;
+size_t attn_lds_bytes(int hd, int qg_max);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- embedding --
+enum EmbedMode : int {
+  EMB_VERIFY = 0,   // rows [hist[LT], d_0..d_{K-1}] at LT..LT+K
+  EMB_DRAFT0 = 1,   // rows hist[LD..LT] at LD..
+  EMB_DRAFTS = 2,   // row d_{step-1} at LT+step
+  EMB_PREFILL = 3,  // rows hist[pos0..pos0+n-1]
+};
+struct EmbedArgs {
+  const uint16_t* E;  // [vocab][d]
+  int d, vocab, max_seq;
+  DevState* st;
+  const int32_t* hist;
+  const int32_t* dtok;
+  int mode, n_rows, pos0, step;
+  PassRows* rows_out;
+  float* x;           // [8][d]
+  float* ssq;         // [d/64][8]
+};
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+
+// --------------------------------------------------------------- softmax --
+struct SoftmaxArgs {
+  const float* logits;   // [rows][V]
+  const float2* part;    // [G][8]
+  int G, V;
+  const PassRows* rows;
+  int last_row_only;
+  float* out;            // [rows][V]
+  int chunk;
+};
+hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, hipStream_t s);
+
+// -------------------------------------------------------- accept/reject --
+struct ArArgs {
+  const float* T;        // [B][K+1][V]   (K = 0: one row to sample)
+  const float* D;        // [B][K][V]
+  const int32_t* d;      // [B][K]
+  int B, K, V;
+  uint64_t seed, stream_id;
+  const uint64_t* pos;   // [B] position of d_1, or null: P = st->LT + pos_offset
+  const DevState* st;
+  int pos_offset;
+  int greedy;
+  int word;              // Philox word of the final sample (2 verify, 0 draft)
+  int chunk, n_chunks;
+  int32_t* out;          // [B][K+1]
+  int32_t* n_acc;        // [B] or null
+  uint64_t* ws;          // [B][n_chunks][ar_ws_words(K)]
+  int32_t* counters;     // [B]
+};
+__host__ __device__ inline int ar_ws_words(int K) { return (K + 2) > 4 ? (K + 2) : 4; }
+void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks);
+hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- commit --
+hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
+                         const int32_t* n_acc, int drafted_k, hipStream_t s);
+hipError_t launch_inv_freq(double* dst, int hd, double theta, hipStream_t s);
+
+}  // namespace spec

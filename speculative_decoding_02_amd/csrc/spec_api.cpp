@@ -1,0 +1,858 @@
+// spec_api.cpp -- host side of libspec: the C ABI declared in include/spec.h.
+//
+// A context owns two models (target, draft) with repacked weights, one paged
+// KV cache per model, shared activation/workspace buffers, the device-side
+// decoding state and the captured graphs.  Every step of the path runs in
+// the HIP kernels; this file validates arguments, lays out memory, and
+// enqueues launches (directly or through hipGraphs).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "spec.h"
+
+using namespace spec;
+
+namespace {
+
+thread_local std::string g_err;
+
+std::string fmt(const char* f, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+
+// ------------------------------------------------------------ GEMM plans --
+struct GemmPlan {
+  int nb = 1, n_groups = 0, n_wgg = 0, Kb = 0, kcb = 0, splits = 1;
+  size_t ws_floats() const { return (size_t)n_wgg * splits * 4 * nb * 128; }
+};
+
+GemmPlan plan_gemm(int n_cols, int nb, int K) {
+  GemmPlan p;
+  p.nb = nb;
+  p.n_groups = n_cols / (16 * nb);
+  p.n_wgg = (p.n_groups + 3) / 4;
+  p.Kb = K / 32;
+  const int kcb_max = 32;  // 32 KiB of staged activations per workgroup
+  static const int env_kcb = [] {
+    const char* e = getenv("SPEC_GEMM_KCB");
+    return e ? atoi(e) : 0;
+  }();
+  int S;
+  if (env_kcb > 0) {
+    S = (p.Kb + env_kcb - 1) / env_kcb;
+  } else {
+    const int s_min = (p.Kb + kcb_max - 1) / kcb_max;
+    const int s_fill = (512 + p.n_wgg - 1) / p.n_wgg;
+    const int s_cap = std::max(1, p.Kb / 8);
+    S = std::max(s_min, std::min(s_fill, s_cap));
+  }
+  S = std::max(1, std::min(S, p.Kb));
+  p.kcb = (p.Kb + S - 1) / S;
+  p.splits = (p.Kb + p.kcb - 1) / p.kcb;
+  return p;
+}
+
+struct Mat {
+  uint16_t* p = nullptr;  // packed (inside the model arena)
+  GemmPlan plan;
+  int K = 0, N = 0;
+  size_t elems() const { return (size_t)plan.n_groups * plan.Kb * plan.nb * 64 * 8; }
+};
+
+struct Model {
+  int L = 0, d = 0, nq = 0, nkv = 0, hd = 0, F = 0, V = 0, qd = 0, kvd = 0;
+  float theta = 10000.f, eps = 1e-5f;
+  std::vector<Mat> qkv, o, gu, dn;
+  Mat lm;
+  bool lm_shared = false, embed_shared = false;
+  uint16_t* arena = nullptr;      // packed matrices
+  uint16_t* embed = nullptr;      // [V][d] (owned unless shared)
+  uint16_t* norms = nullptr;      // attn [L][d], ffn [L][d], final [d]
+  uint16_t* kcache = nullptr;     // [L][n_blocks][nkv][16][hd]
+  uint16_t* vcache = nullptr;
+  int32_t* block_table = nullptr;
+  double* inv_freq = nullptr;
+  int n_blocks = 0;
+  size_t kv_layer_elems() const { return (size_t)n_blocks * nkv * kBlock * hd; }
+  const uint16_t* attn_norm(int l) const { return norms + (size_t)l * d; }
+  const uint16_t* ffn_norm(int l) const { return norms + (size_t)(L + l) * d; }
+  const uint16_t* final_norm() const { return norms + (size_t)2 * L * d; }
+};
+
+struct GraphEntry {
+  hipGraphExec_t exec = nullptr;
+  std::vector<hipEvent_t> events;  // pairs around profiled launches
+};
+
+}  // namespace
+
+struct spec_ctx {
+  spec_init_params p{};
+  std::string err;
+  hipStream_t stream = nullptr, cap_stream = nullptr;
+  bool own_stream = false;
+  int device = 0;
+  Model T, D;
+  // shared buffers
+  float *x = nullptr, *q = nullptr, *o = nullptr, *a = nullptr, *ssq = nullptr;
+  float *logits = nullptr, *Tbuf = nullptr;
+  float* ws = nullptr;
+  float* attn_ws = nullptr;
+  float2* lm_part = nullptr;
+  uint64_t* ar_ws = nullptr;
+  int32_t *gemm_cnt = nullptr, *attn_cnt = nullptr, *ar_cnt = nullptr;
+  PassRows* rows = nullptr;
+  DevState* st = nullptr;
+  int32_t* hist = nullptr;
+  int hist_cap = 0;
+  int attn_max_chunks = 0;
+  int ar_chunk = 0, ar_nchunks = 0;
+  int sm_chunk = 0, sm_nchunks = 0;
+  // host bookkeeping
+  int LT_ub = 0, lag_ub = 0;
+  int drafted_k = 0;
+  bool verify_pending = false;
+  int last_k = 0;
+  bool graphs = true;
+  std::map<std::vector<uint64_t>, GraphEntry> graph_cache;
+  GraphEntry* last_draft = nullptr;
+  GraphEntry* last_verify = nullptr;
+  std::vector<hipEvent_t> eager_events_draft, eager_events_verify;
+  std::vector<hipEvent_t>* rec_events = nullptr;  // where profiled launches record
+  hipStream_t rec_stream = nullptr;
+};
+
+namespace {
+
+int fail(spec_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  g_err = msg;
+  return code;
+}
+
+#define HIPTRY(ctx, expr)                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    if (e_ != hipSuccess)                                                                       \
+      return fail(ctx, e_ == hipErrorOutOfMemory ? SPEC_ERR_OOM : SPEC_ERR_HIP,                 \
+                  fmt("%s: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, __LINE__));     \
+  } while (0)
+
+template <typename T>
+hipError_t dalloc(T** p, size_t n) {
+  return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
+}
+
+bool valid_model(const spec_model_desc& m, std::string* why) {
+  if (m.n_layers < 1 || m.d_model < 64 || m.n_heads < 1 || m.n_kv_heads < 1 || m.head_dim < 2 ||
+      m.d_ffn < 32 || m.vocab < 16) {
+    *why = "non-positive or too small dimension";
+    return false;
+  }
+  if (m.d_model % 64 || m.d_ffn % 32 || m.vocab % 16 || m.head_dim % 2) {
+    *why = "need d_model % 64 == 0, d_ffn % 32 == 0, vocab % 16 == 0, even head_dim";
+    return false;
+  }
+  if (m.n_heads % m.n_kv_heads) {
+    *why = "n_heads must be a multiple of n_kv_heads";
+    return false;
+  }
+  if ((m.n_heads * m.head_dim / 2) % 8 || (m.n_kv_heads * m.head_dim / 2) % 8) {
+    *why = "n_heads*head_dim/2 and n_kv_heads*head_dim/2 must be multiples of 8";
+    return false;
+  }
+  if (m.head_dim > 256 || (m.n_heads / m.n_kv_heads) * kMaxRows > 64 || m.head_dim % 8) {
+    *why = "head_dim must be a multiple of 8 and <= 256; n_heads/n_kv_heads <= 8";
+    return false;
+  }
+  if ((m.n_heads * m.head_dim) % 32) {
+    *why = "n_heads*head_dim must be a multiple of 32";
+    return false;
+  }
+  if (!m.embed || !m.attn_norm || !m.wq || !m.wk || !m.wv || !m.wo || !m.ffn_norm || !m.wg ||
+      !m.wu || !m.wd || !m.final_norm || !m.lm_head) {
+    *why = "null weight pointer";
+    return false;
+  }
+  if (!(m.rms_eps >= 0.0f) || !(m.rope_theta > 0.0f)) {
+    *why = "rms_eps must be >= 0 and rope_theta > 0";
+    return false;
+  }
+  return true;
+}
+
+// Packs one matrix from row pointers (host list) into dst.
+int pack_rows(spec_ctx* c, const std::vector<const uint16_t*>& rows, const Mat& m) {
+  const uint16_t** drows = nullptr;
+  HIPTRY(c, dalloc(&drows, rows.size()));
+  hipError_t e = hipMemcpyAsync(drows, rows.data(), rows.size() * sizeof(void*),
+                                hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = launch_pack(drows, m.K, m.plan.nb, m.plan.n_groups, m.p, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  (void)hipFree(drows);
+  HIPTRY(c, e);
+  return SPEC_OK;
+}
+
+int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* share_from,
+                const spec_model_desc* share_desc) {
+  m.L = md.n_layers; m.d = md.d_model; m.nq = md.n_heads; m.nkv = md.n_kv_heads;
+  m.hd = md.head_dim; m.F = md.d_ffn; m.V = md.vocab;
+  m.qd = m.nq * m.hd; m.kvd = m.nkv * m.hd;
+  m.theta = md.rope_theta; m.eps = md.rms_eps;
+  const int L = m.L, d = m.d;
+  auto mk = [](int N, int nb, int K) {
+    Mat x;
+    x.N = N; x.K = K;
+    x.plan = plan_gemm(N, nb, K);
+    return x;
+  };
+  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, 1, d));
+  m.o.assign(L, mk(d, 1, m.qd));
+  m.gu.assign(L, mk(2 * m.F, 2, d));
+  m.dn.assign(L, mk(d, 1, m.F));
+  m.lm = mk(m.V, 1, d);
+  m.lm_shared = share_from && share_desc && md.lm_head == share_desc->lm_head &&
+                md.d_model == share_desc->d_model && md.vocab == share_desc->vocab;
+  m.embed_shared = share_from && share_desc && md.embed == share_desc->embed &&
+                   md.d_model == share_desc->d_model && md.vocab == share_desc->vocab;
+  size_t total = 0;
+  for (int l = 0; l < L; ++l)
+    total += m.qkv[l].elems() + m.o[l].elems() + m.gu[l].elems() + m.dn[l].elems();
+  if (!m.lm_shared) total += m.lm.elems();
+  HIPTRY(c, dalloc(&m.arena, total));
+  size_t off = 0;
+  auto place = [&](Mat& x) { x.p = m.arena + off; off += x.elems(); };
+  for (int l = 0; l < L; ++l) {
+    place(m.qkv[l]); place(m.o[l]); place(m.gu[l]); place(m.dn[l]);
+  }
+  if (m.lm_shared) m.lm.p = share_from->lm.p;
+  else place(m.lm);
+
+  const uint16_t* wq = (const uint16_t*)md.wq;
+  const uint16_t* wk = (const uint16_t*)md.wk;
+  const uint16_t* wv = (const uint16_t*)md.wv;
+  const uint16_t* wo = (const uint16_t*)md.wo;
+  const uint16_t* wg = (const uint16_t*)md.wg;
+  const uint16_t* wu = (const uint16_t*)md.wu;
+  const uint16_t* wdn = (const uint16_t*)md.wd;
+  const int half = m.hd / 2;
+  std::vector<const uint16_t*> rows;
+  for (int l = 0; l < L; ++l) {
+    // QKV: q and k rows in pair-interleaved order (columns w, w+8 of a block
+    // are the halves j, j+hd/2 of one RoPE pair), then v rows in order.
+    rows.assign((size_t)m.qkv[l].plan.n_groups * 16, nullptr);
+    for (int p = 0; p < m.qd + 2 * m.kvd; ++p) {
+      const uint16_t* src;
+      if (p < m.qd + m.kvd) {
+        const bool is_q = p < m.qd;
+        const int pl = is_q ? p : p - m.qd;
+        const int b = pl / 16, w = pl % 16;
+        const int pair = b * 8 + (w & 7), hf = w >> 3;
+        const int head = pair / half, jj = pair % half;
+        const int row = head * m.hd + jj + hf * half;
+        src = is_q ? wq + ((size_t)l * m.qd + row) * d : wk + ((size_t)l * m.kvd + row) * d;
+      } else {
+        src = wv + ((size_t)l * m.kvd + (p - m.qd - m.kvd)) * d;
+      }
+      rows[p] = src;
+    }
+    if (int r = pack_rows(c, rows, m.qkv[l])) return r;
+    rows.assign((size_t)m.o[l].plan.n_groups * 16, nullptr);
+    for (int n = 0; n < d; ++n) rows[n] = wo + ((size_t)l * d + n) * m.qd;
+    if (int r = pack_rows(c, rows, m.o[l])) return r;
+    rows.assign((size_t)m.gu[l].plan.n_groups * 32, nullptr);
+    for (int g = 0; g < m.F / 16; ++g)
+      for (int w = 0; w < 16; ++w) {
+        rows[(size_t)(g * 2 + 0) * 16 + w] = wg + ((size_t)l * m.F + g * 16 + w) * d;
+        rows[(size_t)(g * 2 + 1) * 16 + w] = wu + ((size_t)l * m.F + g * 16 + w) * d;
+      }
+    if (int r = pack_rows(c, rows, m.gu[l])) return r;
+    rows.assign((size_t)m.dn[l].plan.n_groups * 16, nullptr);
+    for (int n = 0; n < d; ++n) rows[n] = wdn + ((size_t)l * d + n) * m.F;
+    if (int r = pack_rows(c, rows, m.dn[l])) return r;
+  }
+  if (!m.lm_shared) {
+    rows.assign((size_t)m.lm.plan.n_groups * 16, nullptr);
+    const uint16_t* lm = (const uint16_t*)md.lm_head;
+    for (int n = 0; n < m.V; ++n) rows[n] = lm + (size_t)n * d;
+    if (int r = pack_rows(c, rows, m.lm)) return r;
+  }
+  // embedding and norm gains (owned copies)
+  if (m.embed_shared) {
+    m.embed = share_from->embed;
+  } else {
+    HIPTRY(c, dalloc(&m.embed, (size_t)m.V * d));
+    HIPTRY(c, hipMemcpyAsync(m.embed, md.embed, (size_t)m.V * d * 2, hipMemcpyDeviceToDevice,
+                             c->stream));
+  }
+  HIPTRY(c, dalloc(&m.norms, (size_t)(2 * L + 1) * d));
+  HIPTRY(c, hipMemcpyAsync(m.norms, md.attn_norm, (size_t)L * d * 2, hipMemcpyDeviceToDevice, c->stream));
+  HIPTRY(c, hipMemcpyAsync(m.norms + (size_t)L * d, md.ffn_norm, (size_t)L * d * 2,
+                           hipMemcpyDeviceToDevice, c->stream));
+  HIPTRY(c, hipMemcpyAsync(m.norms + (size_t)2 * L * d, md.final_norm, (size_t)d * 2,
+                           hipMemcpyDeviceToDevice, c->stream));
+  // paged KV cache: blocks of 16 tokens; the block table maps logical block i
+  // to physical block n_blocks-1-i (any permutation works).
+  m.n_blocks = (c->p.max_seq + kBlock - 1) / kBlock;
+  HIPTRY(c, dalloc(&m.kcache, (size_t)L * m.kv_layer_elems()));
+  HIPTRY(c, dalloc(&m.vcache, (size_t)L * m.kv_layer_elems()));
+  std::vector<int32_t> bt(m.n_blocks);
+  for (int i = 0; i < m.n_blocks; ++i) bt[i] = m.n_blocks - 1 - i;
+  HIPTRY(c, dalloc(&m.block_table, (size_t)m.n_blocks));
+  HIPTRY(c, hipMemcpyAsync(m.block_table, bt.data(), bt.size() * 4, hipMemcpyHostToDevice, c->stream));
+  HIPTRY(c, dalloc(&m.inv_freq, (size_t)half));
+  HIPTRY(c, launch_inv_freq(m.inv_freq, m.hd, (double)m.theta, c->stream));
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  return SPEC_OK;
+}
+
+void free_model(Model& m) {
+  (void)hipFree(m.arena);
+  if (!m.embed_shared) (void)hipFree(m.embed);
+  (void)hipFree(m.norms);
+  (void)hipFree(m.kcache);
+  (void)hipFree(m.vcache);
+  (void)hipFree(m.block_table);
+  (void)hipFree(m.inv_freq);
+  m = Model();
+}
+
+// ------------------------------------------------------------ enqueuing --
+GemmArgs gemm_base(spec_ctx* c, const Mat& w) {
+  GemmArgs a{};
+  a.Wp = w.p;
+  a.n_groups = w.plan.n_groups;
+  a.Kb = w.plan.Kb;
+  a.kcb = w.plan.kcb;
+  a.splits = w.plan.splits;
+  a.K = w.K;
+  a.rows = c->rows;
+  a.ws = c->ws;
+  a.counters = c->gemm_cnt;
+  return a;
+}
+
+hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profile) {
+  hipError_t e = hipSuccess;
+  const int G64 = m.d / 64;
+  for (int l = 0; l < m.L && e == hipSuccess; ++l) {
+    // RMSNorm + QKV + RoPE + KV append
+    GemmArgs a = gemm_base(c, m.qkv[l]);
+    a.X = c->x; a.ldx = m.d; a.ssq = c->ssq; a.ssq_groups = G64; a.gain = m.attn_norm(l);
+    a.eps = m.eps;
+    a.out = c->q; a.ldo = m.qd;
+    a.q_dim = m.qd; a.kv_dim = m.kvd; a.head_dim = m.hd; a.n_kv = m.nkv;
+    a.k_cache = m.kcache + (size_t)l * m.kv_layer_elems();
+    a.v_cache = m.vcache + (size_t)l * m.kv_layer_elems();
+    a.block_table = m.block_table; a.inv_freq = m.inv_freq; a.max_seq = c->p.max_seq;
+    e = launch_gemm(1, EPI_QKV, a, s);
+    if (e != hipSuccess) break;
+    // causal attention over the paged cache
+    AttnArgs at{};
+    at.q = c->q; at.k_cache = a.k_cache; at.v_cache = a.v_cache; at.block_table = m.block_table;
+    at.rows = c->rows; at.n_q = m.nq; at.n_kv = m.nkv; at.hd = m.hd;
+    at.max_chunks = c->attn_max_chunks; at.o = c->o; at.ws = c->attn_ws; at.counters = c->attn_cnt;
+    at.qg_max = (m.nq / m.nkv) * kMaxRows;
+    e = launch_attn(at, s);
+    if (e != hipSuccess) break;
+    // O projection + residual
+    GemmArgs b = gemm_base(c, m.o[l]);
+    b.X = c->o; b.ldx = m.qd;
+    b.resid = c->x; b.ldr = m.d; b.ssq_out = c->ssq;
+    e = launch_gemm(1, EPI_RESID, b, s);
+    if (e != hipSuccess) break;
+    // RMSNorm + gate/up + SiLU*mul
+    GemmArgs g = gemm_base(c, m.gu[l]);
+    g.X = c->x; g.ldx = m.d; g.ssq = c->ssq; g.ssq_groups = G64; g.gain = m.ffn_norm(l);
+    g.eps = m.eps; g.out = c->a; g.ldo = m.F;
+    if (profile && c->rec_events) {
+      hipEvent_t e0 = nullptr, e1 = nullptr;
+      e = hipEventCreate(&e0);
+      if (e == hipSuccess) e = hipEventCreate(&e1);
+      if (e0) c->rec_events->push_back(e0);
+      if (e1) c->rec_events->push_back(e1);
+      if (e == hipSuccess) e = hipEventRecord(e0, s);
+      if (e == hipSuccess) e = launch_gemm(2, EPI_SILU, g, s);
+      if (e == hipSuccess) e = hipEventRecord(e1, s);
+    } else {
+      e = launch_gemm(2, EPI_SILU, g, s);
+    }
+    if (e != hipSuccess) break;
+    // down projection + residual
+    GemmArgs dn = gemm_base(c, m.dn[l]);
+    dn.X = c->a; dn.ldx = m.F;
+    dn.resid = c->x; dn.ldr = m.d; dn.ssq_out = c->ssq;
+    e = launch_gemm(1, EPI_RESID, dn, s);
+  }
+  return e;
+}
+
+// final norm + LM head (+ logits partials) + softmax into `dst`
+hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only,
+                        float* logits_dst, float* dst) {
+  GemmArgs a = gemm_base(c, m.lm);
+  a.X = c->x; a.ldx = m.d; a.ssq = c->ssq; a.ssq_groups = m.d / 64; a.gain = m.final_norm();
+  a.eps = m.eps; a.last_row_only = last_row_only;
+  a.out = logits_dst; a.ldo = m.V; a.lm_part = c->lm_part; a.n_valid = m.V;
+  hipError_t e = launch_gemm(1, EPI_LOGITS, a, s);
+  if (e != hipSuccess) return e;
+  SoftmaxArgs sm{};
+  sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.n_wgg; sm.V = m.V;
+  sm.rows = c->rows; sm.last_row_only = last_row_only; sm.out = dst; sm.chunk = c->sm_chunk;
+  return launch_softmax(sm, c->sm_nchunks, s);
+}
+
+hipError_t enqueue_embed(spec_ctx* c, const Model& m, hipStream_t s, int mode, int n_rows, int pos0,
+                         int step, const int32_t* dtok) {
+  EmbedArgs a{};
+  a.E = m.embed; a.d = m.d; a.vocab = m.V; a.max_seq = c->p.max_seq;
+  a.st = c->st; a.hist = c->hist; a.dtok = dtok;
+  a.mode = mode; a.n_rows = n_rows; a.pos0 = pos0; a.step = step;
+  a.rows_out = c->rows; a.x = c->x; a.ssq = c->ssq;
+  return launch_embed(a, s);
+}
+
+hipError_t enqueue_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32_t* d, float* Dp) {
+  const Model& m = c->D;
+  hipError_t e = hipSuccess;
+  for (int st = 0; st < K && e == hipSuccess; ++st) {
+    e = enqueue_embed(c, m, s, st == 0 ? EMB_DRAFT0 : EMB_DRAFTS, 0, 0, st, d);
+    if (e == hipSuccess) e = enqueue_layers(c, m, s, c->p.profile_kernels != 0);
+    float* drow = Dp + (size_t)st * m.V;
+    if (e == hipSuccess) e = enqueue_head(c, m, s, 1, c->logits, drow);
+    if (e == hipSuccess) {
+      ArArgs ar{};
+      ar.T = drow; ar.D = nullptr; ar.d = d; ar.B = 1; ar.K = 0; ar.V = m.V;
+      ar.seed = seed; ar.stream_id = c->p.stream_id; ar.pos = nullptr; ar.st = c->st;
+      ar.pos_offset = st + 1; ar.greedy = c->p.greedy; ar.word = 0;
+      ar.chunk = c->ar_chunk; ar.n_chunks = c->ar_nchunks;
+      ar.out = d + st; ar.n_acc = nullptr; ar.ws = c->ar_ws; ar.counters = c->ar_cnt;
+      e = launch_accept_reject(ar, s);
+    }
+  }
+  return e;
+}
+
+hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, const int32_t* d,
+                          const float* Dp, int32_t* out, int32_t* nacc, float* Tdst, float* Ldst) {
+  const Model& m = c->T;
+  float* Tb = Tdst ? Tdst : c->Tbuf;
+  float* Lb = Ldst ? Ldst : c->logits;
+  hipError_t e = enqueue_embed(c, m, s, EMB_VERIFY, K + 1, 0, 0, d);
+  if (e == hipSuccess) e = enqueue_layers(c, m, s, c->p.profile_kernels != 0);
+  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, Lb, Tb);
+  if (e == hipSuccess) {
+    ArArgs ar{};
+    ar.T = Tb; ar.D = Dp; ar.d = d; ar.B = 1; ar.K = K; ar.V = m.V;
+    ar.seed = seed; ar.stream_id = c->p.stream_id; ar.pos = nullptr; ar.st = c->st;
+    ar.pos_offset = 1; ar.greedy = c->p.greedy; ar.word = 2;
+    ar.chunk = c->ar_chunk; ar.n_chunks = c->ar_nchunks;
+    ar.out = out; ar.n_acc = nacc; ar.ws = c->ar_ws; ar.counters = c->ar_cnt;
+    e = launch_accept_reject(ar, s);
+  }
+  return e;
+}
+
+// Runs `body` either directly on the context stream or through a cached
+// graph captured on the capture stream.
+template <typename F>
+int run_pass(spec_ctx* c, const std::vector<uint64_t>& key, std::vector<hipEvent_t>* eager_events,
+             GraphEntry** last, F body) {
+  if (!c->graphs) {
+    for (hipEvent_t ev : *eager_events) (void)hipEventDestroy(ev);
+    eager_events->clear();
+    c->rec_events = eager_events;
+    hipError_t e = body(c->stream);
+    c->rec_events = nullptr;
+    HIPTRY(c, e);
+    *last = nullptr;
+    return SPEC_OK;
+  }
+  auto it = c->graph_cache.find(key);
+  if (it == c->graph_cache.end()) {
+    GraphEntry ge;
+    HIPTRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeRelaxed));
+    c->rec_events = &ge.events;
+    hipError_t e = body(c->cap_stream);
+    c->rec_events = nullptr;
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(c->cap_stream, &g);
+    if (e == hipSuccess) e = e2;
+    if (e == hipSuccess) e = hipGraphInstantiate(&ge.exec, g, nullptr, nullptr, 0);
+    if (g) (void)hipGraphDestroy(g);
+    HIPTRY(c, e);
+    it = c->graph_cache.emplace(key, ge).first;
+  }
+  HIPTRY(c, hipGraphLaunch(it->second.exec, c->stream));
+  *last = &it->second;
+  return SPEC_OK;
+}
+
+int sync_state(spec_ctx* c, DevState* hs) {
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  HIPTRY(c, hipMemcpy(hs, c->st, sizeof(DevState), hipMemcpyDeviceToHost));
+  return SPEC_OK;
+}
+
+// Prefill rows [pos0, pos0+n) of the committed history into model m.
+int prefill(spec_ctx* c, const Model& m, int pos0, int n) {
+  for (int p = pos0; p < pos0 + n; p += kMaxRows) {
+    const int cnt = std::min(kMaxRows, pos0 + n - p);
+    HIPTRY(c, enqueue_embed(c, m, c->stream, EMB_PREFILL, cnt, p, 0, nullptr));
+    HIPTRY(c, enqueue_layers(c, m, c->stream, false));
+  }
+  return SPEC_OK;
+}
+
+void destroy_ctx(spec_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->device);
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  for (auto& kv : c->graph_cache) {
+    if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+    for (hipEvent_t ev : kv.second.events) (void)hipEventDestroy(ev);
+  }
+  for (hipEvent_t ev : c->eager_events_draft) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : c->eager_events_verify) (void)hipEventDestroy(ev);
+  free_model(c->D);
+  free_model(c->T);
+  void* bufs[] = {c->x, c->q, c->o, c->a, c->ssq, c->logits, c->Tbuf, c->ws, c->attn_ws, c->lm_part,
+                  c->ar_ws, c->gemm_cnt, c->attn_cnt, c->ar_cnt, c->rows, c->st, c->hist};
+  for (void* b : bufs) (void)hipFree(b);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
+  delete c;
+}
+
+}  // namespace
+
+// ===================================================================== ABI ==
+extern "C" {
+
+int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_prompt,
+              spec_ctx** out) {
+  if (!out) return fail(nullptr, SPEC_ERR_ARG, "spec_init: out is null");
+  *out = nullptr;
+  if (!p || !prompt_host) return fail(nullptr, SPEC_ERR_ARG, "spec_init: null argument");
+  std::string why;
+  if (!valid_model(p->target, &why)) return fail(nullptr, SPEC_ERR_ARG, "target: " + why);
+  if (!valid_model(p->draft, &why)) return fail(nullptr, SPEC_ERR_ARG, "draft: " + why);
+  if (p->draft.vocab != p->target.vocab)
+    return fail(nullptr, SPEC_ERR_ARG, "draft and target must share the vocabulary");
+  if (p->k_max < 1 || p->k_max > SPEC_K_MAX)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("k_max must be in 1..%d", SPEC_K_MAX));
+  if (n_prompt < 1) return fail(nullptr, SPEC_ERR_ARG, "n_prompt must be >= 1");
+  for (int i = 0; i < n_prompt; ++i)
+    if (prompt_host[i] < 0 || prompt_host[i] >= p->target.vocab)
+      return fail(nullptr, SPEC_ERR_ARG, fmt("prompt token %d out of range", i));
+  if (p->max_seq < n_prompt + p->k_max + 1)
+    return fail(nullptr, SPEC_ERR_CAPACITY, "max_seq must be >= n_prompt + k_max + 1");
+
+  spec_ctx* c = new spec_ctx();
+  c->p = *p;
+  (void)hipGetDevice(&c->device);
+  c->graphs = p->use_graphs != 0 && getenv("SPEC_NO_GRAPH") == nullptr;
+  auto bail = [&](int rc) {
+    std::string msg = c->err;
+    destroy_ctx(c);
+    g_err = msg;
+    return rc;
+  };
+#define TRY(expr)                     \
+  do {                                \
+    int rc_ = (expr);                 \
+    if (rc_ != SPEC_OK) return bail(rc_); \
+  } while (0)
+#define TRYH(expr)                                                                        \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return bail(fail(c, e_ == hipErrorOutOfMemory ? SPEC_ERR_OOM : SPEC_ERR_HIP,        \
+                       fmt("%s: %s", #expr, hipGetErrorString(e_))));                      \
+  } while (0)
+
+  if (p->hip_stream) {
+    c->stream = (hipStream_t)p->hip_stream;
+  } else {
+    TRYH(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
+    c->own_stream = true;
+  }
+  TRYH(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+
+  TRY(build_model(c, p->target, c->T, nullptr, nullptr));
+  TRY(build_model(c, p->draft, c->D, &c->T, &p->target));
+
+  const Model* ms[2] = {&c->T, &c->D};
+  int dmax = 0, qmax = 0, fmax = 0, V = c->T.V, lm_wgg = 0, gcnt = 0;
+  size_t ws = 0, attn_ws = 0;
+  c->attn_max_chunks = (p->max_seq + kAttnChunk - 1) / kAttnChunk;
+  for (const Model* m : ms) {
+    dmax = std::max(dmax, m->d);
+    qmax = std::max(qmax, m->qd);
+    fmax = std::max(fmax, m->F);
+    lm_wgg = std::max(lm_wgg, m->lm.plan.n_wgg);
+    auto upd = [&](const Mat& x) {
+      ws = std::max(ws, x.plan.ws_floats());
+      gcnt = std::max(gcnt, x.plan.n_wgg);
+    };
+    for (int l = 0; l < m->L; ++l) { upd(m->qkv[l]); upd(m->o[l]); upd(m->gu[l]); upd(m->dn[l]); }
+    upd(m->lm);
+    const int qg = (m->nq / m->nkv) * kMaxRows;
+    attn_ws = std::max(attn_ws, (size_t)m->nkv * c->attn_max_chunks * qg * (m->hd + 2));
+    if (attn_lds_bytes(m->hd, qg) > 64 * 1024) {
+      return bail(fail(c, SPEC_ERR_ARG, "attention tile exceeds 64 KiB of LDS"));
+    }
+  }
+  ar_choose_chunks(1, V, &c->ar_chunk, &c->ar_nchunks);
+  c->sm_chunk = 4096;
+  c->sm_nchunks = (V + c->sm_chunk - 1) / c->sm_chunk;
+  TRYH(dalloc(&c->x, (size_t)kMaxRows * dmax));
+  TRYH(dalloc(&c->q, (size_t)kMaxRows * qmax));
+  TRYH(dalloc(&c->o, (size_t)kMaxRows * qmax));
+  TRYH(dalloc(&c->a, (size_t)kMaxRows * fmax));
+  TRYH(dalloc(&c->ssq, (size_t)kMaxRows * (dmax / 64)));
+  TRYH(dalloc(&c->logits, (size_t)kMaxRows * V));
+  TRYH(dalloc(&c->Tbuf, (size_t)kMaxRows * V));
+  TRYH(dalloc(&c->ws, ws));
+  TRYH(dalloc(&c->attn_ws, attn_ws));
+  TRYH(dalloc(&c->lm_part, (size_t)lm_wgg * kMaxRows));
+  TRYH(dalloc(&c->ar_ws, (size_t)c->ar_nchunks * ar_ws_words(SPEC_K_MAX)));
+  TRYH(dalloc(&c->gemm_cnt, (size_t)gcnt));
+  TRYH(dalloc(&c->attn_cnt, (size_t)std::max(c->T.nkv, c->D.nkv)));
+  TRYH(dalloc(&c->ar_cnt, (size_t)4));
+  TRYH(dalloc(&c->rows, 1));
+  TRYH(dalloc(&c->st, 1));
+  c->hist_cap = p->max_seq + 16;
+  TRYH(dalloc(&c->hist, (size_t)c->hist_cap));
+  TRYH(hipMemsetAsync(c->gemm_cnt, 0, (size_t)gcnt * 4, c->stream));
+  TRYH(hipMemsetAsync(c->attn_cnt, 0, (size_t)std::max(c->T.nkv, c->D.nkv) * 4, c->stream));
+  TRYH(hipMemsetAsync(c->ar_cnt, 0, 4 * 4, c->stream));
+  TRYH(hipMemsetAsync(c->x, 0, (size_t)kMaxRows * dmax * 4, c->stream));
+  TRYH(hipMemsetAsync(c->hist, 0, (size_t)c->hist_cap * 4, c->stream));
+  TRYH(hipMemcpyAsync(c->hist, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, c->stream));
+  DevState hs{0, 0, 0, 0};
+  TRYH(hipMemcpyAsync(c->st, &hs, sizeof hs, hipMemcpyHostToDevice, c->stream));
+  TRYH(hipStreamSynchronize(c->stream));
+
+  // prompt[0..n-2] into both caches; prompt[n-1] is the pending token
+  TRY(prefill(c, c->T, 0, n_prompt - 1));
+  TRY(prefill(c, c->D, 0, n_prompt - 1));
+  hs.LT = n_prompt - 1;
+  hs.LD = n_prompt - 1;
+  TRYH(hipMemcpyAsync(c->st, &hs, sizeof hs, hipMemcpyHostToDevice, c->stream));
+  TRYH(hipStreamSynchronize(c->stream));
+  c->LT_ub = n_prompt - 1;
+  c->lag_ub = 0;
+  *out = c;
+  return SPEC_OK;
+#undef TRY
+#undef TRYH
+}
+
+int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_draft: null context");
+  if (K < 1 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..k_max", K));
+  if (!d_dev || !D_dev) return fail(c, SPEC_ERR_ARG, "spec_draft: null output");
+  HIPTRY(c, hipSetDevice(c->device));
+  if (c->lag_ub > kMaxRows - 1 || c->LT_ub + K > c->p.max_seq) {
+    DevState hs;
+    if (int r = sync_state(c, &hs)) return r;
+    c->LT_ub = hs.LT;
+    if (hs.LT + K > c->p.max_seq)
+      return fail(c, SPEC_ERR_CAPACITY, "draft positions would exceed max_seq");
+    if (hs.LT - hs.LD > kMaxRows - 1) {
+      // catch the draft cache up with the committed history, then continue
+      if (int r = prefill(c, c->D, hs.LD, hs.LT - hs.LD)) return r;
+      hs.LD = hs.LT;
+      HIPTRY(c, hipMemcpyAsync(&c->st->LD, &hs.LD, 4, hipMemcpyHostToDevice, c->stream));
+      HIPTRY(c, hipStreamSynchronize(c->stream));
+    }
+    c->lag_ub = hs.LT - hs.LD;
+  }
+  std::vector<uint64_t> key = {1, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
+                               (uint64_t)(uintptr_t)D_dev};
+  int r = run_pass(c, key, &c->eager_events_draft, &c->last_draft,
+                   [&](hipStream_t s) { return enqueue_draft(c, s, K, seed, d_dev, D_dev); });
+  if (r) return r;
+  c->drafted_k = K;
+  return SPEC_OK;
+}
+
+int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
+                int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_verify: null context");
+  if (K < 1 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..k_max", K));
+  if (!d_dev || !out_dev || !n_acc_dev || (!D_dev && !c->p.greedy))
+    return fail(c, SPEC_ERR_ARG, "spec_verify: null argument");
+  if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_verify: previous verify not committed");
+  HIPTRY(c, hipSetDevice(c->device));
+  if (c->LT_ub + K + 1 > c->p.max_seq) {
+    DevState hs;
+    if (int r = sync_state(c, &hs)) return r;
+    c->LT_ub = hs.LT;
+    if (hs.LT + K + 1 > c->p.max_seq)
+      return fail(c, SPEC_ERR_CAPACITY, "verify positions would exceed max_seq");
+  }
+  std::vector<uint64_t> key = {2,
+                               (uint64_t)K,
+                               seed,
+                               (uint64_t)(uintptr_t)d_dev,
+                               (uint64_t)(uintptr_t)D_dev,
+                               (uint64_t)(uintptr_t)out_dev,
+                               (uint64_t)(uintptr_t)n_acc_dev,
+                               (uint64_t)(uintptr_t)T_dev,
+                               (uint64_t)(uintptr_t)logits_dev};
+  int r = run_pass(c, key, &c->eager_events_verify, &c->last_verify, [&](hipStream_t s) {
+    return enqueue_verify(c, s, K, seed, d_dev, D_dev, out_dev, n_acc_dev, T_dev, logits_dev);
+  });
+  if (r) return r;
+  c->verify_pending = true;
+  c->last_k = K;
+  return SPEC_OK;
+}
+
+int spec_commit(spec_ctx* c, const int32_t* out_dev, const int32_t* n_acc_dev) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_commit: null context");
+  if (!out_dev || !n_acc_dev) return fail(c, SPEC_ERR_ARG, "spec_commit: null argument");
+  if (!c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_commit: no verify pending");
+  HIPTRY(c, hipSetDevice(c->device));
+  HIPTRY(c, launch_commit(c->st, c->hist, c->hist_cap, out_dev, n_acc_dev, c->drafted_k, c->stream));
+  c->LT_ub += c->last_k + 1;
+  c->lag_ub = c->drafted_k > 0 ? 1 : c->lag_ub + c->last_k + 1;
+  c->drafted_k = 0;
+  c->verify_pending = false;
+  return SPEC_OK;
+}
+
+int spec_destroy(spec_ctx* c) {
+  destroy_ctx(c);
+  return SPEC_OK;
+}
+
+const char* spec_last_error(const spec_ctx* c) { return c ? c->err.c_str() : g_err.c_str(); }
+
+int spec_sync(spec_ctx* c) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_sync: null context");
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  return SPEC_OK;
+}
+
+void* spec_stream(const spec_ctx* c) { return c ? (void*)c->stream : nullptr; }
+
+int spec_get_state(spec_ctx* c, spec_state* out) {
+  if (!c || !out) return fail(c, SPEC_ERR_ARG, "spec_get_state: null argument");
+  DevState hs;
+  if (int r = sync_state(c, &hs)) return r;
+  int32_t pend = -1;
+  if (hs.LT >= 0 && hs.LT < c->hist_cap)
+    HIPTRY(c, hipMemcpy(&pend, c->hist + hs.LT, 4, hipMemcpyDeviceToHost));
+  out->target_len = hs.LT;
+  out->draft_len = hs.LD;
+  out->pending = pend;
+  out->device_error = hs.err;
+  return SPEC_OK;
+}
+
+int spec_get_history(spec_ctx* c, int32_t* host_out, int32_t n) {
+  if (!c || !host_out || n < 0 || n > c->hist_cap)
+    return fail(c, SPEC_ERR_ARG, "spec_get_history: bad argument");
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  HIPTRY(c, hipMemcpy(host_out, c->hist, (size_t)n * 4, hipMemcpyDeviceToHost));
+  return SPEC_OK;
+}
+
+int spec_kernel_times(spec_ctx* c, float* ms_out, int32_t cap, int32_t* n_out) {
+  if (!c || !n_out || (cap > 0 && !ms_out)) return fail(c, SPEC_ERR_ARG, "spec_kernel_times: bad argument");
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  int n = 0;
+  auto take = [&](const std::vector<hipEvent_t>& ev) -> int {
+    for (size_t i = 0; i + 1 < ev.size(); i += 2) {
+      float ms = 0.f;
+      HIPTRY(c, hipEventElapsedTime(&ms, ev[i], ev[i + 1]));
+      if (n < cap) ms_out[n] = ms;
+      ++n;
+    }
+    return SPEC_OK;
+  };
+  if (c->graphs) {
+    if (c->last_draft) if (int r = take(c->last_draft->events)) return r;
+    if (c->last_verify) if (int r = take(c->last_verify->events)) return r;
+  } else {
+    if (int r = take(c->eager_events_draft)) return r;
+    if (int r = take(c->eager_events_verify)) return r;
+  }
+  *n_out = std::min(n, cap);
+  return SPEC_OK;
+}
+
+// -------------------------------------------------- stateless accept/reject --
+namespace {
+struct ArWorkspace {
+  uint64_t* ws = nullptr;
+  size_t ws_words = 0;
+  int32_t* cnt = nullptr;
+  size_t n_cnt = 0;
+};
+std::mutex g_ar_mu;
+std::map<int, ArWorkspace> g_ar;
+}  // namespace
+
+int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_dev, int32_t B,
+                       int32_t K, int32_t V, uint64_t seed, const uint64_t* pos_dev,
+                       uint64_t stream_id, int32_t greedy, int32_t* out_dev, int32_t* n_acc_dev,
+                       void* hip_stream) {
+  if (B < 0 || K < 1 || K > SPEC_AR_K_MAX || V < 1)
+    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: bad B, K or V");
+  if (B == 0) return SPEC_OK;
+  if (!T_dev || !d_dev || !pos_dev || !out_dev || !n_acc_dev || (!greedy && !D_dev))
+    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: null pointer");
+  hipStream_t s = (hipStream_t)hip_stream;
+  int dev = 0;
+  HIPTRY(nullptr, hipGetDevice(&dev));
+  int chunk, nch;
+  ar_choose_chunks(B, V, &chunk, &nch);
+  const size_t words = (size_t)B * nch * ar_ws_words(K);
+  std::lock_guard<std::mutex> lk(g_ar_mu);
+  ArWorkspace& w = g_ar[dev];
+  if (w.ws_words < words) {
+    (void)hipFree(w.ws);
+    w.ws = nullptr;
+    w.ws_words = 0;
+    HIPTRY(nullptr, dalloc(&w.ws, words));
+    w.ws_words = words;
+  }
+  if (w.n_cnt < (size_t)B) {
+    (void)hipFree(w.cnt);
+    w.cnt = nullptr;
+    w.n_cnt = 0;
+    HIPTRY(nullptr, dalloc(&w.cnt, (size_t)B));
+    HIPTRY(nullptr, hipMemsetAsync(w.cnt, 0, (size_t)B * 4, s));
+    w.n_cnt = B;
+  }
+  ArArgs a{};
+  a.T = T_dev; a.D = D_dev; a.d = d_dev; a.B = B; a.K = K; a.V = V;
+  a.seed = seed; a.stream_id = stream_id; a.pos = pos_dev; a.st = nullptr; a.pos_offset = 0;
+  a.greedy = greedy; a.word = 2; a.chunk = chunk; a.n_chunks = nch;
+  a.out = out_dev; a.n_acc = n_acc_dev; a.ws = w.ws; a.counters = w.cnt;
+  HIPTRY(nullptr, launch_accept_reject(a, s));
+  return SPEC_OK;
+}
+
+}  // extern "C"
