@@ -1,0 +1,264 @@
+"""Benchmark of the speculative-decoding hot path on one MI355X.
+
+A step is one speculative round of the whole path: K draft-model steps
+(hipGraph), the (K+1)-row target verify pass, the accept/reject rule and the
+commit, at batch 1.  Workload: 8B-shaped Llama target (32 layers, d 4096,
+32/8 heads x 128, FFN 14336, vocab 128256, RoPE theta 5e5) with a 1B-shaped
+draft (16 layers, d 2048, 32/8 heads x 64, FFN 8192, tied head), bf16
+random-init weights N(0, 0.02), 1024-token uniform prompt, K = 4,
+temperature-1 sampling.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: accepted tokens/s (value), verify-pass HBM GB/s, the
+roofline of the dominant kernel (the feed-forward gate/up GEMM) from hipEvents
+around each of its launches, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def verify_pass_bytes(cfg, K: int, L: int) -> int:
+    """Algorithmic bytes of one verify pass: every weight once, K+1 embedding
+    rows, keys/values of L+K+1 positions read and K+1 written, T rows written."""
+    w = cfg.weight_bytes()
+    emb = (K + 1) * cfg.d_model * 2
+    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    kv = (L + K + 1) * kv_tok + (K + 1) * kv_tok
+    t_rows = (K + 1) * cfg.vocab * 4
+    return w + emb + kv + t_rows
+
+
+def draft_step_bytes(cfg, L: int) -> int:
+    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    return cfg.weight_bytes() + cfg.d_model * 2 + (L + 1) * kv_tok + kv_tok + cfg.vocab * 4
+
+
+def gateup_bytes(cfg, rows: int) -> int:
+    """Algorithmic bytes of one feed-forward gate/up GEMM launch: W_gate and
+    W_up once, the norm gain, the input rows (fp32) and the SiLU*up output
+    rows (fp32)."""
+    d, F = cfg.d_model, cfg.d_ffn
+    return 2 * F * d * 2 + d * 2 + rows * d * 4 + rows * F * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--pair", default="8b", choices=["toy", "1.3b", "8b", "31b"])
+    ap.add_argument("--prompt-len", type=int, default=None)
+    ap.add_argument("--greedy", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rounds", type=int, default=2)
+    ap.add_argument("--kernel-rounds", type=int, default=5)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path is "
+              "measured on a single MI355X; multi-GPU sharding is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import speculative_decoding_02_amd as sd
+    import synth
+
+    tcfg, dcfg = synth.PAIRS[args.pair]
+    K = args.k
+    plen = args.prompt_len or {"toy": 32, "1.3b": 512, "8b": 1024, "31b": 2048}[args.pair]
+    rounds_total = args.steps + args.warmup
+    max_seq = plen + (K + 1) * (rounds_total + args.kernel_rounds) + 16
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    tw = synth.weights_torch(tcfg, device="cuda")
+    share = ("embed", "lm_head") if args.pair in ("toy", "1.3b") else ()
+    dw = synth.weights_torch(dcfg, seed=synth.SEED_WEIGHTS + 1, device="cuda", share_from=tw,
+                             share=share)
+    torch.cuda.synchronize()
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    prompt = synth.prompt(tcfg.vocab, plen)
+    t0 = time.time()
+    ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=args.greedy,
+                       use_graphs=True, profile_kernels=False)
+    log(f"spec_init (pack + prefill {plen} tokens) in {time.time() - t0:.1f}s")
+
+    V = tcfg.vocab
+    d = torch.zeros(K, dtype=torch.int32, device="cuda")
+    D = torch.zeros(K, V, dtype=torch.float32, device="cuda")
+    out = torch.zeros(K + 1, dtype=torch.int32, device="cuda")
+    nacc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    seed = synth.SEED_PHILOX
+    stream = torch.cuda.ExternalStream(sd.spec_stream(ctx))
+
+    def one_round(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sd.spec_draft(ctx, K, seed, d, D)
+        if ev is not None:
+            ev[1].record(stream)
+        sd.spec_verify(ctx, K, seed, d, D, out, nacc)
+        if ev is not None:
+            ev[2].record(stream)
+        sd.spec_commit(ctx, out, nacc)
+
+    for _ in range(args.warmup):
+        one_round()
+    sd.spec_sync(ctx)
+    st0 = sd.spec_get_state(ctx)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        one_round(evs[i])
+    t_end.record(stream)
+    sd.spec_sync(ctx)
+    wall = time.perf_counter() - w0
+    st1 = sd.spec_get_state(ctx)
+    assert st1["device_error"] == 0, st1
+    ms_total = t_start.elapsed_time(t_end)
+    tokens = st1["target_len"] - st0["target_len"]
+    draft_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    verify_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    tok_per_s = tokens / (ms_total / 1e3)
+    tpr = tokens / args.steps
+    L_mid = plen + tokens // 2 + st0["target_len"] - plen
+    vbytes = verify_pass_bytes(tcfg, K, L_mid)
+    vgbs = vbytes / (np.median(verify_ms) / 1e3) / 1e9
+    dbytes = K * draft_step_bytes(dcfg, L_mid)
+    dgbs = dbytes / (np.median(draft_ms) / 1e3) / 1e9
+
+    # dominant kernel: the feed-forward gate/up GEMM.  A second timed region
+    # replays the same rounds with plain launches and a hipEvent pair on the
+    # context's stream around every gate/up launch (draft and target).
+    roof = None
+    if not args.no_kernel_events:
+        sd.spec_set_profiling(ctx, True)
+        kts = []
+        for _ in range(args.kernel_rounds):
+            one_round()
+            kts.append(sd.spec_kernel_times(ctx))
+        sd.spec_set_profiling(ctx, False)
+        n_draft = K * dcfg.n_layers
+        kt_d = np.concatenate([k[:n_draft] for k in kts])
+        kt_t = np.concatenate([k[n_draft:] for k in kts])
+        b_d = gateup_bytes(dcfg, 1) * len(kt_d)
+        b_t = gateup_bytes(tcfg, K + 1) * len(kt_t)
+        n_l = len(kt_d) + len(kt_t)
+        avg_bytes = (b_d + b_t) / n_l
+        avg_ms = float((kt_d.sum() + kt_t.sum()) / n_l)
+        ach = avg_bytes / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "gemm_skinny<..., EPI_SILU>: gate/up GEMM + RMSNorm scale + SiLU*up",
+                "launches": n_l, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "avg_algorithmic_bytes": int(avg_bytes),
+                "target_launch_us": round(float(kt_t.mean()) * 1e3, 2),
+                "target_GBs": round(gateup_bytes(tcfg, K + 1) / (float(kt_t.mean()) / 1e3) / 1e9, 1),
+                "draft_launch_us": round(float(kt_d.mean()) * 1e3, 2),
+                "draft_GBs": round(gateup_bytes(dcfg, 1) / (float(kt_d.mean()) / 1e3) / 1e9, 1)}
+
+    res = {
+        "metric": "accepted tokens/s at batch 1, K=4; verify-pass HBM GB/s as % of MI355X peak",
+        "value": round(tok_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{tcfg.name} target + {dcfg.name} draft, batch 1, K={K}, prompt {plen}, "
+                        f"{'greedy' if args.greedy else 'temperature-1 sampling'}, random-init bf16",
+            "K": K, "batch": 1, "prompt_len": plen, "mode": "greedy" if args.greedy else "sampling",
+        },
+        "verify_pass": {"ms_median": round(float(np.median(verify_ms)), 4),
+                        "algorithmic_GB": round(vbytes / 1e9, 4),
+                        "GB_s": round(vgbs, 1), "frac_of_peak": round(vgbs / PEAK_HBM_GBS, 4)},
+        "draft_loop": {"ms_median": round(float(np.median(draft_ms)), 4),
+                       "algorithmic_GB": round(dbytes / 1e9, 4), "GB_s": round(dgbs, 1)},
+        "tokens_per_round": round(tpr, 4),
+        "target_passes_per_token": round(args.steps / max(tokens, 1), 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    log(json.dumps({k: res[k] for k in ("value", "ms_per_step", "verify_pass", "draft_loop",
+                                         "tokens_per_round")}))
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr)
+    sd.spec_destroy(ctx)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
+    """The oracle (plain C, fp64, OpenMP over output features) on the host
+    cores: a few full speculative rounds of the same pair with an 8-token
+    prompt (prefill untimed).  Attention over an 8- instead of 1024-token
+    context is ~4% of the oracle's per-row work, so this bounds the sample
+    without changing what a round computes."""
+    import numpy as np
+    import oracle
+    import synth
+    import torch
+    t0 = time.time()
+    tb = synth.torch_to_bits(tw)
+    db = synth.torch_to_bits(dw)
+    log(f"host copies of the weights in {time.time() - t0:.1f}s")
+    T = oracle.Model(tcfg, tb)
+    Dm = oracle.Model(dcfg, db)
+    prompt = synth.prompt(tcfg.vocab, 8, seed=7)
+    # untimed prefill, then timed rounds: run spec_generate twice (n rounds
+    # and 0 rounds) and subtract, so the prefill is excluded.
+    n_new = 64
+    t0 = time.perf_counter()
+    oracle.spec_generate(T, Dm, prompt, 0, K, greedy=args.greedy, seed=synth.SEED_PHILOX)
+    t_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    out, nacc, st = _rounds(oracle, T, Dm, prompt, K, args)
+    t_all = time.perf_counter() - t0
+    t_rounds = max(t_all - t_pre, 1e-9)
+    rounds = st["rounds"]
+    val = rounds * gpu_tokens_per_round / t_rounds
+    return {"value": round(val, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rounds} speculative rounds (K={K} draft steps + {K + 1}-row verify + "
+                      f"accept/reject) of the same pair with an 8-token prompt, prefill excluded "
+                      f"({t_pre:.1f}s); tokens/round taken from the GPU run "
+                      f"({gpu_tokens_per_round:.3f}); oracle's own rounds emitted {st['emitted']}",
+            "seconds": round(t_rounds, 3)}
+
+
+def _rounds(oracle, T, Dm, prompt, K, args):
+    # n_new = 1 token per round minimum: ask for cpu_rounds tokens, which
+    # takes at most cpu_rounds rounds; the stats report the rounds run.
+    return oracle.spec_generate(T, Dm, prompt, args.cpu_rounds, K, greedy=args.greedy,
+                                seed=1003)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,8 +92,7 @@ typedef struct spec_init_params {
   int32_t max_seq;           /* token capacity of each KV cache (>= n_prompt + k_max + 1) */
   int32_t greedy;            /* 1: greedy checking ([en] Floor 4); 0: sampling at T = 1 (Floor 5) */
   int32_t use_graphs;        /* 1: replay draft/verify from captured hipGraphs; 0: plain launches */
-  int32_t profile_kernels;   /* 1: record hipEvents around every launch of the feed-forward
-                                gate/up GEMM (see spec_kernel_times) */
+  int32_t profile_kernels;   /* 1: start with profiling on (see spec_set_profiling) */
   uint64_t stream_id;        /* Philox counter word c (0 in normal use) */
   void* hip_stream;          /* hipStream_t to enqueue on; NULL: the context creates one */
 } spec_init_params;
@@ -183,10 +182,17 @@ int spec_get_state(spec_ctx* ctx, spec_state* out);
 /* Synchronises and copies committed tokens [0, n) (prompt included) to host. */
 int spec_get_history(spec_ctx* ctx, int32_t* host_out, int32_t n);
 
-/* With profile_kernels = 1: durations in ms of the feed-forward gate/up GEMM
+/* With profiling on: durations in ms of the feed-forward gate/up GEMM
  * launches of the most recent spec_draft and spec_verify calls, in launch
  * order (draft launches first).  Synchronises.  *n_out = count written. */
 int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out);
+
+/* Profiling switch.  When on, spec_draft and spec_verify launch their
+ * kernels directly (no graph replay) and record a hipEvent pair around every
+ * launch of the feed-forward gate/up GEMM, read back by spec_kernel_times;
+ * kernels and results are the same as with graphs.  Synchronises.  Also set
+ * at creation by spec_init_params.profile_kernels. */
+int spec_set_profiling(spec_ctx* ctx, int32_t enable);
 
 /* Stateless accept/reject over a batch of independent sequences (the rule of
  * spec_verify without the forward pass).

@@ -80,6 +80,7 @@ def lib():
         L.spec_get_state.argtypes = [_p, C.POINTER(SpecState)]
         L.spec_get_history.argtypes = [_p, _p, _i32]
         L.spec_kernel_times.argtypes = [_p, _p, _i32, C.POINTER(_i32)]
+        L.spec_set_profiling.argtypes = [_p, _i32]
         L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
                                          _p, _p]
         _lib = L
@@ -88,7 +89,7 @@ def lib():
 
 EXPORTED = ("spec_init", "spec_draft", "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
-            "spec_kernel_times", "spec_accept_reject")
+            "spec_kernel_times", "spec_set_profiling", "spec_accept_reject")
 
 
 def _check(rc: int, ctx=None):
@@ -198,6 +199,10 @@ def spec_kernel_times(ctx: Ctx, cap: int = 4096) -> np.ndarray:
     n = _i32()
     _check(lib().spec_kernel_times(ctx.handle, buf.ctypes.data, cap, C.byref(n)), ctx)
     return buf[: n.value].copy()
+
+
+def spec_set_profiling(ctx: Ctx, enable: bool) -> None:
+    _check(lib().spec_set_profiling(ctx.handle, int(bool(enable))), ctx)
 
 
 def spec_accept_reject(T, D, d, seed: int, pos, stream_id: int, greedy: bool, out, n_acc,

@@ -47,6 +47,48 @@ SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ------------------------------------------------- packed MFMA A operand --
+// Activations enter the skinny GEMM as the A operand of
+// v_mfma_f32_16x16x32_bf16: 16 rows x 32 k per 1 KiB block, lane l holding 8
+// bf16 of row l%16 at k = 32*kb + 8*(l/16) + 0..7.  Rows 0-7 carry the bf16
+// high part of the fp32 activation rows 0-7, rows 8-15 the bf16 low part
+// (x - hi), so products against bf16 weights keep ~16 mantissa bits.
+// Producers write this layout directly; [Kb][64 lanes][8] bf16 per matrix.
+SPEC_DEVICE size_t apack_index(int m, int part, int k) {
+  const int kk = k & 31;
+  const int lane = (m + 8 * part) + 16 * (kk >> 3);
+  return ((size_t)(k >> 5) * 64 + lane) * 8 + (kk & 7);
+}
+
+SPEC_DEVICE uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Stores 8 consecutive activations of row m starting at k0 (k0 % 8 == 0) as
+// their high and low bf16 parts: two 16-byte stores.
+SPEC_DEVICE void apack_store8(uint16_t* Ap, int m, int k0, const float* v) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16_rne(v[e]);
+    l[e] = f32_to_bf16_rne(v[e] - bf16_to_f32(h[e]));
+  }
+  *(uint4*)(Ap + apack_index(m, 0, k0)) =
+      make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                 pack_bf16x2(h[6], h[7]));
+  *(uint4*)(Ap + apack_index(m, 1, k0)) =
+      make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
+                 pack_bf16x2(l[6], l[7]));
+}
+
+// 8 bf16 gains starting at k0 -> fp32
+SPEC_DEVICE void load_gain8(const uint16_t* g, int k0, float* out) {
+  const uint4 v = *(const uint4*)(g + k0);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = bf16_to_f32((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+}
+
 // ---------------------------------------------------------------- Philox --
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 64x64->128-bit multiplies, key bumped by two Weyl constants between rounds.
@@ -147,28 +189,6 @@ SPEC_DEVICE T block_reduce(T v, T* lds /* >= 16 */, Op op) {
   for (int i = 1; i < nw; ++i) r = op(r, lds[i]);
   __syncthreads();
   return r;
-}
-
-// "Last block done" protocol for reductions across the blocks of one kernel:
-// every block publishes its partial, then counts itself in; the block that
-// brings the count to `expected` sees all partials and resets the counter
-// for the next launch.  Returns true in every thread of the last block.
-SPEC_DEVICE bool arrive_last(int32_t* counter, int32_t expected, int32_t* lds_flag) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const int32_t old = atomicAdd(counter, 1);
-    const bool last = (old == expected - 1);
-    if (last) {
-      __threadfence();
-      *counter = 0;
-    }
-    *lds_flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
 }
 
 }  // namespace spec

@@ -8,9 +8,11 @@
 // h / (n_q / n_kv); all query heads of a group and all rows share one read of
 // each key/value chunk.
 //
-// Split over keys: workgroup (chunk c, kv head h) handles 64 keys and writes,
-// per query, (max score, sum of exp, unnormalised value sum); the last
-// workgroup of head h merges the chunks in chunk order (deterministic).
+// Two launches, no inter-block waiting: (1) workgroup (chunk c, kv head h)
+// handles 64 keys and writes, per query, (max score, sum of exp,
+// unnormalised value sum); (2) one merge block per (kv head, slice) combines
+// the chunks in chunk order (deterministic) and writes the output rows as the
+// packed A operand of the O projection.
 #include "kernels.h"
 
 namespace spec {
@@ -23,9 +25,8 @@ size_t attn_lds_bytes(int hd, int qg_max) {
 
 constexpr int kMaxQPerWave = 16;
 
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int32_t s_flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, h = blockIdx.y;
   const int hd = a.hd;
@@ -116,34 +117,49 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < kAttnChunk; ++i) acc += pr[i] * bf16_to_f32(Vs[i * hd + e]);
     my_ws[(size_t)qi * (hd + 2) + 2 + e] = acc;
   }
-  __threadfence();
-  if (!arrive_last(a.counters + h, n_active, &s_flag)) return;
+}
 
-  // ---- merge chunks in order ----------------------------------------------
-  const float* base = a.ws + (size_t)h * a.max_chunks * a.qg_max * (hd + 2);
+// Merge the chunks of kv head h in chunk order; each thread produces 8
+// consecutive dims of one query vector and stores them packed (hi/lo bf16).
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int h = blockIdx.x;
+  const int hd = a.hd, G = a.n_q / a.n_kv;
+  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int n_keys = pos0 + n_rows;
+  const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
+  if (n_rows <= 0) return;
+  const int QG = G * n_rows, per = hd / 8;
+  const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+  if (idx >= QG * per) return;
+  const int qi = idx / per, e0 = (idx % per) * 8;
+  const float* base = a.ws + (size_t)h * a.max_chunks * a.qg_max * (hd + 2) + (size_t)qi * (hd + 2);
   const size_t cstride = (size_t)a.qg_max * (hd + 2);
-  for (int idx = tid; idx < QG * hd; idx += 256) {
-    const int qi = idx / hd, e = idx % hd;
-    const float* p = base + (size_t)qi * (hd + 2);
-    float M = -INFINITY;
-    for (int cc = 0; cc < n_active; ++cc) M = fmaxf(M, __builtin_nontemporal_load(p + cc * cstride));
-    float L = 0.0f, O = 0.0f;
-    for (int cc = 0; cc < n_active; ++cc) {
-      const float* pc = p + cc * cstride;
-      const float m = __builtin_nontemporal_load(pc);
-      if (m == -INFINITY) continue;
-      const float w = expf(m - M);
-      L += __builtin_nontemporal_load(pc + 1) * w;
-      O += __builtin_nontemporal_load(pc + 2 + e) * w;
-    }
-    const int r = qi / G, gi = qi % G;
-    a.o[(size_t)r * a.n_q * hd + (size_t)(h * G + gi) * hd + e] = O / L;
+  float M = -INFINITY;
+  for (int cc = 0; cc < n_active; ++cc) M = fmaxf(M, base[cc * cstride]);
+  float L = 0.0f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < n_active; ++cc) {
+    const float* pc = base + cc * cstride;
+    const float m = pc[0];
+    if (m == -INFINITY) continue;
+    const float w = expf(m - M);
+    L += pc[1] * w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] += pc[2 + e0 + e] * w;
   }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) O[e] *= inv;
+  const int r = qi / G, gi = qi % G;
+  apack_store8(a.Ap_out, r, (h * G + gi) * hd + e0, O);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_kernel, dim3(a.max_chunks, a.n_kv), dim3(256),
+  hipLaunchKernelGGL(attn_partial_kernel, dim3(a.max_chunks, a.n_kv), dim3(256),
                      attn_lds_bytes(a.hd, a.qg_max), s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per_head = a.qg_max * (a.hd / 8);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_kv, (per_head + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,26 +10,25 @@
 //  * W is repacked once (launch_pack) so that each 16-byte lane load of a
 //    wave is one B fragment of v_mfma_f32_16x16x32_bf16 and a wave's k-range
 //    is one contiguous span: [group][k-block][NB][64 lanes][8 bf16].
-//  * The A tile is 16 rows: rows 0-7 hold the bf16 high part of the fp32
-//    activations, rows 8-15 the bf16 low part (x - hi), so one MFMA gives
-//    ~16-bit-mantissa activations at no extra weight traffic.  It is staged in
-//    LDS once per workgroup, with the RMSNorm of the consumer applied on the
-//    fly from per-64-column sums of squares published by the producer.
-//  * A workgroup = 4 waves; each wave owns NB 16-column blocks and the whole
-//    k-range of its workgroup.  Column groups are split along K over `splits`
-//    workgroups; partials go to a workspace and the last workgroup to arrive
-//    sums them in split order (deterministic) and runs the epilogue.
+//  * A arrives already packed by its producer (see apack_index): bf16 high
+//    and low halves of up to 8 fp32 rows in one 16-row MFMA tile.  It is
+//    small and shared by every workgroup, so it is read from L2; lanes of
+//    rows the pass does not use skip the load.
+//  * A workgroup owns NB 16-column blocks for the whole of K; its waves split
+//    K and are reduced through LDS in wave order (deterministic, and no
+//    workgroup ever waits for another).
+//  * RMSNorm is folded in: the producer packs x * gain, and the row scale
+//    1/sqrt(mean(x^2) + eps) multiplies Y here, from per-workgroup sums of
+//    squares published by the producer.
 #include "kernels.h"
 
 namespace spec {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 SPEC_DEVICE bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 SPEC_DEVICE uint4 load_stream(const uint4* p) {
   // weights are read once per pass: non-temporal hint
@@ -37,41 +36,17 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-SPEC_DEVICE float4 load_nt_f4(const float* p) {
-  const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)p);
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-
-SPEC_DEVICE uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
-
-// Per-thread split of 8 fp32 values into bf16 (high or low part).
-SPEC_DEVICE uint4 split8(const float* v, int part) {
-  uint16_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t hi = f32_to_bf16_rne(v[e]);
-    h[e] = part ? f32_to_bf16_rne(v[e] - bf16_to_f32(hi)) : hi;
-  }
-  return make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-}
-
-constexpr int kUnroll = 8;
-
-template <int NB, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny(GemmArgs a) {
-  extern __shared__ uint4 lds_a[];  // [kcb][64]
+template <int NB, int W, int EPI>
+__global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
+  constexpr int YW = NB * 16;            // columns owned by the workgroup
+  constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : 4);  // k-blocks per batch of loads
+  __shared__ float s_red[W * NB * 128];
+  __shared__ float s_y[kMaxRows * YW];
   __shared__ float s_scale[kMaxRows];
-  __shared__ float s_red[4][kMaxRows];
-  __shared__ float s_red2[4][kMaxRows];
-  __shared__ int32_t s_flag;
+  __shared__ float s_part[kMaxRows][YW / 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x % a.splits;
-  const int wgg = blockIdx.x / a.splits;
-  const int kb0 = split * a.kcb;
-  const int kb1 = min(a.Kb, kb0 + a.kcb);
-  const int nkb = kb1 - kb0;
-
+  const int g = blockIdx.x;
   int n_rows = a.rows->n_rows;
   int row_base = 0;
   if (a.last_row_only) {
@@ -79,284 +54,217 @@ __global__ __launch_bounds__(256) void gemm_skinny(GemmArgs a) {
     n_rows = n_rows > 0 ? 1 : 0;
   }
 
-  // ---- prologue: RMSNorm scale per row (fixed summation order) ----------
+  // row scale of the consumer's RMSNorm (fixed summation order)
   if (tid < kMaxRows) {
     float sc = 1.0f;
     if (a.ssq != nullptr && tid < n_rows) {
       float ss = 0.0f;
-      for (int g = 0; g < a.ssq_groups; ++g) ss += a.ssq[g * kMaxRows + row_base + tid];
+      for (int q = 0; q < a.ssq_groups; ++q) ss += a.ssq[q * kMaxRows + row_base + tid];
       sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     }
     s_scale[tid] = sc;
   }
-  __syncthreads();
 
-  // ---- stage the A tile (hi rows 0-7, lo rows 8-15) ----------------------
-  for (int idx = tid; idx < nkb * 64; idx += 256) {
-    const int kbl = idx >> 6, l = idx & 63;
-    const int row = l & 15, m = row & 7, part = row >> 3;
-    uint4 packed = make_uint4(0, 0, 0, 0);
-    if (m < n_rows) {
-      const int k = (kb0 + kbl) * 32 + (l >> 4) * 8;
-      const float* xr = a.X + (size_t)(row_base + m) * a.ldx + k;
-      const float4 v0 = *(const float4*)xr;
-      const float4 v1 = *(const float4*)(xr + 4);
-      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if (a.ssq != nullptr) {
-        const float sc = s_scale[m];
-        const uint4 gv = *(const uint4*)(a.gain + k);
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = bf16_to_f32((uint16_t)(gw[e >> 1] >> ((e & 1) * 16)));
-          v[e] = v[e] * sc * g;
-        }
-      }
-      packed = split8(v, part);
-    }
-    lds_a[idx] = packed;
-  }
-  __syncthreads();
-
-  // ---- main loop: stream W, MFMA against the staged A tile ----------------
-  const int g = wgg * 4 + wave;
+  // ---- main loop: this wave's share of K ---------------------------------
+  const int kb0 = (a.Kb * wave) / W, kb1 = (a.Kb * (wave + 1)) / W;
+  const int am = lane & 7;  // activation row of this lane (hi rows 0-7, lo rows 8-15)
+  const bool aload = a.last_row_only ? (am == row_base) : (am < n_rows);
+  const uint4* ap = (const uint4*)a.Ap + lane;
+  const uint4* wp = (const uint4*)a.Wp + (size_t)g * a.Kb * NB * 64 + lane;
   floatx4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (g < a.n_groups) {
-    const uint4* wp = (const uint4*)a.Wp + ((size_t)g * a.Kb + kb0) * NB * 64 + lane;
-    int kb = 0;
-    for (; kb + kUnroll <= nkb; kb += kUnroll) {
-      uint4 b[kUnroll][NB];
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) {
+    uint4 av[U], wv[U][NB];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) b[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
+      for (int j = 0; j < NB; ++j) wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const bf16x8_t av = as_bf16x8(lds_a[(kb + u) * 64 + lane]);
+    for (int u = 0; u < U; ++u) av[u] = aload ? ap[(size_t)(kb + u) * 64] : make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(b[u][j]), acc[j], 0, 0, 0);
-      }
-    }
-    for (; kb < nkb; ++kb) {
-      uint4 b[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) b[j] = load_stream(wp + ((size_t)kb * NB + j) * 64);
-      const bf16x8_t av = as_bf16x8(lds_a[kb * 64 + lane]);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(b[j]), acc[j], 0, 0, 0);
-    }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(wv[u][j]),
+                                                         acc[j], 0, 0, 0);
   }
-
-  // ---- combine hi and lo rows: lane l < 32 gets rows 4*(l/16)+r ----------
-  float y[NB][4];
+  for (; kb < kb1; ++kb) {
+    uint4 wv[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) y[j][r] = acc[j][r] + __shfl_down(acc[j][r], 32);
-
-  // ---- split-K: publish partials, last workgroup reduces in split order ---
-  if (a.splits > 1) {
-    float* my = a.ws + ((size_t)(wgg * a.splits + split) * 4 + wave) * NB * 128;
-    if (lane < 32) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        *(float4*)(my + j * 128 + lane * 4) = make_float4(y[j][0], y[j][1], y[j][2], y[j][3]);
-    }
-    __threadfence();
-    if (!arrive_last(a.counters + wgg, a.splits, &s_flag)) return;
+    for (int j = 0; j < NB; ++j) wv[j] = load_stream(wp + ((size_t)kb * NB + j) * 64);
+    const uint4 av = aload ? ap[(size_t)kb * 64] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[j][r] = 0.0f;
-    if (lane < 32) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float* p = a.ws + ((size_t)(wgg * a.splits + s) * 4 + wave) * NB * 128;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const float4 v = load_nt_f4(p + j * 128 + lane * 4);
-          y[j][0] += v.x; y[j][1] += v.y; y[j][2] += v.z; y[j][3] += v.w;
-        }
-      }
-    }
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(wv[j]), acc[j], 0,
+                                                       0, 0);
   }
 
-  // ---- epilogues ----------------------------------------------------------
-  const int nl = lane & 15;           // column within the 16-block
-  const int mrow0 = 4 * ((lane >> 4) & 1);  // first of the lane's 4 rows (lanes < 32)
-  const bool lane_ok = lane < 32 && g < a.n_groups;
+  // ---- hi + lo rows, then the waves' partial sums in wave order ----------
+  // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); rows
+  // 8-15 (lanes 32-63) are the low-part products of rows 0-7.
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float4 v;  // shuffles run with every lane active
+    v.x = acc[j][0] + __shfl_down(acc[j][0], 32);
+    v.y = acc[j][1] + __shfl_down(acc[j][1], 32);
+    v.z = acc[j][2] + __shfl_down(acc[j][2], 32);
+    v.w = acc[j][3] + __shfl_down(acc[j][3], 32);
+    if (lane < 32) *(float4*)&s_red[((wave * NB + j) * 32 + lane) * 4] = v;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NB * 128; idx += W * 64) {
+    const int j = idx >> 7, ln = (idx >> 2) & 31, r = idx & 3;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += s_red[((w * NB + j) * 32 + ln) * 4 + r];
+    const int mm = 4 * (ln >> 4) + r;  // MFMA row = activation row
+    // with last_row_only the one used row (row_base) becomes output row 0
+    const int m = a.last_row_only ? (mm == row_base ? 0 : -1) : mm;
+    if (m >= 0) s_y[m * YW + j * 16 + (ln & 15)] = v * s_scale[m];
+  }
+  __syncthreads();
 
+  // ---- epilogues on the [8][YW] tile ---------------------------------------
+  const int col0 = g * YW;
   if constexpr (EPI == EPI_STORE) {
-    if (lane_ok) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mrow0 + r;
-          if (m < n_rows) a.out[(size_t)m * a.ldo + (size_t)(g * NB + j) * 16 + nl] = y[j][r];
-        }
+    for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
+      const int m = idx / YW, c = idx % YW;
+      a.out[(size_t)m * a.ldo + col0 + c] = s_y[m * YW + c];
     }
-  } else if constexpr (EPI == EPI_SILU) {
-    static_assert(NB == 2, "gate/up epilogue pairs two blocks");
-    if (lane_ok) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mrow0 + r;
-        if (m < n_rows) {
-          const float gt = y[0][r], up = y[1][r];
-          a.out[(size_t)m * a.ldo + (size_t)g * 16 + nl] = gt / (1.0f + expf(-gt)) * up;
-        }
+  } else if constexpr (EPI == EPI_LOGITS) {
+    for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
+      const int m = idx / YW, c = idx % YW;
+      if (col0 + c < a.n_valid) a.out[(size_t)m * a.ldo + col0 + c] = s_y[m * YW + c];
+    }
+    if (tid < kMaxRows) {
+      const int m = tid;
+      float M = -INFINITY, S = 0.0f;
+      if (m < n_rows) {
+        for (int c = 0; c < YW; ++c)
+          if (col0 + c < a.n_valid) M = fmaxf(M, s_y[m * YW + c]);
+        for (int c = 0; c < YW; ++c)
+          if (col0 + c < a.n_valid) S += expf(s_y[m * YW + c] - M);
       }
+      a.lm_part[g * kMaxRows + m] = make_float2(M, S);
     }
   } else if constexpr (EPI == EPI_RESID) {
-    static_assert(NB == 1, "residual epilogue publishes 64-column norm partials");
-    float sq[4] = {0.f, 0.f, 0.f, 0.f};
-    if (lane_ok) {
+    // x += y; next GEMM's packed A = x * gain_next; sums of squares of x
+    constexpr int C8 = YW / 8;
+    for (int idx = tid; idx < kMaxRows * C8; idx += W * 64) {
+      const int m = idx / C8, c8 = idx % C8;
+      float sq = 0.0f;
+      if (m < n_rows) {
+        const int k0 = col0 + c8 * 8;
+        float* px = a.resid + (size_t)m * a.ldr + k0;
+        const float4 x0 = *(const float4*)px, x1 = *(const float4*)(px + 4);
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float gn[8], xg[8];
+        load_gain8(a.gain_next, k0, gn);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mrow0 + r;
-        if (m < n_rows) {
-          float* px = a.resid + (size_t)m * a.ldr + (size_t)g * 16 + nl;
-          const float nx = *px + y[0][r];
-          *px = nx;
-          sq[r] = nx * nx;
+        for (int e = 0; e < 8; ++e) {
+          x[e] += s_y[m * YW + c8 * 8 + e];
+          sq += x[e] * x[e];
+          xg[e] = x[e] * gn[e];
         }
+        *(float4*)px = make_float4(x[0], x[1], x[2], x[3]);
+        *(float4*)(px + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        apack_store8(a.Ap_out, m, k0, xg);
       }
-    }
-    // sum over the 16 columns of the block (lanes sharing lane>>4), fixed tree
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int msk = 8; msk >= 1; msk >>= 1) sq[r] += __shfl_xor(sq[r], msk);
-    }
-    if (lane == 0 || lane == 16) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_red[wave][mrow0 + r] = sq[r];
-    }
-    __syncthreads();
-    if (tid < kMaxRows)
-      a.ssq_out[wgg * kMaxRows + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
-  } else if constexpr (EPI == EPI_LOGITS) {
-    float mx[4], sm[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mrow0 + r;
-      const int col = g * 16 + nl;
-      const bool ok = lane_ok && m < n_rows && col < a.n_valid;
-      if (ok) a.out[(size_t)m * a.ldo + col] = y[0][r];
-      mx[r] = ok ? y[0][r] : -INFINITY;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int msk = 8; msk >= 1; msk >>= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], msk));
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mrow0 + r;
-      const int col = g * 16 + nl;
-      const bool ok = lane_ok && m < n_rows && col < a.n_valid;
-      sm[r] = ok ? expf(y[0][r] - mx[r]) : 0.0f;
-#pragma unroll
-      for (int msk = 8; msk >= 1; msk >>= 1) sm[r] += __shfl_xor(sm[r], msk);
-    }
-    if (lane == 0 || lane == 16) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s_red[wave][mrow0 + r] = mx[r];
-        s_red2[wave][mrow0 + r] = sm[r];
-      }
+      s_part[m][c8] = sq;
     }
     __syncthreads();
     if (tid < kMaxRows) {
-      float M = s_red[0][tid];
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, s_red[w][tid]);
-      float S = 0.0f;
-      if (M != -INFINITY) {
-        for (int w = 0; w < 4; ++w)
-          if (s_red[w][tid] != -INFINITY) S += s_red2[w][tid] * expf(s_red[w][tid] - M);
+      float s = 0.0f;
+      for (int c8 = 0; c8 < C8; ++c8) s += s_part[tid][c8];
+      a.ssq_out[g * kMaxRows + tid] = s;
+    }
+  } else if constexpr (EPI == EPI_SILU) {
+    static_assert(NB % 2 == 0, "gate/up epilogue pairs blocks");
+    // blocks 2p / 2p+1 hold gate / up of features (g*NB/2 + p)*16 + 0..15
+    for (int idx = tid; idx < n_rows * NB; idx += W * 64) {
+      const int m = idx / NB, rest = idx % NB;
+      const int p = rest >> 1, half = rest & 1;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gt = s_y[m * YW + (2 * p) * 16 + half * 8 + e];
+        const float up = s_y[m * YW + (2 * p + 1) * 16 + half * 8 + e];
+        v[e] = gt / (1.0f + expf(-gt)) * up;
       }
-      a.lm_part[wgg * kMaxRows + tid] = make_float2(M, S);
+      apack_store8(a.Ap_out, m, (g * (NB / 2) + p) * 16 + half * 8, v);
     }
   } else if constexpr (EPI == EPI_QKV) {
-    static_assert(NB == 1, "qkv epilogue works on single blocks");
-    if (g < a.n_groups) {
-      const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
-      const int half_hd = a.head_dim / 2;
-      const int pos0 = a.rows->pos0;
-      if (g < q_blocks + k_blocks) {
+    const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
+    const int half_hd = a.head_dim / 2;
+    const int pos0 = a.rows->pos0;
+    for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
+      const int m = idx / YW, c = idx % YW;
+      const int b = g * NB + c / 16, w = c % 16;
+      const int pos = pos0 + m;
+      if (pos >= a.max_seq) continue;
+      const float mine = s_y[m * YW + c];
+      if (b < q_blocks + k_blocks) {
         // pair-interleaved block: columns w and w^8 are the two halves of one pair
-        const bool is_q = g < q_blocks;
-        const int bl = is_q ? g : g - q_blocks;
-        const int pair = bl * 8 + (nl & 7), half = nl >> 3;
+        const bool is_q = b < q_blocks;
+        const int bl = is_q ? b : b - q_blocks;
+        const int pair = bl * 8 + (w & 7), hf = w >> 3;
         const int head = pair / half_hd, jj = pair % half_hd;
-        const double f = a.inv_freq[jj];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float mine = y[0][r];
-          const float other = __shfl_xor(mine, 8);
-          const int m = mrow0 + r;
-          const int pos = pos0 + m;
-          if (lane < 32 && m < n_rows && pos < a.max_seq) {
-            double sn, cs;
-            sincos((double)pos * f, &sn, &cs);
-            const double lo = half ? (double)other : (double)mine;
-            const double hi = half ? (double)mine : (double)other;
-            const float val = (float)(half ? hi * cs + lo * sn : lo * cs - hi * sn);
-            const int dim = jj + half * half_hd;
-            if (is_q) {
-              a.out[(size_t)m * a.ldo + (size_t)head * a.head_dim + dim] = val;
-            } else {
-              const int blk = a.block_table[pos / kBlock];
-              a.k_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
-                  f32_to_bf16_rne(val);
-            }
-          }
+        const float other = s_y[m * YW + (c ^ 8)];
+        double sn, cs;
+        sincos((double)pos * a.inv_freq[jj], &sn, &cs);
+        const double lo = hf ? (double)other : (double)mine;
+        const double hi = hf ? (double)mine : (double)other;
+        const float val = (float)(hf ? hi * cs + lo * sn : lo * cs - hi * sn);
+        const int dim = jj + hf * half_hd;
+        if (is_q) {
+          a.out[(size_t)m * a.ldo + (size_t)head * a.head_dim + dim] = val;
+        } else {
+          const int blk = a.block_table[pos / kBlock];
+          a.k_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
+              f32_to_bf16_rne(val);
         }
       } else {
-        const int f0 = (g - q_blocks - k_blocks) * 16 + nl;
+        const int f0 = (b - q_blocks - k_blocks) * 16 + w;
         const int head = f0 / a.head_dim, dim = f0 % a.head_dim;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mrow0 + r;
-          const int pos = pos0 + m;
-          if (lane < 32 && m < n_rows && pos < a.max_seq) {
-            const int blk = a.block_table[pos / kBlock];
-            a.v_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
-                f32_to_bf16_rne(y[0][r]);
-          }
-        }
+        const int blk = a.block_table[pos / kBlock];
+        a.v_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
+            f32_to_bf16_rne(mine);
       }
     }
   }
 }
 
-template <int NB, int EPI>
-static hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  const int n_wgg = (a.n_groups + 3) / 4;
-  hipLaunchKernelGGL((gemm_skinny<NB, EPI>), dim3(n_wgg * a.splits), dim3(256),
-                     gemm_lds_bytes(a.kcb), s, a);
+template <int NB, int W>
+static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_groups), block(W * 64);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE>), grid, block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID>), grid, block, 0, s, a); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV>), grid, block, 0, s, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS>), grid, block, 0, s, a); break;
+    case EPI_SILU:
+      if constexpr (NB % 2 == 0) {
+        hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int nb, int epi, const GemmArgs& a, hipStream_t s) {
-  if (nb == 1) {
-    switch (epi) {
-      case EPI_STORE: return launch_one<1, EPI_STORE>(a, s);
-      case EPI_RESID: return launch_one<1, EPI_RESID>(a, s);
-      case EPI_QKV: return launch_one<1, EPI_QKV>(a, s);
-      case EPI_LOGITS: return launch_one<1, EPI_LOGITS>(a, s);
-      default: break;
-    }
-  } else if (nb == 2) {
-    switch (epi) {
-      case EPI_STORE: return launch_one<2, EPI_STORE>(a, s);
-      case EPI_SILU: return launch_one<2, EPI_SILU>(a, s);
-      default: break;
-    }
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) {
+  if (sh.waves == 4) {
+    if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s);
+    if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s);
+    if (sh.nb == 4) return launch_epi<4, 4>(epi, a, s);
+  } else if (sh.waves == 8) {
+    if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s);
+    if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s);
+    if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s);
   }
   return hipErrorInvalidValue;
 }

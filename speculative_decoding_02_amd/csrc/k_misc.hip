@@ -1,5 +1,5 @@
 // k_misc.hip -- embedding gather, LM-head softmax normalisation, the
-// accept/reject kernel (also used to sample draft tokens) and the commit.
+// accept/reject kernels (also used to sample draft tokens) and the commit.
 #include "kernels.h"
 
 namespace spec {
@@ -7,9 +7,11 @@ namespace spec {
 // ============================================================ embedding ==
 // Decides the rows of a pass from the device state (so captured graphs can be
 // replayed whatever the previous round accepted), gathers their embedding
-// rows into the fp32 residual stream and publishes per-64-column sums of
-// squares for the first RMSNorm.  Grid: one block per possible row.
-__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+// rows into the fp32 residual stream, writes x * gain (first RMSNorm gain) as
+// the packed A operand of the QKV projection, and publishes per-64-column
+// sums of squares.  Grid: one block of 64 threads per 64 columns; thread t
+// handles row t/8, columns 8*(t%8)..+7.
+__global__ __launch_bounds__(64) void embed_kernel(EmbedArgs a) {
   const int LT = a.st->LT, LD = a.st->LD;
   int n_rows = 0, pos0 = 0;
   int tok[kMaxRows];
@@ -53,30 +55,43 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     for (int r = 0; r < kMaxRows; ++r) a.rows_out->tok[r] = tok[r];
     if (err) atomicOr(&a.st->err, err);
   }
-  const int r = blockIdx.x;
-  if (r >= n_rows) return;
-  const uint16_t* e = a.E + (size_t)tok[r] * a.d;
-  float* x = a.x + (size_t)r * a.d;
-  for (int k = threadIdx.x; k < a.d; k += blockDim.x) x[k] = bf16_to_f32(e[k]);
-  // each thread owns whole 64-column groups: sequential sums, deterministic
-  for (int gi = threadIdx.x; gi < a.d / 64; gi += blockDim.x) {
-    float s = 0.0f;
-    for (int k = 0; k < 64; ++k) {
-      const float v = bf16_to_f32(e[gi * 64 + k]);
-      s += v * v;
+  const int r = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  const int k0 = blockIdx.x * 64 + cg * 8;
+  float sq = 0.0f;
+  if (r < n_rows) {
+    int tk = tok[0];
+    for (int i = 1; i < kMaxRows; ++i)
+      if (i == r) tk = tok[i];
+    const uint4 ev = *(const uint4*)(a.E + (size_t)tk * a.d + k0);
+    const uint32_t w[4] = {ev.x, ev.y, ev.z, ev.w};
+    float x[8], gn[8], xg[8];
+    load_gain8(a.gain, k0, gn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = bf16_to_f32((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+      sq += x[e] * x[e];
+      xg[e] = x[e] * gn[e];
     }
-    a.ssq[gi * kMaxRows + r] = s;
+    float* px = a.x + (size_t)r * a.d + k0;
+    *(float4*)px = make_float4(x[0], x[1], x[2], x[3]);
+    *(float4*)(px + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    apack_store8(a.Ap_out, r, k0, xg);
   }
+  // sum over the 8 threads of the row (fixed butterfly)
+  sq += __shfl_xor(sq, 4);
+  sq += __shfl_xor(sq, 2);
+  sq += __shfl_xor(sq, 1);
+  if (cg == 0) a.ssq[blockIdx.x * kMaxRows + r] = sq;
 }
 
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(kMaxRows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(embed_kernel, dim3(a.d / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 // ============================================================== softmax ==
 // T_i = softmax(logits_i) at temperature 1 ([en] Floor 5: the target's
-// wheel).  The LM-head GEMM left per-64-column (max, sum exp) partials; each
+// wheel).  The LM-head GEMM left per-workgroup (max, sum exp) partials; each
 // block folds them in a fixed order, then normalises its chunk of the row.
 __global__ __launch_bounds__(256) void softmax_kernel(SoftmaxArgs a) {
   __shared__ float s_m[16], s_s[16];
@@ -107,43 +122,31 @@ hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, hipStream_t s) {
 
 // ======================================================== accept/reject ==
 // The rule of [int] algorithm core Steps 3-4 / [en] Floors 4-5, per
-// sequence b, split over vocabulary chunks:
-//  1. every block gathers T_i(d_i), D_i(d_i) and decides the K exact accept
-//     tests r_i * D_i(d_i) < T_i(d_i) (r_i = Philox w1 at the draft's
-//     position); a wave ballot gives the first reject j (j = K: none);
-//  2. each block scans its chunk of the row to sample from: the residual
-//     fix(T_j) - fix(D_j) (saturating, 2^-40 grid) on a reject, else the
-//     bonus row fix(T_K); integer sums are order-free, so the result does not
-//     depend on the reduction tree; the fallbacks (sum of fix(T_j), argmax
-//     of the row) are gathered in the same pass;
-//  3. the last block to finish folds the chunk partials in chunk order, finds
-//     the chunk holding the inverse-CDF needle floor(u24 * Z / 2^24)
-//     (u24 = Philox w2 at the decided position), rescans that chunk and
-//     writes the emitted tokens.
-// Greedy mode replaces 1-2 by per-chunk argmaxes of every row.
+// sequence b, in two launches:
+//  1. partial kernel, one block per (vocabulary chunk, sequence): decide the
+//     K exact accept tests r_i * D_i(d_i) < T_i(d_i) (r_i = Philox w1 at the
+//     draft's position); a wave ballot gives the first reject j (j = K:
+//     none).  Then sum, over the chunk, the integer weights of the row to
+//     sample from: the residual fix(T_j) - fix(D_j) (saturating, 2^-40 grid)
+//     on a reject, else the bonus row fix(T_K); integer sums are order-free,
+//     so the result does not depend on the reduction tree.  The fallbacks
+//     (sum of fix(T_j), argmax of the row) are gathered in the same pass.
+//  2. finish kernel, one block per sequence: repeat the accept tests, fold
+//     the chunk partials in chunk order, find the chunk holding the
+//     inverse-CDF needle floor(u24 * Z / 2^24) (u24 = Philox w2 at the
+//     decided position), rescan that chunk and write the emitted tokens.
+// Greedy mode replaces the sums by per-chunk argmaxes of every row.
 // K = 0 samples one row (draft tokens, word w0).
-struct ArPart {
-  uint64_t z_res, z_t, amax;
-  uint64_t bad;
-};
 
-__global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
-  __shared__ int32_t s_j, s_err, s_flag;
-  __shared__ uint64_t s_u64[16];
-  __shared__ uint64_t s_scan[256];
-  __shared__ int32_t s_tok;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int K = a.K, V = a.V;
-  const uint64_t P = a.pos ? a.pos[b] : (uint64_t)(a.st->LT + a.pos_offset);
-  const float* Tb = a.T + (size_t)b * (K + 1) * V;
-  const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
-  const int32_t* db = a.d + (size_t)b * K;
-  const int W = ar_ws_words(K);
-  uint64_t* ws_b = a.ws + (size_t)b * a.n_chunks * W;
-
-  // ---- 1. drafts and accept tests (wave 0; K < 64) ------------------------
-  if (wave == 0) {
+// Accept tests and draft validation (wave 0).  Returns j (first reject, K if
+// none; K in greedy mode) and whether the inputs read so far are invalid.
+SPEC_DEVICE void decide_first_reject(const ArArgs& a, int b, uint64_t P, int* s_j, int* s_err) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    const int K = a.K, V = a.V;
+    const float* Tb = a.T + (size_t)b * (K + 1) * V;
+    const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
+    const int32_t* db = a.d + (size_t)b * K;
     bool bad_d = false, stop = false, invalid = false;
     if (lane < K) {
       const int di = db[lane];
@@ -162,15 +165,32 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
     const int j = st ? __ffsll((long long)st) - 1 : K;
     const uint64_t inv = __ballot(invalid);
     if (lane == 0) {
-      s_j = a.greedy ? K : j;
-      s_err = (bd != 0) || (!a.greedy && j < K && ((inv >> j) & 1));
+      *s_j = a.greedy ? K : j;
+      *s_err = (bd != 0) || (!a.greedy && j < K && ((inv >> j) & 1));
     }
   }
   __syncthreads();
+}
+
+SPEC_DEVICE uint64_t seq_pos(const ArArgs& a, int b) {
+  return a.pos ? a.pos[b] : (uint64_t)(a.st->LT + a.pos_offset);
+}
+
+__global__ __launch_bounds__(256) void ar_partial_kernel(ArArgs a) {
+  __shared__ int32_t s_j, s_err;
+  __shared__ uint64_t s_u64[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int K = a.K, V = a.V;
+  const uint64_t P = seq_pos(a, b);
+  const float* Tb = a.T + (size_t)b * (K + 1) * V;
+  const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
+  const int W = ar_ws_words(K);
+  uint64_t* p = a.ws + ((size_t)b * a.n_chunks + c) * W;
+  decide_first_reject(a, b, P, &s_j, &s_err);
   const int j = s_j;
   const int lo = c * a.chunk, hi = min(V, lo + a.chunk);
 
-  // ---- 2. chunk partials ---------------------------------------------------
   if (!a.greedy) {
     uint64_t zr = 0, zt = 0, am = 0, bad = 0;
     if (!s_err) {
@@ -201,14 +221,14 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      uint64_t* p = ws_b + (size_t)c * W;
       p[0] = s_u64[0] + s_u64[1] + s_u64[2] + s_u64[3];
       p[1] = s_u64[4] + s_u64[5] + s_u64[6] + s_u64[7];
       p[2] = max(max(s_u64[8], s_u64[9]), max(s_u64[10], s_u64[11]));
       p[3] = s_u64[12] | s_u64[13] | s_u64[14] | s_u64[15];
     }
   } else {
-    // greedy: per-row argmax keys of this chunk, rows 0..K
+    // per-row argmax keys of this chunk, rows 0..K, and an invalid-value flag
+    uint64_t bad_all = 0;
     for (int i = 0; i <= K; ++i) {
       const float* Tr = Tb + (size_t)i * V;
       uint64_t am = 0, bad = 0;
@@ -222,28 +242,41 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
       if (lane == 0) { s_u64[wave] = am; s_u64[4 + wave] = bad; }
       __syncthreads();
       if (tid == 0) {
-        uint64_t* p = ws_b + (size_t)c * W;
         p[i] = max(max(s_u64[0], s_u64[1]), max(s_u64[2], s_u64[3]));
-        if (i == 0) p[K + 1] = 0;
-        p[K + 1] |= s_u64[4] | s_u64[5] | s_u64[6] | s_u64[7];
+        bad_all |= s_u64[4] | s_u64[5] | s_u64[6] | s_u64[7];
       }
       __syncthreads();
     }
+    if (tid == 0) p[K + 1] = bad_all;
   }
-  __threadfence();
-  if (!arrive_last(a.counters + b, a.n_chunks, &s_flag)) return;
+}
 
-  // ---- 3. last block: fold partials, sample, emit ---------------------------
+__global__ __launch_bounds__(256) void ar_finish_kernel(ArArgs a) {
+  __shared__ int32_t s_j, s_err, s_tok, s_c, s_bad;
+  __shared__ uint64_t s_u64[4];
+  __shared__ uint64_t s_before;
+  __shared__ uint64_t s_scan[256];
+  __shared__ int32_t s_am[64];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int K = a.K, V = a.V;
+  const uint64_t P = seq_pos(a, b);
+  const float* Tb = a.T + (size_t)b * (K + 1) * V;
+  const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
+  const int32_t* db = a.d + (size_t)b * K;
+  const int W = ar_ws_words(K);
+  const uint64_t* ws_b = a.ws + (size_t)b * a.n_chunks * W;
   int32_t* ob = a.out + (size_t)b * (K + 1);
+  decide_first_reject(a, b, P, &s_j, &s_err);
+  const int j = s_j;
+
   if (a.greedy) {
-    __shared__ int32_t s_am[64];
-    __shared__ int32_t s_bad;
     if (tid == 0) s_bad = 0;
     __syncthreads();
     for (int i = tid; i <= K + 1; i += 256) {
       uint64_t acc = 0;
       for (int cc = 0; cc < a.n_chunks; ++cc) {
-        const uint64_t v = __builtin_nontemporal_load(ws_b + (size_t)cc * W + i);
+        const uint64_t v = ws_b[(size_t)cc * W + i];
         acc = (i <= K) ? max(acc, v) : (acc | v);
       }
       if (i <= K) s_am[i] = (int32_t)argmax_key_index(acc);
@@ -269,10 +302,10 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
     uint64_t zr = 0, zt = 0, am = 0, bad = s_err;
     for (int cc = 0; cc < a.n_chunks; ++cc) {
       const uint64_t* p = ws_b + (size_t)cc * W;
-      zr += __builtin_nontemporal_load(p + 0);
-      zt += __builtin_nontemporal_load(p + 1);
-      am = max(am, __builtin_nontemporal_load(p + 2));
-      bad |= __builtin_nontemporal_load(p + 3);
+      zr += p[0];
+      zt += p[1];
+      am = max(am, p[2]);
+      bad |= p[3];
     }
     s_u64[0] = zr; s_u64[1] = zt; s_u64[2] = am; s_u64[3] = bad;
     s_tok = -1;
@@ -290,14 +323,11 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
     const uint32_t u = uniform_u24(a.seed, P + j, b, a.stream_id, a.word);
     const uint64_t Z = use == 0 ? zr : zt;
     const uint64_t t = icdf_needle(u, Z);
-    // chunk holding the needle
-    __shared__ int32_t s_c;
-    __shared__ uint64_t s_before;
     if (tid == 0) {
       uint64_t cum = 0;
       int cs = a.n_chunks - 1;
       for (int cc = 0; cc < a.n_chunks; ++cc) {
-        const uint64_t zc = __builtin_nontemporal_load(ws_b + (size_t)cc * W + use);
+        const uint64_t zc = ws_b[(size_t)cc * W + use];
         if (cum + zc > t) { cs = cc; break; }
         cum += zc;
       }
@@ -309,8 +339,7 @@ __global__ __launch_bounds__(256) void accept_reject_kernel(ArArgs a) {
     const uint64_t before = s_before;
     // rescan chunk cs: contiguous segment per thread, exclusive scan over threads
     const int clo = cs * a.chunk, chi = min(V, clo + a.chunk);
-    const int len = chi - clo;
-    const int per = (len + 255) / 256;
+    const int per = (chi - clo + 255) / 256;
     const int slo = clo + tid * per, shi = min(chi, slo + per);
     const float* Tr = Tb + (size_t)j * V;
     const float* Dr = (j < K && use == 0) ? Db + (size_t)j * V : nullptr;
@@ -375,7 +404,10 @@ void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks) {
 }
 
 hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(accept_reject_kernel, dim3(a.n_chunks, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(ar_partial_kernel, dim3(a.n_chunks, a.B), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ar_finish_kernel, dim3(a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

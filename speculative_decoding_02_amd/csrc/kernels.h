@@ -1,5 +1,7 @@
 // kernels.h -- launch-argument structs and host-side launchers of the HIP
-// kernels (one translation unit per kernel family).
+// kernels (one translation unit per kernel family).  No kernel waits on, or
+// synchronises with, another workgroup of the same launch: every cross-block
+// reduction goes through a kernel boundary.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -11,41 +13,38 @@ namespace spec {
 // ------------------------------------------------------------------ GEMM --
 // Epilogue kinds of the skinny GEMM Y[m][n] = sum_k A[m][k] W[n][k].
 enum Epi : int {
-  EPI_STORE = 0,   // out[m][n] = y
-  EPI_RESID = 1,   // resid[m][n] += y; per-64-column sums of squares for the next RMSNorm
-  EPI_SILU = 2,    // out[m][f] = silu(gate) * up   (NB = 2: gate block, up block)
+  EPI_STORE = 0,   // out[m][n] = y (fp32)
+  EPI_RESID = 1,   // resid[m][n] += y; packed (resid * gain_next) for the next GEMM;
+                   // per-workgroup sums of squares for the next RMSNorm
+  EPI_SILU = 2,    // packed silu(gate) * up for the down projection (blocks alternate gate/up)
   EPI_QKV = 3,     // RoPE on q/k, q -> out, k/v -> paged KV cache
-  EPI_LOGITS = 4,  // out[m][n] = logit; per-64-column (max, sum exp) partials
+  EPI_LOGITS = 4,  // out[m][n] = logit; per-workgroup (max, sum exp) partials
 };
 
 struct GemmArgs {
   // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16]
   const uint16_t* Wp;
-  int n_groups;      // groups of NB 16-column blocks
+  int n_groups;      // one workgroup per group of NB 16-column blocks
   int Kb;            // K / 32
-  int kcb;           // k-blocks staged per workgroup
-  int splits;        // workgroups along K per column group
-  // A operand: fp32 rows [n_rows][K] with row stride ldx, optional RMSNorm
-  const float* X;
-  int ldx;
-  const float* ssq;  // [ssq_groups][8] partial sums of squares, or null (no norm)
-  int ssq_groups;
-  const uint16_t* gain;  // [K] bf16 norm gain (with ssq)
-  float eps;
   int K;
+  // A operand: packed rows (see apack_index) of length K
+  const uint16_t* Ap;
   const PassRows* rows;
   int last_row_only;  // use only row n_rows-1 (written as output row 0)
-  // split-K workspace
-  float* ws;
-  int32_t* counters;
+  // RMSNorm of the consumer: y[m][.] *= 1/sqrt(sum_g ssq[g][m] / K + eps)
+  const float* ssq;   // [ssq_groups][8] or null (no norm)
+  int ssq_groups;
+  float eps;
   // epilogue
   float* out;
   int ldo;
-  float* resid;
+  float* resid;       // EPI_RESID: fp32 residual rows [8][ldr]
   int ldr;
-  float* ssq_out;
-  float2* lm_part;   // EPI_LOGITS partials [n_wgg][8]
-  int n_valid;       // EPI_LOGITS: valid columns (vocab)
+  const uint16_t* gain_next;  // EPI_RESID: gain of the next RMSNorm (bf16 [N])
+  uint16_t* Ap_out;   // EPI_RESID / EPI_SILU: packed A rows for the next GEMM
+  float* ssq_out;     // EPI_RESID: [n_groups][8]
+  float2* lm_part;    // EPI_LOGITS: [n_groups][8]
+  int n_valid;        // EPI_LOGITS: valid columns (vocab)
   // EPI_QKV
   int q_dim, kv_dim, head_dim, n_kv;
   uint16_t* k_cache;
@@ -55,9 +54,11 @@ struct GemmArgs {
   int max_seq;
 };
 
-// Dynamic LDS bytes the GEMM needs for a given kcb.
-inline size_t gemm_lds_bytes(int kcb) { return (size_t)kcb * 64 * 16; }
-hipError_t launch_gemm(int nb, int epi, const GemmArgs& a, hipStream_t s);
+struct GemmShape {
+  int nb;      // 16-column blocks per workgroup
+  int waves;   // waves per workgroup, splitting K
+};
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
 
 // Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
 // layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
@@ -72,11 +73,10 @@ struct AttnArgs {
   const int32_t* block_table;
   const PassRows* rows;
   int n_q, n_kv, hd;
-  int max_chunks;            // grid.x; chunks of kAttnChunk keys
-  float* o;                  // [n_rows][n_q*hd]
+  int max_chunks;            // grid.x of the partial kernel
   float* ws;                 // [n_kv][max_chunks][qg_max][hd+2]
-  int32_t* counters;         // [n_kv]
   int qg_max;                // (n_q/n_kv) * kMaxRows
+  uint16_t* Ap_out;          // packed attention output rows (K = n_q*hd) for the O projection
 };
 constexpr int kAttnChunk = 64;
 size_t attn_lds_bytes(int hd, int qg_max);
@@ -97,8 +97,10 @@ struct EmbedArgs {
   const int32_t* dtok;
   int mode, n_rows, pos0, step;
   PassRows* rows_out;
-  float* x;           // [8][d]
-  float* ssq;         // [d/64][8]
+  float* x;               // [8][d]
+  const uint16_t* gain;   // first RMSNorm gain [d]
+  uint16_t* Ap_out;       // packed x * gain
+  float* ssq;             // [d/64][8]
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 
@@ -129,11 +131,11 @@ struct ArArgs {
   int chunk, n_chunks;
   int32_t* out;          // [B][K+1]
   int32_t* n_acc;        // [B] or null
-  uint64_t* ws;          // [B][n_chunks][ar_ws_words(K)]
-  int32_t* counters;     // [B]
+  uint64_t* ws;          // [B][n_chunks][ar_ws_words(K)] chunk partials
 };
 __host__ __device__ inline int ar_ws_words(int K) { return (K + 2) > 4 ? (K + 2) : 4; }
 void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks);
+// Two launches: chunk partials, then one finishing block per sequence.
 hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- commit --

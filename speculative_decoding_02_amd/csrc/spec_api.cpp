@@ -37,34 +37,18 @@ std::string fmt(const char* f, ...) {
 }
 
 // ------------------------------------------------------------ GEMM plans --
+// One workgroup per group of `nb` 16-column blocks, `waves` waves splitting K.
 struct GemmPlan {
-  int nb = 1, n_groups = 0, n_wgg = 0, Kb = 0, kcb = 0, splits = 1;
-  size_t ws_floats() const { return (size_t)n_wgg * splits * 4 * nb * 128; }
+  GemmShape shape{1, 4};
+  int n_groups = 0, Kb = 0;
 };
 
 GemmPlan plan_gemm(int n_cols, int nb, int K) {
   GemmPlan p;
-  p.nb = nb;
-  p.n_groups = n_cols / (16 * nb);
-  p.n_wgg = (p.n_groups + 3) / 4;
+  p.shape.nb = nb;
   p.Kb = K / 32;
-  const int kcb_max = 32;  // 32 KiB of staged activations per workgroup
-  static const int env_kcb = [] {
-    const char* e = getenv("SPEC_GEMM_KCB");
-    return e ? atoi(e) : 0;
-  }();
-  int S;
-  if (env_kcb > 0) {
-    S = (p.Kb + env_kcb - 1) / env_kcb;
-  } else {
-    const int s_min = (p.Kb + kcb_max - 1) / kcb_max;
-    const int s_fill = (512 + p.n_wgg - 1) / p.n_wgg;
-    const int s_cap = std::max(1, p.Kb / 8);
-    S = std::max(s_min, std::min(s_fill, s_cap));
-  }
-  S = std::max(1, std::min(S, p.Kb));
-  p.kcb = (p.Kb + S - 1) / S;
-  p.splits = (p.Kb + p.kcb - 1) / p.kcb;
+  p.n_groups = n_cols / (16 * nb);
+  p.shape.waves = p.Kb >= 64 ? 8 : 4;
   return p;
 }
 
@@ -72,7 +56,7 @@ struct Mat {
   uint16_t* p = nullptr;  // packed (inside the model arena)
   GemmPlan plan;
   int K = 0, N = 0;
-  size_t elems() const { return (size_t)plan.n_groups * plan.Kb * plan.nb * 64 * 8; }
+  size_t elems() const { return (size_t)plan.n_groups * plan.Kb * plan.shape.nb * 64 * 8; }
 };
 
 struct Model {
@@ -97,7 +81,6 @@ struct Model {
 
 struct GraphEntry {
   hipGraphExec_t exec = nullptr;
-  std::vector<hipEvent_t> events;  // pairs around profiled launches
 };
 
 }  // namespace
@@ -109,14 +92,13 @@ struct spec_ctx {
   bool own_stream = false;
   int device = 0;
   Model T, D;
-  // shared buffers
-  float *x = nullptr, *q = nullptr, *o = nullptr, *a = nullptr, *ssq = nullptr;
+  // shared buffers (sized for the larger of the two models)
+  float *x = nullptr, *q = nullptr, *ssq_a = nullptr, *ssq_b = nullptr;
+  uint16_t *ap_x = nullptr, *ap_o = nullptr, *ap_a = nullptr;  // packed A operands
   float *logits = nullptr, *Tbuf = nullptr;
-  float* ws = nullptr;
   float* attn_ws = nullptr;
   float2* lm_part = nullptr;
   uint64_t* ar_ws = nullptr;
-  int32_t *gemm_cnt = nullptr, *attn_cnt = nullptr, *ar_cnt = nullptr;
   PassRows* rows = nullptr;
   DevState* st = nullptr;
   int32_t* hist = nullptr;
@@ -131,11 +113,13 @@ struct spec_ctx {
   int last_k = 0;
   bool graphs = true;
   std::map<std::vector<uint64_t>, GraphEntry> graph_cache;
-  GraphEntry* last_draft = nullptr;
-  GraphEntry* last_verify = nullptr;
-  std::vector<hipEvent_t> eager_events_draft, eager_events_verify;
-  std::vector<hipEvent_t>* rec_events = nullptr;  // where profiled launches record
-  hipStream_t rec_stream = nullptr;
+  // profiling: plain launches with hipEvent pairs around every gate/up GEMM
+  bool profiling = false;
+  std::vector<hipEvent_t> pool_draft, pool_verify;  // reusable events per call kind
+  std::vector<hipEvent_t> prof_draft, prof_verify;  // pairs recorded by the last calls
+  std::vector<hipEvent_t>* rec_events = nullptr;    // where profiled launches record
+  std::vector<hipEvent_t>* rec_pool = nullptr;
+  size_t rec_used = 0;
 };
 
 namespace {
@@ -203,7 +187,7 @@ int pack_rows(spec_ctx* c, const std::vector<const uint16_t*>& rows, const Mat& 
   HIPTRY(c, dalloc(&drows, rows.size()));
   hipError_t e = hipMemcpyAsync(drows, rows.data(), rows.size() * sizeof(void*),
                                 hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess) e = launch_pack(drows, m.K, m.plan.nb, m.plan.n_groups, m.p, c->stream);
+  if (e == hipSuccess) e = launch_pack(drows, m.K, m.plan.shape.nb, m.plan.n_groups, m.p, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   (void)hipFree(drows);
   HIPTRY(c, e);
@@ -335,86 +319,110 @@ void free_model(Model& m) {
 }
 
 // ------------------------------------------------------------ enqueuing --
-GemmArgs gemm_base(spec_ctx* c, const Mat& w) {
+GemmArgs gemm_base(spec_ctx* c, const Mat& w, const uint16_t* ap) {
   GemmArgs a{};
   a.Wp = w.p;
   a.n_groups = w.plan.n_groups;
   a.Kb = w.plan.Kb;
-  a.kcb = w.plan.kcb;
-  a.splits = w.plan.splits;
   a.K = w.K;
+  a.Ap = ap;
   a.rows = c->rows;
-  a.ws = c->ws;
-  a.counters = c->gemm_cnt;
   return a;
 }
 
+hipError_t next_event(spec_ctx* c, hipEvent_t* ev) {
+  std::vector<hipEvent_t>& pool = *c->rec_pool;
+  if (c->rec_used == pool.size()) {
+    hipEvent_t e = nullptr;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
+    pool.push_back(e);
+  }
+  *ev = pool[c->rec_used++];
+  return hipSuccess;
+}
+
+// Per layer: QKV (norm scale, RoPE, KV append) -> attention -> O (+residual)
+// -> gate/up (norm scale, SiLU*up) -> down (+residual).  The sums of squares
+// for each RMSNorm alternate between two buffers so a producer never writes
+// the partials its own consumer-to-be is still to read.
 hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profile) {
   hipError_t e = hipSuccess;
-  const int G64 = m.d / 64;
+  int ssq_groups = m.d / 64;  // produced by the embedding
+  float* ssq_in = c->ssq_a;
+  float* ssq_other = c->ssq_b;
   for (int l = 0; l < m.L && e == hipSuccess; ++l) {
     // RMSNorm + QKV + RoPE + KV append
-    GemmArgs a = gemm_base(c, m.qkv[l]);
-    a.X = c->x; a.ldx = m.d; a.ssq = c->ssq; a.ssq_groups = G64; a.gain = m.attn_norm(l);
-    a.eps = m.eps;
+    GemmArgs a = gemm_base(c, m.qkv[l], c->ap_x);
+    a.ssq = ssq_in; a.ssq_groups = ssq_groups; a.eps = m.eps;
     a.out = c->q; a.ldo = m.qd;
     a.q_dim = m.qd; a.kv_dim = m.kvd; a.head_dim = m.hd; a.n_kv = m.nkv;
     a.k_cache = m.kcache + (size_t)l * m.kv_layer_elems();
     a.v_cache = m.vcache + (size_t)l * m.kv_layer_elems();
     a.block_table = m.block_table; a.inv_freq = m.inv_freq; a.max_seq = c->p.max_seq;
-    e = launch_gemm(1, EPI_QKV, a, s);
+    e = launch_gemm(m.qkv[l].plan.shape, EPI_QKV, a, s);
     if (e != hipSuccess) break;
-    // causal attention over the paged cache
+    // causal attention over the paged cache -> packed A of the O projection
     AttnArgs at{};
     at.q = c->q; at.k_cache = a.k_cache; at.v_cache = a.v_cache; at.block_table = m.block_table;
     at.rows = c->rows; at.n_q = m.nq; at.n_kv = m.nkv; at.hd = m.hd;
-    at.max_chunks = c->attn_max_chunks; at.o = c->o; at.ws = c->attn_ws; at.counters = c->attn_cnt;
-    at.qg_max = (m.nq / m.nkv) * kMaxRows;
+    at.max_chunks = c->attn_max_chunks; at.ws = c->attn_ws;
+    at.qg_max = (m.nq / m.nkv) * kMaxRows; at.Ap_out = c->ap_o;
     e = launch_attn(at, s);
     if (e != hipSuccess) break;
-    // O projection + residual
-    GemmArgs b = gemm_base(c, m.o[l]);
-    b.X = c->o; b.ldx = m.qd;
-    b.resid = c->x; b.ldr = m.d; b.ssq_out = c->ssq;
-    e = launch_gemm(1, EPI_RESID, b, s);
+    // O projection + residual; packs x * ffn_norm for gate/up
+    GemmArgs b = gemm_base(c, m.o[l], c->ap_o);
+    b.resid = c->x; b.ldr = m.d; b.gain_next = m.ffn_norm(l); b.Ap_out = c->ap_x;
+    b.ssq_out = ssq_other;
+    e = launch_gemm(m.o[l].plan.shape, EPI_RESID, b, s);
     if (e != hipSuccess) break;
-    // RMSNorm + gate/up + SiLU*mul
-    GemmArgs g = gemm_base(c, m.gu[l]);
-    g.X = c->x; g.ldx = m.d; g.ssq = c->ssq; g.ssq_groups = G64; g.gain = m.ffn_norm(l);
-    g.eps = m.eps; g.out = c->a; g.ldo = m.F;
+    std::swap(ssq_in, ssq_other);
+    ssq_groups = m.o[l].plan.n_groups;
+    // RMSNorm + gate/up + SiLU*mul -> packed A of the down projection
+    GemmArgs g = gemm_base(c, m.gu[l], c->ap_x);
+    g.ssq = ssq_in; g.ssq_groups = ssq_groups; g.eps = m.eps; g.Ap_out = c->ap_a;
     if (profile && c->rec_events) {
       hipEvent_t e0 = nullptr, e1 = nullptr;
-      e = hipEventCreate(&e0);
-      if (e == hipSuccess) e = hipEventCreate(&e1);
-      if (e0) c->rec_events->push_back(e0);
-      if (e1) c->rec_events->push_back(e1);
+      e = next_event(c, &e0);
+      if (e == hipSuccess) e = next_event(c, &e1);
       if (e == hipSuccess) e = hipEventRecord(e0, s);
-      if (e == hipSuccess) e = launch_gemm(2, EPI_SILU, g, s);
+      if (e == hipSuccess) e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
       if (e == hipSuccess) e = hipEventRecord(e1, s);
+      if (e == hipSuccess) {
+        c->rec_events->push_back(e0);
+        c->rec_events->push_back(e1);
+      }
     } else {
-      e = launch_gemm(2, EPI_SILU, g, s);
+      e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
     }
     if (e != hipSuccess) break;
-    // down projection + residual
-    GemmArgs dn = gemm_base(c, m.dn[l]);
-    dn.X = c->a; dn.ldx = m.F;
-    dn.resid = c->x; dn.ldr = m.d; dn.ssq_out = c->ssq;
-    e = launch_gemm(1, EPI_RESID, dn, s);
+    // down projection + residual; packs x * (next attn_norm or final norm)
+    GemmArgs dn = gemm_base(c, m.dn[l], c->ap_a);
+    dn.resid = c->x; dn.ldr = m.d; dn.Ap_out = c->ap_x; dn.ssq_out = ssq_other;
+    dn.gain_next = l + 1 < m.L ? m.attn_norm(l + 1) : m.final_norm();
+    e = launch_gemm(m.dn[l].plan.shape, EPI_RESID, dn, s);
+    std::swap(ssq_in, ssq_other);
+    ssq_groups = m.dn[l].plan.n_groups;
   }
   return e;
 }
 
+// Sums of squares left by the last layer's down projection (each layer ends
+// with them back in ssq_a) for the final RMSNorm.
+int final_ssq_groups(const Model& m) { return m.dn[m.L - 1].plan.n_groups; }
+float* final_ssq(spec_ctx* c, const Model&) { return c->ssq_a; }
+
 // final norm + LM head (+ logits partials) + softmax into `dst`
 hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only,
                         float* logits_dst, float* dst) {
-  GemmArgs a = gemm_base(c, m.lm);
-  a.X = c->x; a.ldx = m.d; a.ssq = c->ssq; a.ssq_groups = m.d / 64; a.gain = m.final_norm();
-  a.eps = m.eps; a.last_row_only = last_row_only;
+  GemmArgs a = gemm_base(c, m.lm, c->ap_x);
+  a.ssq = final_ssq(c, m); a.ssq_groups = final_ssq_groups(m); a.eps = m.eps;
+  a.last_row_only = last_row_only;
   a.out = logits_dst; a.ldo = m.V; a.lm_part = c->lm_part; a.n_valid = m.V;
-  hipError_t e = launch_gemm(1, EPI_LOGITS, a, s);
+  hipError_t e = launch_gemm(m.lm.plan.shape, EPI_LOGITS, a, s);
   if (e != hipSuccess) return e;
   SoftmaxArgs sm{};
-  sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.n_wgg; sm.V = m.V;
+  sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.n_groups; sm.V = m.V;
   sm.rows = c->rows; sm.last_row_only = last_row_only; sm.out = dst; sm.chunk = c->sm_chunk;
   return launch_softmax(sm, c->sm_nchunks, s);
 }
@@ -425,7 +433,8 @@ hipError_t enqueue_embed(spec_ctx* c, const Model& m, hipStream_t s, int mode, i
   a.E = m.embed; a.d = m.d; a.vocab = m.V; a.max_seq = c->p.max_seq;
   a.st = c->st; a.hist = c->hist; a.dtok = dtok;
   a.mode = mode; a.n_rows = n_rows; a.pos0 = pos0; a.step = step;
-  a.rows_out = c->rows; a.x = c->x; a.ssq = c->ssq;
+  a.rows_out = c->rows; a.x = c->x; a.gain = m.attn_norm(0); a.Ap_out = c->ap_x;
+  a.ssq = c->ssq_a;
   return launch_embed(a, s);
 }
 
@@ -434,7 +443,7 @@ hipError_t enqueue_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32
   hipError_t e = hipSuccess;
   for (int st = 0; st < K && e == hipSuccess; ++st) {
     e = enqueue_embed(c, m, s, st == 0 ? EMB_DRAFT0 : EMB_DRAFTS, 0, 0, st, d);
-    if (e == hipSuccess) e = enqueue_layers(c, m, s, c->p.profile_kernels != 0);
+    if (e == hipSuccess) e = enqueue_layers(c, m, s, c->profiling);
     float* drow = Dp + (size_t)st * m.V;
     if (e == hipSuccess) e = enqueue_head(c, m, s, 1, c->logits, drow);
     if (e == hipSuccess) {
@@ -443,7 +452,7 @@ hipError_t enqueue_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32
       ar.seed = seed; ar.stream_id = c->p.stream_id; ar.pos = nullptr; ar.st = c->st;
       ar.pos_offset = st + 1; ar.greedy = c->p.greedy; ar.word = 0;
       ar.chunk = c->ar_chunk; ar.n_chunks = c->ar_nchunks;
-      ar.out = d + st; ar.n_acc = nullptr; ar.ws = c->ar_ws; ar.counters = c->ar_cnt;
+      ar.out = d + st; ar.n_acc = nullptr; ar.ws = c->ar_ws;
       e = launch_accept_reject(ar, s);
     }
   }
@@ -456,7 +465,7 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
   float* Tb = Tdst ? Tdst : c->Tbuf;
   float* Lb = Ldst ? Ldst : c->logits;
   hipError_t e = enqueue_embed(c, m, s, EMB_VERIFY, K + 1, 0, 0, d);
-  if (e == hipSuccess) e = enqueue_layers(c, m, s, c->p.profile_kernels != 0);
+  if (e == hipSuccess) e = enqueue_layers(c, m, s, c->profiling);
   if (e == hipSuccess) e = enqueue_head(c, m, s, 0, Lb, Tb);
   if (e == hipSuccess) {
     ArArgs ar{};
@@ -464,34 +473,33 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
     ar.seed = seed; ar.stream_id = c->p.stream_id; ar.pos = nullptr; ar.st = c->st;
     ar.pos_offset = 1; ar.greedy = c->p.greedy; ar.word = 2;
     ar.chunk = c->ar_chunk; ar.n_chunks = c->ar_nchunks;
-    ar.out = out; ar.n_acc = nacc; ar.ws = c->ar_ws; ar.counters = c->ar_cnt;
+    ar.out = out; ar.n_acc = nacc; ar.ws = c->ar_ws;
     e = launch_accept_reject(ar, s);
   }
   return e;
 }
 
-// Runs `body` either directly on the context stream or through a cached
-// graph captured on the capture stream.
+// Runs `body` either through a cached graph captured on the capture stream,
+// or (no graphs, or profiling) directly on the context stream.
 template <typename F>
-int run_pass(spec_ctx* c, const std::vector<uint64_t>& key, std::vector<hipEvent_t>* eager_events,
-             GraphEntry** last, F body) {
-  if (!c->graphs) {
-    for (hipEvent_t ev : *eager_events) (void)hipEventDestroy(ev);
-    eager_events->clear();
-    c->rec_events = eager_events;
+int run_pass(spec_ctx* c, const std::vector<uint64_t>& key, std::vector<hipEvent_t>* prof_events,
+             std::vector<hipEvent_t>* pool, F body) {
+  if (!c->graphs || c->profiling) {
+    prof_events->clear();
+    c->rec_events = prof_events;
+    c->rec_pool = pool;
+    c->rec_used = 0;
     hipError_t e = body(c->stream);
     c->rec_events = nullptr;
+    c->rec_pool = nullptr;
     HIPTRY(c, e);
-    *last = nullptr;
     return SPEC_OK;
   }
   auto it = c->graph_cache.find(key);
   if (it == c->graph_cache.end()) {
     GraphEntry ge;
     HIPTRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeRelaxed));
-    c->rec_events = &ge.events;
     hipError_t e = body(c->cap_stream);
-    c->rec_events = nullptr;
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(c->cap_stream, &g);
     if (e == hipSuccess) e = e2;
@@ -501,7 +509,6 @@ int run_pass(spec_ctx* c, const std::vector<uint64_t>& key, std::vector<hipEvent
     it = c->graph_cache.emplace(key, ge).first;
   }
   HIPTRY(c, hipGraphLaunch(it->second.exec, c->stream));
-  *last = &it->second;
   return SPEC_OK;
 }
 
@@ -525,16 +532,14 @@ void destroy_ctx(spec_ctx* c) {
   if (!c) return;
   (void)hipSetDevice(c->device);
   if (c->stream) (void)hipStreamSynchronize(c->stream);
-  for (auto& kv : c->graph_cache) {
+  for (auto& kv : c->graph_cache)
     if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
-    for (hipEvent_t ev : kv.second.events) (void)hipEventDestroy(ev);
-  }
-  for (hipEvent_t ev : c->eager_events_draft) (void)hipEventDestroy(ev);
-  for (hipEvent_t ev : c->eager_events_verify) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : c->pool_draft) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : c->pool_verify) (void)hipEventDestroy(ev);
   free_model(c->D);
   free_model(c->T);
-  void* bufs[] = {c->x, c->q, c->o, c->a, c->ssq, c->logits, c->Tbuf, c->ws, c->attn_ws, c->lm_part,
-                  c->ar_ws, c->gemm_cnt, c->attn_cnt, c->ar_cnt, c->rows, c->st, c->hist};
+  void* bufs[] = {c->x, c->q, c->ssq_a, c->ssq_b, c->ap_x, c->ap_o, c->ap_a, c->logits, c->Tbuf,
+                  c->attn_ws, c->lm_part, c->ar_ws, c->rows, c->st, c->hist};
   for (void* b : bufs) (void)hipFree(b);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
@@ -569,6 +574,7 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   c->p = *p;
   (void)hipGetDevice(&c->device);
   c->graphs = p->use_graphs != 0 && getenv("SPEC_NO_GRAPH") == nullptr;
+  c->profiling = p->profile_kernels != 0;
   auto bail = [&](int rc) {
     std::string msg = c->err;
     destroy_ctx(c);
@@ -600,20 +606,17 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   TRY(build_model(c, p->draft, c->D, &c->T, &p->target));
 
   const Model* ms[2] = {&c->T, &c->D};
-  int dmax = 0, qmax = 0, fmax = 0, V = c->T.V, lm_wgg = 0, gcnt = 0;
-  size_t ws = 0, attn_ws = 0;
+  int dmax = 0, qmax = 0, fmax = 0, V = c->T.V, lm_groups = 0, ssq_groups = 0;
+  size_t attn_ws = 0;
   c->attn_max_chunks = (p->max_seq + kAttnChunk - 1) / kAttnChunk;
   for (const Model* m : ms) {
     dmax = std::max(dmax, m->d);
     qmax = std::max(qmax, m->qd);
     fmax = std::max(fmax, m->F);
-    lm_wgg = std::max(lm_wgg, m->lm.plan.n_wgg);
-    auto upd = [&](const Mat& x) {
-      ws = std::max(ws, x.plan.ws_floats());
-      gcnt = std::max(gcnt, x.plan.n_wgg);
-    };
-    for (int l = 0; l < m->L; ++l) { upd(m->qkv[l]); upd(m->o[l]); upd(m->gu[l]); upd(m->dn[l]); }
-    upd(m->lm);
+    lm_groups = std::max(lm_groups, m->lm.plan.n_groups);
+    ssq_groups = std::max(ssq_groups, m->d / 64);
+    for (int l = 0; l < m->L; ++l)
+      ssq_groups = std::max({ssq_groups, m->o[l].plan.n_groups, m->dn[l].plan.n_groups});
     const int qg = (m->nq / m->nkv) * kMaxRows;
     attn_ws = std::max(attn_ws, (size_t)m->nkv * c->attn_max_chunks * qg * (m->hd + 2));
     if (attn_lds_bytes(m->hd, qg) > 64 * 1024) {
@@ -625,25 +628,24 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   c->sm_nchunks = (V + c->sm_chunk - 1) / c->sm_chunk;
   TRYH(dalloc(&c->x, (size_t)kMaxRows * dmax));
   TRYH(dalloc(&c->q, (size_t)kMaxRows * qmax));
-  TRYH(dalloc(&c->o, (size_t)kMaxRows * qmax));
-  TRYH(dalloc(&c->a, (size_t)kMaxRows * fmax));
-  TRYH(dalloc(&c->ssq, (size_t)kMaxRows * (dmax / 64)));
+  TRYH(dalloc(&c->ssq_a, (size_t)kMaxRows * ssq_groups));
+  TRYH(dalloc(&c->ssq_b, (size_t)kMaxRows * ssq_groups));
+  // packed A operands: 16 bf16 rows (8 hi + 8 lo) per column
+  TRYH(dalloc(&c->ap_x, (size_t)16 * dmax));
+  TRYH(dalloc(&c->ap_o, (size_t)16 * qmax));
+  TRYH(dalloc(&c->ap_a, (size_t)16 * fmax));
   TRYH(dalloc(&c->logits, (size_t)kMaxRows * V));
   TRYH(dalloc(&c->Tbuf, (size_t)kMaxRows * V));
-  TRYH(dalloc(&c->ws, ws));
   TRYH(dalloc(&c->attn_ws, attn_ws));
-  TRYH(dalloc(&c->lm_part, (size_t)lm_wgg * kMaxRows));
+  TRYH(dalloc(&c->lm_part, (size_t)lm_groups * kMaxRows));
   TRYH(dalloc(&c->ar_ws, (size_t)c->ar_nchunks * ar_ws_words(SPEC_K_MAX)));
-  TRYH(dalloc(&c->gemm_cnt, (size_t)gcnt));
-  TRYH(dalloc(&c->attn_cnt, (size_t)std::max(c->T.nkv, c->D.nkv)));
-  TRYH(dalloc(&c->ar_cnt, (size_t)4));
   TRYH(dalloc(&c->rows, 1));
   TRYH(dalloc(&c->st, 1));
+  TRYH(hipMemsetAsync(c->ap_x, 0, (size_t)32 * dmax, c->stream));
+  TRYH(hipMemsetAsync(c->ap_o, 0, (size_t)32 * qmax, c->stream));
+  TRYH(hipMemsetAsync(c->ap_a, 0, (size_t)32 * fmax, c->stream));
   c->hist_cap = p->max_seq + 16;
   TRYH(dalloc(&c->hist, (size_t)c->hist_cap));
-  TRYH(hipMemsetAsync(c->gemm_cnt, 0, (size_t)gcnt * 4, c->stream));
-  TRYH(hipMemsetAsync(c->attn_cnt, 0, (size_t)std::max(c->T.nkv, c->D.nkv) * 4, c->stream));
-  TRYH(hipMemsetAsync(c->ar_cnt, 0, 4 * 4, c->stream));
   TRYH(hipMemsetAsync(c->x, 0, (size_t)kMaxRows * dmax * 4, c->stream));
   TRYH(hipMemsetAsync(c->hist, 0, (size_t)c->hist_cap * 4, c->stream));
   TRYH(hipMemcpyAsync(c->hist, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, c->stream));
@@ -688,7 +690,7 @@ int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_d
   }
   std::vector<uint64_t> key = {1, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev};
-  int r = run_pass(c, key, &c->eager_events_draft, &c->last_draft,
+  int r = run_pass(c, key, &c->prof_draft, &c->pool_draft,
                    [&](hipStream_t s) { return enqueue_draft(c, s, K, seed, d_dev, D_dev); });
   if (r) return r;
   c->drafted_k = K;
@@ -719,7 +721,7 @@ int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, con
                                (uint64_t)(uintptr_t)n_acc_dev,
                                (uint64_t)(uintptr_t)T_dev,
                                (uint64_t)(uintptr_t)logits_dev};
-  int r = run_pass(c, key, &c->eager_events_verify, &c->last_verify, [&](hipStream_t s) {
+  int r = run_pass(c, key, &c->prof_verify, &c->pool_verify, [&](hipStream_t s) {
     return enqueue_verify(c, s, K, seed, d_dev, D_dev, out_dev, n_acc_dev, T_dev, logits_dev);
   });
   if (r) return r;
@@ -791,14 +793,16 @@ int spec_kernel_times(spec_ctx* c, float* ms_out, int32_t cap, int32_t* n_out) {
     }
     return SPEC_OK;
   };
-  if (c->graphs) {
-    if (c->last_draft) if (int r = take(c->last_draft->events)) return r;
-    if (c->last_verify) if (int r = take(c->last_verify->events)) return r;
-  } else {
-    if (int r = take(c->eager_events_draft)) return r;
-    if (int r = take(c->eager_events_verify)) return r;
-  }
+  if (int r = take(c->prof_draft)) return r;
+  if (int r = take(c->prof_verify)) return r;
   *n_out = std::min(n, cap);
+  return SPEC_OK;
+}
+
+int spec_set_profiling(spec_ctx* c, int32_t enable) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_set_profiling: null context");
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  c->profiling = enable != 0;
   return SPEC_OK;
 }
 
@@ -807,8 +811,6 @@ namespace {
 struct ArWorkspace {
   uint64_t* ws = nullptr;
   size_t ws_words = 0;
-  int32_t* cnt = nullptr;
-  size_t n_cnt = 0;
 };
 std::mutex g_ar_mu;
 std::map<int, ArWorkspace> g_ar;
@@ -832,25 +834,19 @@ int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_
   std::lock_guard<std::mutex> lk(g_ar_mu);
   ArWorkspace& w = g_ar[dev];
   if (w.ws_words < words) {
+    // the previous workspace may still be read by work queued on any stream
+    HIPTRY(nullptr, hipDeviceSynchronize());
     (void)hipFree(w.ws);
     w.ws = nullptr;
     w.ws_words = 0;
     HIPTRY(nullptr, dalloc(&w.ws, words));
     w.ws_words = words;
   }
-  if (w.n_cnt < (size_t)B) {
-    (void)hipFree(w.cnt);
-    w.cnt = nullptr;
-    w.n_cnt = 0;
-    HIPTRY(nullptr, dalloc(&w.cnt, (size_t)B));
-    HIPTRY(nullptr, hipMemsetAsync(w.cnt, 0, (size_t)B * 4, s));
-    w.n_cnt = B;
-  }
   ArArgs a{};
   a.T = T_dev; a.D = D_dev; a.d = d_dev; a.B = B; a.K = K; a.V = V;
   a.seed = seed; a.stream_id = stream_id; a.pos = pos_dev; a.st = nullptr; a.pos_offset = 0;
   a.greedy = greedy; a.word = 2; a.chunk = chunk; a.n_chunks = nch;
-  a.out = out_dev; a.n_acc = n_acc_dev; a.ws = w.ws; a.counters = w.cnt;
+  a.out = out_dev; a.n_acc = n_acc_dev; a.ws = w.ws;
   HIPTRY(nullptr, launch_accept_reject(a, s));
   return SPEC_OK;
 }

@@ -148,11 +148,13 @@ def weights_torch(cfg: ModelConfig, seed: int = SEED_WEIGHTS, device="cuda", std
             g = torch.Generator(device=device)
             g.manual_seed(zlib.crc32(f"{seed}/{cfg.name}/{k}".encode()))
             t = torch.empty(shp, dtype=torch.bfloat16, device=device)
-            # generate layer by layer to bound the fp32 temporary
-            flat = t.view(shp[0], -1) if len(shp) > 1 else t.view(1, -1)
-            for i in range(flat.shape[0]):
-                flat[i].copy_(torch.randn(flat.shape[1], generator=g, device=device,
-                                          dtype=torch.float32) * std)
+            # generate in chunks to bound the fp32 temporary
+            flat = t.view(-1)
+            step = 1 << 26
+            for i in range(0, flat.numel(), step):
+                n = min(step, flat.numel() - i)
+                flat[i:i + n].copy_(torch.randn(n, generator=g, device=device,
+                                                dtype=torch.float32) * std)
             out[k] = t
     if cfg.tied_head:
         out["lm_head"] = out["embed"]
