@@ -32,17 +32,18 @@ def log(*a):
 
 def verify_pass_bytes(cfg, K: int, L: int) -> int:
     """Algorithmic bytes of one verify pass: every weight once, K+1 embedding
-    rows, keys/values of L+K+1 positions read and K+1 written, T rows written."""
+    rows, keys/values of L+K+1 positions read and K+1 written (4 bytes per
+    element: bf16 high + low parts), T rows written."""
     w = cfg.weight_bytes()
     emb = (K + 1) * cfg.d_model * 2
-    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 4
     kv = (L + K + 1) * kv_tok + (K + 1) * kv_tok
     t_rows = (K + 1) * cfg.vocab * 4
     return w + emb + kv + t_rows
 
 
 def draft_step_bytes(cfg, L: int) -> int:
-    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 4
     return cfg.weight_bytes() + cfg.d_model * 2 + (L + 1) * kv_tok + kv_tok + cfg.vocab * 4
 
 

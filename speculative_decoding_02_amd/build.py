@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "libspec")
 LIB = os.path.join(HERE, "libspec.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "spec_api.cpp"]
+SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_accept.hip", "spec_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SPEC_ARCH", "gfx950")

@@ -47,6 +47,16 @@ SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ------------------------------------------------------------- KV cache --
+// Paged cache of one layer: [block][kv head][16 tokens][2][head_dim] bf16,
+// where [0] is the bf16 high part of the fp32 key/value and [1] the low part
+// (x - hi).  Keeping ~16 mantissa bits matters: rounding keys and values to
+// one bf16 is the largest error source of the pass (it compounds through the
+// feed-forward blocks to ~1e-2 logit error on an 8B-shaped slice).
+SPEC_DEVICE size_t kv_index(int blk, int n_kv, int head, int slot, int hd, int part, int dim) {
+  return ((((size_t)blk * n_kv + head) * kBlock + slot) * 2 + part) * hd + dim;
+}
+
 // ------------------------------------------------- packed MFMA A operand --
 // Activations enter the skinny GEMM as the A operand of
 // v_mfma_f32_16x16x32_bf16: 16 rows x 32 k per 1 KiB block, lane l holding 8
@@ -174,6 +184,25 @@ SPEC_DEVICE float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
+}
+
+// Exclusive prefix sum of one uint64 per thread over a 256-thread block
+// (integer addition: exact and order-free).  lds: >= 4 entries.
+SPEC_DEVICE uint64_t block_exclusive_scan_u64_256(uint64_t v, uint64_t* lds) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)inc, d), hi = __shfl_up((uint32_t)(inc >> 32), d);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) lds[wid] = inc;
+  __syncthreads();
+  uint64_t base = 0;
+  for (int w = 0; w < wid; ++w) base += lds[w];
+  __syncthreads();
+  return base + inc - v;
 }
 
 // Block-wide reductions through LDS (blockDim.x a multiple of 64, <= 1024).

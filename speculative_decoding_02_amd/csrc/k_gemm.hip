@@ -12,14 +12,16 @@
 //    is one contiguous span: [group][k-block][NB][64 lanes][8 bf16].
 //  * A arrives already packed by its producer (see apack_index): bf16 high
 //    and low halves of up to 8 fp32 rows in one 16-row MFMA tile.  It is
-//    small and shared by every workgroup, so it is read from L2; lanes of
-//    rows the pass does not use skip the load.
+//    small and shared by every workgroup, so it is read from L2; rows the
+//    pass does not use are zeroed in registers.
 //  * A workgroup owns NB 16-column blocks for the whole of K; its waves split
 //    K and are reduced through LDS in wave order (deterministic, and no
 //    workgroup ever waits for another).
 //  * RMSNorm is folded in: the producer packs x * gain, and the row scale
 //    1/sqrt(mean(x^2) + eps) multiplies Y here, from per-workgroup sums of
 //    squares published by the producer.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace spec {
@@ -43,9 +45,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   __shared__ float s_red[W * NB * 128];
   __shared__ float s_y[kMaxRows * YW];
   __shared__ float s_scale[kMaxRows];
+  __shared__ float s_ssq[W * 64];
   __shared__ float s_part[kMaxRows][YW / 8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = blockIdx.x;
   int n_rows = a.rows->n_rows;
   int row_base = 0;
@@ -54,15 +58,23 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     n_rows = n_rows > 0 ? 1 : 0;
   }
 
-  // row scale of the consumer's RMSNorm (fixed summation order)
-  if (tid < kMaxRows) {
-    float sc = 1.0f;
-    if (a.ssq != nullptr && tid < n_rows) {
-      float ss = 0.0f;
-      for (int q = 0; q < a.ssq_groups; ++q) ss += a.ssq[q * kMaxRows + row_base + tid];
-      sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+  // Row scale of the consumer's RMSNorm.  The producer's partial sums of
+  // squares are spread over all threads (thread t: row t%8, partials
+  // q = t/8, t/8 + P, ...), loaded before the main loop so their latency
+  // hides behind the weight stream, and folded in a fixed order after it.
+  constexpr int P = W * 64 / kMaxRows;
+  constexpr int kMaxSsq = kGemmMaxSsqPerThread;  // ssq_groups <= P * kMaxSsq
+  float ssq_part = 0.0f;
+  if (a.ssq != nullptr) {
+    const int m = tid % kMaxRows, p0 = tid / kMaxRows;
+    float v[kMaxSsq];
+#pragma unroll
+    for (int i = 0; i < kMaxSsq; ++i) {
+      const int q = p0 + i * P;
+      v[i] = (q < a.ssq_groups && m < n_rows) ? a.ssq[q * kMaxRows + row_base + m] : 0.0f;
     }
-    s_scale[tid] = sc;
+#pragma unroll
+    for (int i = 0; i < kMaxSsq; ++i) ssq_part += v[i];
   }
 
   // ---- main loop: this wave's share of K ---------------------------------
@@ -74,33 +86,33 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   floatx4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  int kb = kb0;
-  for (; kb + U <= kb1; kb += U) {
-    uint4 av[U], wv[U][NB];
+  // Batches of k-blocks: all loads of a batch are issued before its first
+  // MFMA (the scheduling barrier keeps the compiler from interleaving them),
+  // so each wave keeps UB*NB KiB of weights in flight.  A is loaded by every
+  // lane (always in bounds) and rows the pass does not use are zeroed after.
+  auto batch = [&](auto ub_tag, int kb) {
+    constexpr int UB = decltype(ub_tag)::value;
+    uint4 av[UB], wv[UB][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < UB; ++u) av[u] = ap[(size_t)(kb + u) * 64];
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
 #pragma unroll
       for (int j = 0; j < NB; ++j) wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
-#pragma unroll
-    for (int u = 0; u < U; ++u) av[u] = aload ? ap[(size_t)(kb + u) * 64] : make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < UB; ++u) {
+      const uint4 a4 = aload ? av[u] : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(wv[u][j]),
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a4), as_bf16x8(wv[u][j]),
                                                          acc[j], 0, 0, 0);
-  }
-  for (; kb < kb1; ++kb) {
-    uint4 wv[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) wv[j] = load_stream(wp + ((size_t)kb * NB + j) * 64);
-    const uint4 av = aload ? ap[(size_t)kb * 64] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(wv[j]), acc[j], 0,
-                                                       0, 0);
-  }
+    }
+  };
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) batch(std::integral_constant<int, U>{}, kb);
+  for (; kb + 4 <= kb1; kb += 4) batch(std::integral_constant<int, 4>{}, kb);
+  for (; kb < kb1; ++kb) batch(std::integral_constant<int, 1>{}, kb);
 
   // ---- hi + lo rows, then the waves' partial sums in wave order ----------
   // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); rows
@@ -113,6 +125,17 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     v.z = acc[j][2] + __shfl_down(acc[j][2], 32);
     v.w = acc[j][3] + __shfl_down(acc[j][3], 32);
     if (lane < 32) *(float4*)&s_red[((wave * NB + j) * 32 + lane) * 4] = v;
+  }
+  s_ssq[tid] = ssq_part;
+  __syncthreads();
+  if (tid < kMaxRows) {
+    float sc = 1.0f;
+    if (a.ssq != nullptr && tid < n_rows) {
+      float ss = 0.0f;
+      for (int p = 0; p < P; ++p) ss += s_ssq[p * kMaxRows + tid];
+      sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    }
+    s_scale[tid] = sc;
   }
   __syncthreads();
   for (int idx = tid; idx < NB * 128; idx += W * 64) {
@@ -213,25 +236,28 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
         const int pair = bl * 8 + (w & 7), hf = w >> 3;
         const int head = pair / half_hd, jj = pair % half_hd;
         const float other = s_y[m * YW + (c ^ 8)];
-        double sn, cs;
-        sincos((double)pos * a.inv_freq[jj], &sn, &cs);
-        const double lo = hf ? (double)other : (double)mine;
-        const double hi = hf ? (double)mine : (double)other;
-        const float val = (float)(hf ? hi * cs + lo * sn : lo * cs - hi * sn);
+        const float2 r = a.rope[(size_t)pos * half_hd + jj];  // (cos, sin) of pos * theta^(-2jj/hd)
+        const float lo = hf ? other : mine;
+        const float hi = hf ? mine : other;
+        const float val = hf ? hi * r.x + lo * r.y : lo * r.x - hi * r.y;
         const int dim = jj + hf * half_hd;
         if (is_q) {
           a.out[(size_t)m * a.ldo + (size_t)head * a.head_dim + dim] = val;
         } else {
           const int blk = a.block_table[pos / kBlock];
-          a.k_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
-              f32_to_bf16_rne(val);
+          const uint16_t hb = f32_to_bf16_rne(val);
+          a.k_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 0, dim)] = hb;
+          a.k_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 1, dim)] =
+              f32_to_bf16_rne(val - bf16_to_f32(hb));
         }
       } else {
         const int f0 = (b - q_blocks - k_blocks) * 16 + w;
         const int head = f0 / a.head_dim, dim = f0 % a.head_dim;
         const int blk = a.block_table[pos / kBlock];
-        a.v_cache[(((size_t)blk * a.n_kv + head) * kBlock + pos % kBlock) * a.head_dim + dim] =
-            f32_to_bf16_rne(mine);
+        const uint16_t hb = f32_to_bf16_rne(mine);
+        a.v_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 0, dim)] = hb;
+        a.v_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 1, dim)] =
+            f32_to_bf16_rne(mine - bf16_to_f32(hb));
       }
     }
   }

@@ -50,7 +50,7 @@ struct GemmArgs {
   uint16_t* k_cache;
   uint16_t* v_cache;
   const int32_t* block_table;
-  const double* inv_freq;  // [head_dim/2]
+  const float2* rope;      // [max_seq][head_dim/2] (cos, sin)
   int max_seq;
 };
 
@@ -59,6 +59,8 @@ struct GemmShape {
   int waves;   // waves per workgroup, splitting K
 };
 hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
+// Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
+constexpr int kGemmMaxSsqPerThread = 16;
 
 // Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
 // layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
@@ -68,7 +70,7 @@ hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_grou
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
   const float* q;            // [n_rows][n_q*hd]
-  const uint16_t* k_cache;   // [n_blocks][n_kv][16][hd]
+  const uint16_t* k_cache;   // [n_blocks][n_kv][16][2][hd] (see kv_index)
   const uint16_t* v_cache;
   const int32_t* block_table;
   const PassRows* rows;
@@ -80,6 +82,9 @@ struct AttnArgs {
 };
 constexpr int kAttnChunk = 64;
 size_t attn_lds_bytes(int hd, int qg_max);
+constexpr size_t kAttnMaxLds = 160 * 1024;  // LDS per CU on gfx950
+// Raises the partial kernel's dynamic-LDS limit (needed above 64 KiB).
+hipError_t attn_reserve_lds(size_t bytes);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- embedding --
@@ -141,6 +146,8 @@ hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
 // ---------------------------------------------------------------- commit --
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
                          const int32_t* n_acc, int drafted_k, hipStream_t s);
-hipError_t launch_inv_freq(double* dst, int hd, double theta, hipStream_t s);
+// RoPE table: (cos, sin) of p * theta^(-2j/hd) for p < max_seq, j < hd/2,
+// evaluated in fp64 and stored as fp32.
+hipError_t launch_rope_table(float2* dst, int max_seq, int hd, double theta, hipStream_t s);
 
 }  // namespace spec

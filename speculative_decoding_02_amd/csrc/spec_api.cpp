@@ -43,12 +43,16 @@ struct GemmPlan {
   int n_groups = 0, Kb = 0;
 };
 
-GemmPlan plan_gemm(int n_cols, int nb, int K) {
+// Shapes measured on MI355X (standalone sweep over nb in {1,2,4}, waves in
+// {4,8}): two blocks per workgroup once there are enough columns to keep
+// >= ~400 workgroups, eight waves unless each wave would stream over 64 KiB.
+GemmPlan plan_gemm(int n_cols, int nb_min, int K) {
   GemmPlan p;
-  p.shape.nb = nb;
+  const int n_blocks = n_cols / 16;
+  p.shape.nb = std::max(nb_min, (n_blocks >= 768 && n_blocks % 2 == 0) ? 2 : 1);
   p.Kb = K / 32;
-  p.n_groups = n_cols / (16 * nb);
-  p.shape.waves = p.Kb >= 64 ? 8 : 4;
+  p.n_groups = n_blocks / p.shape.nb;
+  p.shape.waves = p.Kb * p.shape.nb / 8 > 64 ? 4 : 8;
   return p;
 }
 
@@ -68,12 +72,12 @@ struct Model {
   uint16_t* arena = nullptr;      // packed matrices
   uint16_t* embed = nullptr;      // [V][d] (owned unless shared)
   uint16_t* norms = nullptr;      // attn [L][d], ffn [L][d], final [d]
-  uint16_t* kcache = nullptr;     // [L][n_blocks][nkv][16][hd]
+  uint16_t* kcache = nullptr;     // [L][n_blocks][nkv][16][2 (hi, lo)][hd] bf16
   uint16_t* vcache = nullptr;
   int32_t* block_table = nullptr;
-  double* inv_freq = nullptr;
+  float2* rope = nullptr;  // [max_seq][hd/2] (cos, sin)
   int n_blocks = 0;
-  size_t kv_layer_elems() const { return (size_t)n_blocks * nkv * kBlock * hd; }
+  size_t kv_layer_elems() const { return (size_t)n_blocks * nkv * kBlock * 2 * hd; }
   const uint16_t* attn_norm(int l) const { return norms + (size_t)l * d; }
   const uint16_t* ffn_norm(int l) const { return norms + (size_t)(L + l) * d; }
   const uint16_t* final_norm() const { return norms + (size_t)2 * L * d; }
@@ -183,6 +187,8 @@ bool valid_model(const spec_model_desc& m, std::string* why) {
 
 // Packs one matrix from row pointers (host list) into dst.
 int pack_rows(spec_ctx* c, const std::vector<const uint16_t*>& rows, const Mat& m) {
+  if (rows.size() != (size_t)m.plan.n_groups * m.plan.shape.nb * 16)
+    return fail(c, SPEC_ERR_ARG, "internal: row list does not match the packing plan");
   const uint16_t** drows = nullptr;
   HIPTRY(c, dalloc(&drows, rows.size()));
   hipError_t e = hipMemcpyAsync(drows, rows.data(), rows.size() * sizeof(void*),
@@ -241,7 +247,7 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   for (int l = 0; l < L; ++l) {
     // QKV: q and k rows in pair-interleaved order (columns w, w+8 of a block
     // are the halves j, j+hd/2 of one RoPE pair), then v rows in order.
-    rows.assign((size_t)m.qkv[l].plan.n_groups * 16, nullptr);
+    rows.assign((size_t)m.qkv[l].plan.n_groups * m.qkv[l].plan.shape.nb * 16, nullptr);
     for (int p = 0; p < m.qd + 2 * m.kvd; ++p) {
       const uint16_t* src;
       if (p < m.qd + m.kvd) {
@@ -258,22 +264,29 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
       rows[p] = src;
     }
     if (int r = pack_rows(c, rows, m.qkv[l])) return r;
-    rows.assign((size_t)m.o[l].plan.n_groups * 16, nullptr);
+    rows.assign((size_t)m.o[l].plan.n_groups * m.o[l].plan.shape.nb * 16, nullptr);
     for (int n = 0; n < d; ++n) rows[n] = wo + ((size_t)l * d + n) * m.qd;
     if (int r = pack_rows(c, rows, m.o[l])) return r;
-    rows.assign((size_t)m.gu[l].plan.n_groups * 32, nullptr);
-    for (int g = 0; g < m.F / 16; ++g)
-      for (int w = 0; w < 16; ++w) {
-        rows[(size_t)(g * 2 + 0) * 16 + w] = wg + ((size_t)l * m.F + g * 16 + w) * d;
-        rows[(size_t)(g * 2 + 1) * 16 + w] = wu + ((size_t)l * m.F + g * 16 + w) * d;
-      }
+    // gate/up: within a group of nb blocks, block 2p holds gate rows and
+    // block 2p+1 the up rows of the same 16 features (g*nb/2 + p)*16 + w
+    {
+      const int nbg = m.gu[l].plan.shape.nb;
+      rows.assign((size_t)m.gu[l].plan.n_groups * nbg * 16, nullptr);
+      for (int g = 0; g < m.gu[l].plan.n_groups; ++g)
+        for (int p2 = 0; p2 < nbg / 2; ++p2)
+          for (int w = 0; w < 16; ++w) {
+            const size_t f = (size_t)(g * (nbg / 2) + p2) * 16 + w;
+            rows[(size_t)(g * nbg + 2 * p2) * 16 + w] = wg + ((size_t)l * m.F + f) * d;
+            rows[(size_t)(g * nbg + 2 * p2 + 1) * 16 + w] = wu + ((size_t)l * m.F + f) * d;
+          }
+    }
     if (int r = pack_rows(c, rows, m.gu[l])) return r;
-    rows.assign((size_t)m.dn[l].plan.n_groups * 16, nullptr);
+    rows.assign((size_t)m.dn[l].plan.n_groups * m.dn[l].plan.shape.nb * 16, nullptr);
     for (int n = 0; n < d; ++n) rows[n] = wdn + ((size_t)l * d + n) * m.F;
     if (int r = pack_rows(c, rows, m.dn[l])) return r;
   }
   if (!m.lm_shared) {
-    rows.assign((size_t)m.lm.plan.n_groups * 16, nullptr);
+    rows.assign((size_t)m.lm.plan.n_groups * m.lm.plan.shape.nb * 16, nullptr);
     const uint16_t* lm = (const uint16_t*)md.lm_head;
     for (int n = 0; n < m.V; ++n) rows[n] = lm + (size_t)n * d;
     if (int r = pack_rows(c, rows, m.lm)) return r;
@@ -301,8 +314,8 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   for (int i = 0; i < m.n_blocks; ++i) bt[i] = m.n_blocks - 1 - i;
   HIPTRY(c, dalloc(&m.block_table, (size_t)m.n_blocks));
   HIPTRY(c, hipMemcpyAsync(m.block_table, bt.data(), bt.size() * 4, hipMemcpyHostToDevice, c->stream));
-  HIPTRY(c, dalloc(&m.inv_freq, (size_t)half));
-  HIPTRY(c, launch_inv_freq(m.inv_freq, m.hd, (double)m.theta, c->stream));
+  HIPTRY(c, dalloc(&m.rope, (size_t)c->p.max_seq * half));
+  HIPTRY(c, launch_rope_table(m.rope, c->p.max_seq, m.hd, (double)m.theta, c->stream));
   HIPTRY(c, hipStreamSynchronize(c->stream));
   return SPEC_OK;
 }
@@ -314,7 +327,7 @@ void free_model(Model& m) {
   (void)hipFree(m.kcache);
   (void)hipFree(m.vcache);
   (void)hipFree(m.block_table);
-  (void)hipFree(m.inv_freq);
+  (void)hipFree(m.rope);
   m = Model();
 }
 
@@ -359,7 +372,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profi
     a.q_dim = m.qd; a.kv_dim = m.kvd; a.head_dim = m.hd; a.n_kv = m.nkv;
     a.k_cache = m.kcache + (size_t)l * m.kv_layer_elems();
     a.v_cache = m.vcache + (size_t)l * m.kv_layer_elems();
-    a.block_table = m.block_table; a.inv_freq = m.inv_freq; a.max_seq = c->p.max_seq;
+    a.block_table = m.block_table; a.rope = m.rope; a.max_seq = c->p.max_seq;
     e = launch_gemm(m.qkv[l].plan.shape, EPI_QKV, a, s);
     if (e != hipSuccess) break;
     // causal attention over the paged cache -> packed A of the O projection
@@ -617,11 +630,20 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
     ssq_groups = std::max(ssq_groups, m->d / 64);
     for (int l = 0; l < m->L; ++l)
       ssq_groups = std::max({ssq_groups, m->o[l].plan.n_groups, m->dn[l].plan.n_groups});
+    // every RMSNorm consumer must be able to fold its producer's partials
+    auto cap = [](const Mat& x) { return x.plan.shape.waves * 64 / kMaxRows * kGemmMaxSsqPerThread; };
+    bool ok = m->d / 64 <= cap(m->qkv[0]) && m->dn[m->L - 1].plan.n_groups <= cap(m->lm);
+    for (int l = 0; l < m->L; ++l) {
+      ok = ok && m->o[l].plan.n_groups <= cap(m->gu[l]);
+      if (l > 0) ok = ok && m->dn[l - 1].plan.n_groups <= cap(m->qkv[l]);
+    }
+    if (!ok) return bail(fail(c, SPEC_ERR_ARG, "d_model too large for the RMSNorm partial fold"));
     const int qg = (m->nq / m->nkv) * kMaxRows;
     attn_ws = std::max(attn_ws, (size_t)m->nkv * c->attn_max_chunks * qg * (m->hd + 2));
-    if (attn_lds_bytes(m->hd, qg) > 64 * 1024) {
-      return bail(fail(c, SPEC_ERR_ARG, "attention tile exceeds 64 KiB of LDS"));
-    }
+    const size_t lds_need = attn_lds_bytes(m->hd, qg);
+    if (lds_need > kAttnMaxLds)
+      return bail(fail(c, SPEC_ERR_ARG, "attention tile exceeds the LDS of a CU"));
+    if (lds_need > 64 * 1024) TRYH(attn_reserve_lds(lds_need));
   }
   ar_choose_chunks(1, V, &c->ar_chunk, &c->ar_nchunks);
   c->sm_chunk = 4096;

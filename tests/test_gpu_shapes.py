@@ -1,0 +1,76 @@
+"""GPU parity at the workloads' real per-layer shapes, in the launch
+configurations bench.py uses (same GEMM plans, attention tiles, vocabulary
+sizes), with fewer layers so the fp64 oracle finishes in seconds:
+
+  * 8B-shaped target slice (d 4096, 32/8 heads x 128, FFN 14336, vocab
+    128256) with a 1B-shaped draft slice (d 2048, 32/8 x 64, tied head);
+  * 31B-shaped slice (d 5376, 32/16 heads x 168, FFN 21504, vocab 262144)
+    with a 4B-shaped draft slice (20/4 heads x 128: five query heads per KV
+    head), K = 5;
+  * 1.3B-shaped slice (MHA 16 x 128, vocab 32000) with a draft sharing the
+    target's embedding and LM head;
+  * a long context: 1500-token prompt through 32/8 x 128 attention.
+
+Every round is teacher-forced: draft rows (1e-4) and samples (bit-exact),
+target logits (2e-2) and rows (1e-4), accept/reject on the GPU's own rows
+(bit-exact), greedy tokens equal to the oracle's argmax or counted
+near-ties, and the committed state."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import Buffers, Shadow
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def run_case(tcfg, dcfg, prompt_len, K, rounds, greedy, share=(), seed=1003, max_extra=64):
+    import speculative_decoding_02_amd as sd
+    from gpu_util import gpu_round
+    tw = synth.weights_torch(tcfg, device="cuda")
+    dw = synth.weights_torch(dcfg, seed=synth.SEED_WEIGHTS + 1, device="cuda", share_from=tw,
+                             share=share)
+    torch.cuda.synchronize()
+    tb, db = synth.torch_to_bits(tw), synth.torch_to_bits(dw)
+    if share:
+        for k in share:  # the oracle sees the very same arrays
+            db[k] = tb[k]
+    prompt = synth.prompt(tcfg.vocab, prompt_len, seed=17)
+    max_seq = prompt_len + rounds * (K + 1) + max_extra
+    ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=greedy)
+    sh = Shadow(tcfg, tb, dcfg, db, prompt, max_seq, K, seed, greedy)
+    b = Buffers(K, tcfg.vocab)
+    for _ in range(rounds):
+        sh.check_round(gpu_round(sd, ctx, K, seed, b))
+        st = sd.spec_get_state(ctx)
+        assert st["device_error"] == 0
+        assert (st["target_len"], st["draft_len"]) == (sh.LT, sh.LD)
+    print(f"{tcfg.name}: logit err {sh.max_logit_err:.2e}, prob err {sh.max_prob_err:.2e}, "
+          f"draft prob err {sh.max_draft_prob_err:.2e}, near-ties {sh.near_ties}")
+    sd.spec_destroy(ctx)
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_8b_shaped_slice(greedy):
+    run_case(synth.L8B.replace(name="8b-slice-2L", n_layers=2),
+             synth.L8B_DRAFT.replace(name="1b-slice-1L", n_layers=1),
+             prompt_len=12, K=4, rounds=3, greedy=greedy)
+
+
+def test_31b_shaped_slice():
+    run_case(synth.G31B.replace(name="31b-slice-1L", n_layers=1),
+             synth.G31B_DRAFT.replace(name="4b-slice-1L", n_layers=1),
+             prompt_len=7, K=5, rounds=2, greedy=False)
+
+
+def test_13b_shaped_slice_shared_head():
+    run_case(synth.L13B.replace(name="1.3b-slice-2L", n_layers=2),
+             synth.L13B_DRAFT.replace(name="1.3b-draft-slice-1L", n_layers=1),
+             prompt_len=20, K=4, rounds=3, greedy=False, share=("embed", "lm_head"))
+
+
+def test_long_context_attention():
+    t = synth.ModelConfig("long-ctx-1L", 1, 256, 32, 8, 128, 512, 1024)
+    d = t.replace(name="long-ctx-draft")
+    run_case(t, d, prompt_len=1500, K=4, rounds=3, greedy=False)
