@@ -15,6 +15,7 @@ around each of its launches, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +25,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) of this script, with the hash of the kernel sources
+# they were taken with; used only while the sources still hash the same.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_8b_k4_traffic.txt")
+KERNEL_SOURCES = ("k_gemm.hip", "common.h", "kernels.h", "spec_api.cpp")
+COPY_CALIB_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """(bytes per launch, note) from the committed counter summary, or
+    (None, reason) when there is none or the kernel sources changed since."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_digest():
+            return None, "kernel sources changed since the counters were taken"
+        return int(kv["traffic_bytes_per_launch"]), os.path.relpath(TRAFFIC_FILE, ROOT)
+    except (OSError, KeyError, ValueError):
+        return None, "no counter summary"
 
 
 def log(*a):
@@ -66,8 +98,10 @@ def main():
     ap.add_argument("--greedy", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rounds", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--kernel-rounds", type=int, default=5)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run a plain copy of 1 GiB three times (calibrates HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -87,6 +121,15 @@ def main():
     rounds_total = args.steps + args.warmup
     max_seq = plen + (K + 1) * (rounds_total + args.kernel_rounds) + 16
     torch.cuda.set_device(0)
+    if args.copy_calib:
+        # a plain elementwise copy (negation): COPY_CALIB_BYTES read and written per launch
+        xs = torch.ones(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        ys = torch.empty_like(xs)
+        for _ in range(3):
+            torch.neg(xs, out=ys)
+        torch.cuda.synchronize()
+        del xs, ys
+        log("copy calibration: 3 launches of torch.neg over 1 GiB fp32")
     t0 = time.time()
     tw = synth.weights_torch(tcfg, device="cuda")
     share = ("embed", "lm_head") if args.pair in ("toy", "1.3b") else ()
@@ -168,8 +211,10 @@ def main():
         avg_bytes = (b_d + b_t) / n_l
         avg_ms = float((kt_d.sum() + kt_t.sum()) / n_l)
         ach = avg_bytes / (avg_ms / 1e3) / 1e9
+        traffic, traffic_note = measured_traffic()
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "traffic_note": traffic_note,
                 "kernel": "gemm_skinny<..., EPI_SILU>: gate/up GEMM + RMSNorm scale + SiLU*up",
                 "launches": n_l, "avg_launch_us": round(avg_ms * 1e3, 2),
                 "avg_algorithmic_bytes": int(avg_bytes),
@@ -255,10 +300,10 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
 
 
 def _rounds(oracle, T, Dm, prompt, K, args):
-    # n_new = 1 token per round minimum: ask for cpu_rounds tokens, which
-    # takes at most cpu_rounds rounds; the stats report the rounds run.
-    return oracle.spec_generate(T, Dm, prompt, args.cpu_rounds, K, greedy=args.greedy,
-                                seed=1003)
+    # at least one token per round: asking for cpu_tokens tokens bounds the
+    # rounds by cpu_tokens; the stats report the rounds actually run.
+    return oracle.spec_generate(T, Dm, prompt, args.cpu_tokens, K, greedy=args.greedy,
+                                seed=synth.SEED_PHILOX)
 
 
 if __name__ == "__main__":

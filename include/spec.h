@@ -188,8 +188,9 @@ int spec_get_history(spec_ctx* ctx, int32_t* host_out, int32_t n);
 int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out);
 
 /* Profiling switch.  When on, spec_draft and spec_verify launch their
- * kernels directly (no graph replay) and record a hipEvent pair around every
- * launch of the feed-forward gate/up GEMM, read back by spec_kernel_times;
+ * kernels directly (no graph replay) and launch the feed-forward gate/up GEMM
+ * with a hipEvent pair that takes that kernel's own start and end timestamps
+ * (hipExtLaunchKernel), read back by spec_kernel_times;
  * kernels and results are the same as with graphs.  Synchronises.  Also set
  * at creation by spec_init_params.profile_kernels. */
 int spec_set_profiling(spec_ctx* ctx, int32_t enable);

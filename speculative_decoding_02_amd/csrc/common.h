@@ -48,13 +48,35 @@ SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) {
 }
 
 // ------------------------------------------------------------- KV cache --
-// Paged cache of one layer: [block][kv head][16 tokens][2][head_dim] bf16,
-// where [0] is the bf16 high part of the fp32 key/value and [1] the low part
-// (x - hi).  Keeping ~16 mantissa bits matters: rounding keys and values to
-// one bf16 is the largest error source of the pass (it compounds through the
-// feed-forward blocks to ~1e-2 logit error on an 8B-shaped slice).
+// Paged caches of one layer, in blocks of 16 tokens.  Every key and value is
+// kept as two bf16 planes: [0] the bf16 high part of the fp32 value, [1] the
+// low part (x - hi).  Keeping ~16 mantissa bits matters: rounding keys and
+// values to one bf16 is the largest error source of the pass (it compounds
+// through the feed-forward blocks to ~1e-2 logit error on an 8B-shaped
+// slice).
+//   keys:   [block][kv head][16 tokens][2][head_dim]  -- a token's 8
+//           consecutive dims are one 16-byte MFMA fragment row
+//   values: [block][kv head][2][head_dim][16 tokens]  -- transposed, so 4
+//           consecutive tokens of one dim are one 8-byte load
 SPEC_DEVICE size_t kv_index(int blk, int n_kv, int head, int slot, int hd, int part, int dim) {
   return ((((size_t)blk * n_kv + head) * kBlock + slot) * 2 + part) * hd + dim;
+}
+SPEC_DEVICE size_t vt_index(int blk, int n_kv, int head, int part, int hd, int dim, int slot) {
+  return ((((size_t)blk * n_kv + head) * 2 + part) * hd + dim) * kBlock + slot;
+}
+
+// Query fragments of the attention, written by the QKV epilogue:
+// [n_kv][ceil(G/2)][n_es][2 parts][64 lanes][8 bf16] with G = n_q / n_kv and
+// n_es = ceil(hd/32).  Query vector qi = row * G + g of kv head h (query head
+// h*G + g) is column qi % 16 of tile qi / 16; part 0 holds its bf16 high
+// parts, part 1 the low parts; lane l of e-step es holds dims
+// 32 es + 8 (l / 16) .. + 7 of column l % 16 (the B operand layout of
+// v_mfma_f32_16x16x32_bf16).
+SPEC_DEVICE size_t qfrag_index(int h, int G, int n_es, int qi, int part, int dim) {
+  const int lane = (qi & 15) + 16 * ((dim & 31) >> 3);
+  const int n_qt = (G + 1) / 2;
+  return (((((size_t)h * n_qt + (qi >> 4)) * n_es + (dim >> 5)) * 2 + part) * 64 + lane) * 8 +
+         (dim & 7);
 }
 
 // ------------------------------------------------- packed MFMA A operand --

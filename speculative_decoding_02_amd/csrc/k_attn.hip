@@ -4,19 +4,28 @@
 // Row r (position pos0 + r) attends to keys 0..pos0+r: row i of the verify
 // pass sees the context plus drafts d_1..d_{i-1}, which is what makes its
 // output the target distribution T_i = T(. | x, d_1..d_{i-1}) ([int]
-// algorithm core, Step 2).  Grouped-query heads: query head h reads KV head
-// h / (n_q / n_kv); all query heads of a group and all rows share one read of
-// each key/value chunk.
+// algorithm core, Step 2).  Grouped-query heads: query head h*G + g reads KV
+// head h; all G query heads of a group and all rows share one read of each
+// key and value.
 //
 // Two launches, no inter-block waiting:
-//  (1) partial kernel, workgroup (64-key chunk c, kv head h): scores and the
-//      probability-weighted value sums on v_mfma_f32_16x16x32_bf16.  Queries
-//      and probabilities enter as bf16 high/low row pairs, keys and values
-//      as the cache's bf16 high/low planes (two MFMAs per fragment), so every
-//      operand keeps ~16 mantissa bits.  Per query it writes (max score, sum
-//      of exp, unnormalised value sum) for the chunk.
-//  (2) merge kernel: combines the chunks in chunk order (deterministic) and
-//      writes the output rows as the packed A operand of the O projection.
+//  (1) partial kernel, one wave per (32-key chunk, kv head).  Everything
+//      lives in registers: the wave issues all its loads at once (key
+//      fragments, value fragments, query fragments), then
+//        S^T = K Q^T  and  O^T = V^T P^T   on v_mfma_f32_16x16x32_bf16
+//      over tiles of 16 query vectors.  Keys and values enter as the cache's
+//      bf16 high/low planes, queries and probabilities as bf16 high/low
+//      operands; the products hi*hi + hi*lo + lo*hi accumulate in one
+//      register tile, so every product keeps ~16 mantissa bits (the lo*lo
+//      term, ~2^-16 relative to the others, is left out).  The C layout of
+//      S^T already gives each lane the 8 keys that form its slots of the P^T
+//      operand, so lanes exchange data only for the max and the sum over
+//      keys.  Per query it writes (max score, sum of exp, unnormalised value
+//      sum) for the chunk.
+//  (2) merge kernel, one workgroup per (query vector, kv head): all chunk
+//      partials are loaded at once and combined with running-max rescaling,
+//      per thread and then across threads in a fixed order (deterministic);
+//      it writes the packed A operand of the O projection.
 #include "kernels.h"
 
 namespace spec {
@@ -24,250 +33,288 @@ namespace spec {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-SPEC_DEVICE bf16x8_t as_bf16x8_a(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// LDS layout of the partial kernel (bf16 unless noted):
-//   Kt [2][64 keys][E32 + 8]    keys (high, low planes), e padded to a
-//                               multiple of 32 (+8 against bank conflicts)
-//   Vt [2][E16][64 + 8]         values transposed (e-major), for B fragments
-//   Qa [n_qt][n_es][64][8]      query A fragments (hi rows 0-7, lo rows 8-15);
-//                               reused as S [qg_max][64] fp32 after the scores
-//   Pa [n_qt][2][64][8]         probability A fragments
-struct AttnLds {
-  int E32, E16, n_es, n_et, n_qt, kstride, vstride;
-  size_t kplane, vplane;  // elements per plane
-  size_t off_v, off_q, off_p, bytes;
-};
-
-__host__ __device__ inline AttnLds attn_lds(int hd, int qg_max) {
-  AttnLds L;
-  L.E32 = (hd + 31) / 32 * 32;
-  L.E16 = (hd + 15) / 16 * 16;
-  L.n_es = L.E32 / 32;
-  L.n_et = L.E16 / 16;
-  L.n_qt = (qg_max + 7) / 8;
-  L.kstride = L.E32 + 8;
-  L.vstride = kAttnChunk + 8;
-  L.kplane = (size_t)kAttnChunk * L.kstride;
-  L.vplane = (size_t)L.E16 * L.vstride;
-  const size_t qb = (size_t)L.n_qt * L.n_es * 1024;
-  const size_t sb = (size_t)qg_max * kAttnChunk * 4;
-  L.off_v = 2 * L.kplane * 2;
-  L.off_q = L.off_v + 2 * L.vplane * 2;
-  L.off_p = L.off_q + (qb > sb ? qb : sb);
-  L.bytes = L.off_p + (size_t)L.n_qt * 2 * 1024;
-  return L;
+SPEC_DEVICE floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-size_t attn_lds_bytes(int hd, int qg_max) { return attn_lds(hd, qg_max).bytes; }
+// Raw buffer resources (gfx9 descriptor word 3): loads at offsets >= size
+// return zero.
+constexpr uint32_t kOOB = 0x80000000u;
+SPEC_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+SPEC_DEVICE uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+SPEC_DEVICE uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
 
-// element index of (row m of 16, k of 32) inside one 1 KiB A fragment
-SPEC_DEVICE int afrag_index(int row, int kk) { return (row + 16 * (kk >> 3)) * 8 + (kk & 7); }
-
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Fragment layouts (lane l, l16 = l % 16, grp = l / 16):
+//   A (16 x 32):  lane l holds row l16, k = 8 grp .. 8 grp + 7
+//   B (32 x 16):  lane l holds column l16, k = 8 grp .. 8 grp + 7
+//   C (16 x 16):  lane l holds rows 4 grp + r (r = 0..3) of column l16
+// S^T tile (kt, qt): rows = keys 16 kt + 0..15 of the chunk, columns = query
+// vectors 16 qt + 0..15.  The P^T operand's k slot 8 grp + j of lane l is
+// key 16 (j / 4) + 4 grp + (j % 4) -- exactly the keys lane l holds in the C
+// layouts of tiles kt = 0, 1; the V^T operand uses the same slot order (two
+// 4-key runs of the transposed value cache).
+template <int NES>
+__global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
+  constexpr int QTG = NES <= 4 ? 2 : 1;  // 16-query tiles per register group
+  constexpr int NET = 2 * NES;            // e-tiles of 16 covering 32*NES dims
+  const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
   const int c = blockIdx.x, h = blockIdx.y;
-  const int hd = a.hd;
-  const int G = a.n_q / a.n_kv;
+  const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
   const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
   const int n_keys = pos0 + n_rows;
-  const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
-  if (n_rows <= 0 || c >= n_active) return;
-  const int QG = G * n_rows;  // query vectors: qi = r * G + gi
-  const AttnLds L = attn_lds(hd, a.qg_max);
-  uint16_t* Kt = (uint16_t*)lds;
-  uint16_t* Vt = (uint16_t*)(lds + L.off_v);
-  uint16_t* Qa = (uint16_t*)(lds + L.off_q);
-  float* S = (float*)(lds + L.off_q);  // aliases Qa after the scores
-  uint16_t* Pa = (uint16_t*)(lds + L.off_p);
-
-  // ---- stage keys (row-major), values (transposed), queries (hi/lo) -------
-  const int t0 = c * kAttnChunk;
-  const int vec_per_row = L.E32 / 8;
-  for (int idx = tid; idx < 2 * kAttnChunk * vec_per_row; idx += 256) {
-    const int part = idx / (kAttnChunk * vec_per_row);
-    const int rest = idx % (kAttnChunk * vec_per_row);
-    const int i = rest / vec_per_row, e = (rest % vec_per_row) * 8;
-    const int t = t0 + i;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (t < n_keys && e < hd) {
-      const int blk = a.block_table[t / kBlock];
-      const size_t off = kv_index(blk, a.n_kv, h, t % kBlock, hd, part, e);
-      kv = *(const uint4*)(a.k_cache + off);
-      vv = *(const uint4*)(a.v_cache + off);
-    }
-    *(uint4*)(Kt + part * L.kplane + i * L.kstride + e) = kv;
-    if (e < L.E16) {
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-      uint16_t* vp = Vt + part * L.vplane;
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-        if (e + x < L.E16) vp[(e + x) * L.vstride + i] = (uint16_t)(w[x >> 1] >> ((x & 1) * 16));
-    }
-  }
-  // query fragments: (q-tile qt, e-step es, lane) -> 8 e of one query, hi or lo
-  for (int idx = tid; idx < L.n_qt * L.n_es * 64; idx += 256) {
-    const int ln = idx & 63, es = (idx >> 6) % L.n_es, qt = (idx >> 6) / L.n_es;
-    const int row = ln & 15, qi = qt * 8 + (row & 7), part = row >> 3;
-    const int e0 = es * 32 + (ln >> 4) * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (qi < QG) {
-      const int r = qi / G, gi = qi % G;
-      const float* qp = a.q + (size_t)r * a.n_q * hd + (size_t)(h * G + gi) * hd;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) v[x] = e0 + x < hd ? qp[e0 + x] : 0.0f;
-    }
-    uint16_t hv[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const uint16_t hi = f32_to_bf16_rne(v[x]);
-      hv[x] = part ? f32_to_bf16_rne(v[x] - bf16_to_f32(hi)) : hi;
-    }
-    *(uint4*)(Qa + (size_t)idx * 8) =
-        make_uint4(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
-                   pack_bf16x2(hv[6], hv[7]));
-  }
-  __syncthreads();
-
-  // ---- scores S = Q K^T: wave w owns keys 16w..16w+15 ----------------------
-  const int n_qt = (QG + 7) / 8;
-  floatx4 sacc[8];
-#pragma unroll
-  for (int qt = 0; qt < 8; ++qt) sacc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int es = 0; es < L.n_es; ++es) {
-    // B fragments: lane l -> key 16w + l%16, e = 32es + 8(l/16) .. +7, high
-    // and low planes of the key
-    const size_t koff = (size_t)(wave * 16 + (lane & 15)) * L.kstride + es * 32 + (lane >> 4) * 8;
-    const uint4 kh = *(const uint4*)(Kt + koff);
-    const uint4 kl = *(const uint4*)(Kt + L.kplane + koff);
-#pragma unroll
-    for (int qt = 0; qt < 8; ++qt)
-      if (qt < n_qt) {
-        const uint4 qa = *(const uint4*)(Qa + ((size_t)(qt * L.n_es + es) * 64 + lane) * 8);
-        sacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(qa), as_bf16x8_a(kh),
-                                                           sacc[qt], 0, 0, 0);
-        sacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(qa), as_bf16x8_a(kl),
-                                                           sacc[qt], 0, 0, 0);
-      }
-  }
-  __syncthreads();  // Qa is about to be overwritten by S
+  const int key0 = c * kAttnChunk;
+  if (n_rows <= 0 || key0 >= n_keys) return;
+  const int QG = G * n_rows, n_qt = (QG + 15) / 16, n_qt_max = (G + 1) / 2;
+  const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
   const float scale = 1.0f / sqrtf((float)hd);
+  float* wso = a.ws_o + ((size_t)h * a.max_chunks + c) * a.qg_max * E16;
+  float2* wsml = a.ws_ml + ((size_t)h * a.max_chunks + c) * a.qg_max;
+
+  // Buffer loads: an offset at or past the resource's size reads as zero,
+  // which masks padded dims, absent keys and unused query columns without
+  // branches, so every load of the wave is in flight at once.
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.kv_layer_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.kv_layer_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf, a.qf_bytes);
+  uint4 qf[QTG][NES][2];
+  auto load_q = [&](int qt0) {
 #pragma unroll
-  for (int qt = 0; qt < 8; ++qt)
-    if (qt < n_qt) {
+    for (int t = 0; t < QTG; ++t) {
+      const int qt = qt0 + t, qi = 16 * qt + l16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = sacc[qt][r] + __shfl_down(sacc[qt][r], 32);  // hi + lo rows
-        const int qi = qt * 8 + 4 * ((lane >> 4) & 1) + r;
-        const int key = wave * 16 + (lane & 15);
-        if (lane < 32 && qi < QG) {
-          const int t = t0 + key;
-          const bool vis = t < n_keys && t <= pos0 + qi / G;
-          S[qi * kAttnChunk + key] = vis ? v * scale : -INFINITY;
+      for (int es = 0; es < NES; ++es) {
+        const bool ok = qt < n_qt && qi < QG && 32 * es + 8 * grp < hd;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t off =
+              (uint32_t)((((((size_t)h * n_qt_max + qt) * n_es + es) * 2 + p) * 64 + lane) * 16);
+          qf[t][es][p] = load16(rq, ok ? off : kOOB);
         }
       }
     }
-  __syncthreads();
+  };
+  load_q(0);
 
-  // ---- softmax pieces per query (lane = key), probabilities as A fragments --
-  float* my_ws = a.ws + ((size_t)h * a.max_chunks + c) * a.qg_max * (hd + 2);
-  for (int qi = wave; qi < n_qt * 8; qi += 4) {
-    float p = 0.0f;
-    if (qi < QG) {
-      const float sc = S[qi * kAttnChunk + lane];
-      const float mx = wave_max_f32(sc);
-      p = (sc != -INFINITY) ? expf(sc - mx) : 0.0f;
-      const float l = wave_sum_f32(p);
-      if (lane == 0) {
-        my_ws[(size_t)qi * (hd + 2) + 0] = mx;
-        my_ws[(size_t)qi * (hd + 2) + 1] = l;
+  // cache blocks of the chunk; the second only where it holds keys
+  const int blk0 = a.block_table[2 * c];
+  const int blk1 = key0 + kBlock < n_keys ? a.block_table[2 * c + 1] : blk0;
+  uint4 kf[2][NES][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = key0 + 16 * kt + l16;
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      const int e0 = 32 * es + 8 * grp;
+      const bool ok = key < n_keys && e0 < hd;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t off = (uint32_t)(kv_index(kt ? blk1 : blk0, n_kv, h, l16, hd, p, e0) * 2);
+        kf[kt][es][p] = load16(rk, ok ? off : kOOB);
       }
     }
-    const uint16_t ph = f32_to_bf16_rne(p);
-    const uint16_t pl = f32_to_bf16_rne(p - bf16_to_f32(ph));
-    const int qt = qi / 8, m = qi % 8, ks = lane >> 5, kk = lane & 31;
-    uint16_t* frag = Pa + (size_t)(qt * 2 + ks) * 512;
-    frag[afrag_index(m, kk)] = ph;
-    frag[afrag_index(m + 8, kk)] = pl;
   }
-  __syncthreads();
-
-  // ---- unnormalised value sums O = P V: wave w owns e-tiles w, w+4, ... ----
-  for (int et = wave; et < L.n_et; et += 4) {
-    // B fragments: lane l -> e = 16et + l%16, keys 32ks + 8(l/16) .. +7
-    const uint16_t* vrow = Vt + (et * 16 + (lane & 15)) * L.vstride + (lane >> 4) * 8;
-    const uint4 vh0 = *(const uint4*)(vrow);
-    const uint4 vh1 = *(const uint4*)(vrow + 32);
-    const uint4 vl0 = *(const uint4*)(vrow + L.vplane);
-    const uint4 vl1 = *(const uint4*)(vrow + L.vplane + 32);
-    for (int qt = 0; qt < n_qt; ++qt) {
-      floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
-      const uint4 pa0 = *(const uint4*)(Pa + ((size_t)(qt * 2 + 0) * 64 + lane) * 8);
-      const uint4 pa1 = *(const uint4*)(Pa + ((size_t)(qt * 2 + 1) * 64 + lane) * 8);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(pa0), as_bf16x8_a(vh0), o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(pa1), as_bf16x8_a(vh1), o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(pa0), as_bf16x8_a(vl0), o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_a(pa1), as_bf16x8_a(vl1), o, 0, 0, 0);
+  uint4 vf[NET][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = o[r] + __shfl_down(o[r], 32);
-        const int qi = qt * 8 + 4 * ((lane >> 4) & 1) + r;
-        const int e = et * 16 + (lane & 15);
-        if (lane < 32 && qi < QG && e < hd) my_ws[(size_t)qi * (hd + 2) + 2 + e] = v;
+  for (int et = 0; et < NET; ++et) {
+    const int e = 16 * et + l16;
+    const bool ok = e < hd;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t o0 = (uint32_t)(vt_index(blk0, n_kv, h, p, hd, e, 4 * grp) * 2);
+      const uint32_t o1 = (uint32_t)(vt_index(blk1, n_kv, h, p, hd, e, 4 * grp) * 2);
+      const uint2 w0 = load8(rv, ok ? o0 : kOOB), w1 = load8(rv, ok ? o1 : kOOB);
+      vf[et][p] = make_uint4(w0.x, w0.y, w1.x, w1.y);
+    }
+  }
+
+  for (int qt0 = 0; qt0 < n_qt; qt0 += QTG) {
+    if (qt0 > 0) load_q(qt0);
+#pragma unroll
+    for (int t = 0; t < QTG; ++t) {
+      const int qt = qt0 + t;
+      if (qt >= n_qt) continue;  // wave-uniform
+      // ---- scores S^T = K Q^T for the 32 keys -----------------------------
+      floatx4 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int es = 0; es < NES; ++es) {
+          s[kt] = mfma16(kf[kt][es][0], qf[t][es][0], s[kt]);
+          s[kt] = mfma16(kf[kt][es][0], qf[t][es][1], s[kt]);
+          s[kt] = mfma16(kf[kt][es][1], qf[t][es][0], s[kt]);
+        }
       }
+      const int qi = 16 * qt + l16;
+      const int limit = pos0 + qi / G;  // last key row qi's position sees
+      float sc[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kt + 4 * grp + r;
+          const bool vis = qi < QG && key < n_keys && key <= limit;
+          sc[kt][r] = vis ? s[kt][r] * scale : -INFINITY;
+          mx = fmaxf(mx, sc[kt][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float lsum = 0.0f;
+      uint16_t ph[8], pl[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = sc[j >> 2][j & 3];
+        const float pv = x == -INFINITY ? 0.0f : expf(x - mx);
+        lsum += pv;
+        ph[j] = f32_to_bf16_rne(pv);
+        pl[j] = f32_to_bf16_rne(pv - bf16_to_f32(ph[j]));
+      }
+      lsum += __shfl_xor(lsum, 16);
+      lsum += __shfl_xor(lsum, 32);
+      const uint4 pfh = make_uint4(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                                   pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7]));
+      const uint4 pfl = make_uint4(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]),
+                                   pack_bf16x2(pl[4], pl[5]), pack_bf16x2(pl[6], pl[7]));
+      // ---- unnormalised value sums O^T = V^T P^T --------------------------
+#pragma unroll
+      for (int et = 0; et < NET; ++et) {
+        if (et >= n_et) continue;  // wave-uniform
+        floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+        o = mfma16(vf[et][0], pfh, o);
+        o = mfma16(vf[et][0], pfl, o);
+        o = mfma16(vf[et][1], pfh, o);
+        if (qi < QG)
+          *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (grp == 0 && qi < QG) wsml[qi] = make_float2(mx, lsum);
     }
   }
 }
 
-// Merge the chunks of kv head h in chunk order.  Thread = (query, 8 dims);
-// the chunk loop is unrolled so its loads are in flight together.
+// Merge of the chunk partials of query vector qi of kv head h.  Thread
+// (chunk group cg, 8-dim group d8) takes chunks cg, cg + ncg, ... and keeps a
+// running (max, sum, value sum), rescaling by exp(m_old - m_new); the thread
+// states are then brought to the block-wide maximum and summed in cg order
+// (deterministic).
+constexpr int kMergeBatch = 4;
+
+struct MergeState {
+  float m, l, o[8];
+};
+
+// branch-free: a chunk with no visible key has m = -inf and weight 0
+SPEC_DEVICE void merge_in(MergeState& st, float m, float l, const float* o) {
+  const float mn = fmaxf(st.m, m);
+  const float a = st.m == -INFINITY ? 0.0f : expf(st.m - mn);
+  const float b = m == -INFINITY ? 0.0f : expf(m - mn);
+  st.l = st.l * a + l * b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.o[e] = st.o[e] * a + o[e] * b;
+  st.m = mn;
+}
+
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int h = blockIdx.x;
+  __shared__ float s_o[256 * 9];
+  __shared__ float s_m[4];
+  const int qi = blockIdx.x, h = blockIdx.y;
   const int hd = a.hd, G = a.n_q / a.n_kv;
   const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int QG = G * n_rows;
+  if (n_rows <= 0 || qi >= QG) return;
   const int n_keys = pos0 + n_rows;
   const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
-  if (n_rows <= 0) return;
-  const int QG = G * n_rows, per = hd / 8;
-  const int idx = blockIdx.y * blockDim.x + threadIdx.x;
-  if (idx >= QG * per) return;
-  const int qi = idx / per, e0 = (idx % per) * 8;
-  const float* base = a.ws + (size_t)h * a.max_chunks * a.qg_max * (hd + 2) + (size_t)qi * (hd + 2);
-  const size_t cstride = (size_t)a.qg_max * (hd + 2);
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int cc = 0; cc < n_active; ++cc) M = fmaxf(M, base[cc * cstride]);
-  float L = 0.0f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int cc = 0; cc < n_active; ++cc) {
-    const float* pc = base + cc * cstride;
-    const float m = pc[0];
-    const float w = m == -INFINITY ? 0.0f : expf(m - M);
-    L += pc[1] * w;
+  const int E16 = (hd + 15) / 16 * 16;
+  const int n8 = hd / 8, ncg = 256 / n8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = tid / n8, d8 = tid % n8;
+  const size_t cs_ml = (size_t)a.qg_max, cs_o = (size_t)a.qg_max * E16;
+  const float2* ml = a.ws_ml + (size_t)h * a.max_chunks * a.qg_max + qi;
+  const float* wo = a.ws_o + ((size_t)h * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
+  const bool worker = cg < ncg;
+
+  MergeState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) O[e] += pc[2 + e0 + e] * w;
+  for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
+  for (int c0 = worker ? cg : n_active; c0 < n_active; c0 += kMergeBatch * ncg) {
+    float4 v0[kMergeBatch], v1[kMergeBatch];
+    float2 mv[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int cc = c0 + u * ncg;
+      const size_t cl = cc < n_active ? (size_t)cc : 0;
+      mv[u] = ml[cl * cs_ml];
+      v0[u] = *(const float4*)(wo + cl * cs_o);
+      v1[u] = *(const float4*)(wo + cl * cs_o + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before any use
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool ok = c0 + u * ncg < n_active;
+      const float o[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+      merge_in(st, ok ? mv[u].x : -INFINITY, ok ? mv[u].y : 0.0f, o);
+    }
   }
-  const float inv = 1.0f / L;
+  // block-wide maximum
+  const float wm = wave_max_f32(st.m);
+  if (lane == 0) s_m[wave] = wm;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float sc = st.m == -INFINITY ? 0.0f : expf(st.m - M);
+  float* my = s_o + tid * 9;
+  my[0] = st.l * sc;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) O[e] *= inv;
-  const int r = qi / G, gi = qi % G;
-  apack_store8(a.Ap_out, r, (h * G + gi) * hd + e0, O);
+  for (int e = 0; e < 8; ++e) my[1 + e] = st.o[e] * sc;
+  __syncthreads();
+  if (tid < n8) {
+    float acc[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < ncg; ++g) {
+      const float* q = s_o + (g * n8 + tid) * 9;
+#pragma unroll
+      for (int e = 0; e < 9; ++e) acc[e] += q[e];
+    }
+    const float inv = 1.0f / acc[0];
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = acc[1 + e] * inv;
+    const int r = qi / G, gi = qi % G;
+    apack_store8(a.Ap_out, r, (h * G + gi) * hd + tid * 8, out);
+  }
 }
 
-hipError_t attn_reserve_lds(size_t bytes) {
-  return hipFuncSetAttribute((const void*)attn_partial_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+template <int NES>
+static void launch_partial(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv), dim3(64), 0, s, a);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_partial_kernel, dim3(a.max_chunks, a.n_kv), dim3(256),
-                     attn_lds_bytes(a.hd, a.qg_max), s, a);
+  switch ((a.hd + 31) / 32) {
+    case 1: launch_partial<1>(a, s); break;
+    case 2: launch_partial<2>(a, s); break;
+    case 3: launch_partial<3>(a, s); break;
+    case 4: launch_partial<4>(a, s); break;
+    case 5: launch_partial<5>(a, s); break;
+    case 6: launch_partial<6>(a, s); break;
+    case 7: launch_partial<7>(a, s); break;
+    case 8: launch_partial<8>(a, s); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int per_head = a.qg_max * (a.hd / 8);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_kv, (per_head + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.qg_max, a.n_kv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

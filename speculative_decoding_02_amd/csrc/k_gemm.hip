@@ -22,6 +22,8 @@
 //    squares published by the producer.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "kernels.h"
 
 namespace spec {
@@ -242,7 +244,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
         const float val = hf ? hi * r.x + lo * r.y : lo * r.x - hi * r.y;
         const int dim = jj + hf * half_hd;
         if (is_q) {
-          a.out[(size_t)m * a.ldo + (size_t)head * a.head_dim + dim] = val;
+          const int G = a.q_dim / a.kv_dim, n_es = (a.head_dim + 31) / 32;
+          const int qi = m * G + head % G;
+          const uint16_t hb = f32_to_bf16_rne(val);
+          a.qf[qfrag_index(head / G, G, n_es, qi, 0, dim)] = hb;
+          a.qf[qfrag_index(head / G, G, n_es, qi, 1, dim)] = f32_to_bf16_rne(val - bf16_to_f32(hb));
         } else {
           const int blk = a.block_table[pos / kBlock];
           const uint16_t hb = f32_to_bf16_rne(val);
@@ -255,25 +261,37 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
         const int head = f0 / a.head_dim, dim = f0 % a.head_dim;
         const int blk = a.block_table[pos / kBlock];
         const uint16_t hb = f32_to_bf16_rne(mine);
-        a.v_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 0, dim)] = hb;
-        a.v_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 1, dim)] =
+        a.v_cache[vt_index(blk, a.n_kv, head, 0, a.head_dim, dim, pos % kBlock)] = hb;
+        a.v_cache[vt_index(blk, a.n_kv, head, 1, a.head_dim, dim, pos % kBlock)] =
             f32_to_bf16_rne(mine - bf16_to_f32(hb));
       }
     }
   }
 }
 
+// Plain launch, or (ev0 != null) a launch whose start/stop events take the
+// kernel's own start and end timestamps.
+template <typename Kern>
+static void launch_one(Kern k, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a,
+                       hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0)
+    hipExtLaunchKernelGGL(k, grid, block, 0, s, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL(k, grid, block, 0, s, a);
+}
+
 template <int NB, int W>
-static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s, hipEvent_t ev0,
+                             hipEvent_t ev1) {
   const dim3 grid(a.n_groups), block(W * 64);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE>), grid, block, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID>), grid, block, 0, s, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV>), grid, block, 0, s, a); break;
-    case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS>), grid, block, 0, s, a); break;
+    case EPI_STORE: launch_one(gemm_skinny<NB, W, EPI_STORE>, grid, block, s, a, ev0, ev1); break;
+    case EPI_RESID: launch_one(gemm_skinny<NB, W, EPI_RESID>, grid, block, s, a, ev0, ev1); break;
+    case EPI_QKV: launch_one(gemm_skinny<NB, W, EPI_QKV>, grid, block, s, a, ev0, ev1); break;
+    case EPI_LOGITS: launch_one(gemm_skinny<NB, W, EPI_LOGITS>, grid, block, s, a, ev0, ev1); break;
     case EPI_SILU:
       if constexpr (NB % 2 == 0) {
-        hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a);
+        launch_one(gemm_skinny<NB, W, EPI_SILU>, grid, block, s, a, ev0, ev1);
         break;
       }
       return hipErrorInvalidValue;
@@ -282,15 +300,16 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s, hipEvent_t ev0,
+                       hipEvent_t ev1) {
   if (sh.waves == 4) {
-    if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s);
-    if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s);
-    if (sh.nb == 4) return launch_epi<4, 4>(epi, a, s);
+    if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s, ev0, ev1);
+    if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s, ev0, ev1);
+    if (sh.nb == 4) return launch_epi<4, 4>(epi, a, s, ev0, ev1);
   } else if (sh.waves == 8) {
-    if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s);
-    if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s);
-    if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s);
+    if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s, ev0, ev1);
+    if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s, ev0, ev1);
+    if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s, ev0, ev1);
   }
   return hipErrorInvalidValue;
 }

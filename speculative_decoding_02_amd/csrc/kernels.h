@@ -17,7 +17,7 @@ enum Epi : int {
   EPI_RESID = 1,   // resid[m][n] += y; packed (resid * gain_next) for the next GEMM;
                    // per-workgroup sums of squares for the next RMSNorm
   EPI_SILU = 2,    // packed silu(gate) * up for the down projection (blocks alternate gate/up)
-  EPI_QKV = 3,     // RoPE on q/k, q -> out, k/v -> paged KV cache
+  EPI_QKV = 3,     // RoPE on q/k; q -> attention query fragments, k/v -> paged KV cache
   EPI_LOGITS = 4,  // out[m][n] = logit; per-workgroup (max, sum exp) partials
 };
 
@@ -45,7 +45,8 @@ struct GemmArgs {
   float* ssq_out;     // EPI_RESID: [n_groups][8]
   float2* lm_part;    // EPI_LOGITS: [n_groups][8]
   int n_valid;        // EPI_LOGITS: valid columns (vocab)
-  // EPI_QKV
+  // EPI_QKV: q -> query fragments, k/v -> paged caches
+  uint16_t* qf;
   int q_dim, kv_dim, head_dim, n_kv;
   uint16_t* k_cache;
   uint16_t* v_cache;
@@ -58,7 +59,10 @@ struct GemmShape {
   int nb;      // 16-column blocks per workgroup
   int waves;   // waves per workgroup, splitting K
 };
-hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
+// With ev0/ev1 non-null the two events take the kernel's own start and end
+// timestamps (hipExtLaunchKernel), for per-kernel timing on the stream.
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s,
+                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
 constexpr int kGemmMaxSsqPerThread = 16;
 
@@ -69,22 +73,21 @@ hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_grou
 
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
-  const float* q;            // [n_rows][n_q*hd]
-  const uint16_t* k_cache;   // [n_blocks][n_kv][16][2][hd] (see kv_index)
-  const uint16_t* v_cache;
+  const uint16_t* qf;        // query fragments (see qfrag_index)
+  const uint16_t* k_cache;   // one layer, see kv_index
+  const uint16_t* v_cache;   // one layer, see vt_index
+  uint32_t qf_bytes;         // size of the fragment buffer (< 2^31)
+  uint32_t kv_layer_bytes;   // size of one layer's key (= value) cache (< 2^31)
   const int32_t* block_table;
   const PassRows* rows;
   int n_q, n_kv, hd;
-  int max_chunks;            // grid.x of the partial kernel
-  float* ws;                 // [n_kv][max_chunks][qg_max][hd+2]
+  int max_chunks;            // grid.x of the partial kernel: ceil(max_seq / kAttnChunk)
+  float* ws_o;               // [n_kv][max_chunks][qg_max][ceil(hd/16)*16] unnormalised P V
+  float2* ws_ml;             // [n_kv][max_chunks][qg_max] (max score, sum of exp)
   int qg_max;                // (n_q/n_kv) * kMaxRows
   uint16_t* Ap_out;          // packed attention output rows (K = n_q*hd) for the O projection
 };
-constexpr int kAttnChunk = 64;
-size_t attn_lds_bytes(int hd, int qg_max);
-constexpr size_t kAttnMaxLds = 160 * 1024;  // LDS per CU on gfx950
-// Raises the partial kernel's dynamic-LDS limit (needed above 64 KiB).
-hipError_t attn_reserve_lds(size_t bytes);
+constexpr int kAttnChunk = 32;  // keys per partial (one wave), two cache blocks
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- embedding --

@@ -97,10 +97,13 @@ struct spec_ctx {
   int device = 0;
   Model T, D;
   // shared buffers (sized for the larger of the two models)
-  float *x = nullptr, *q = nullptr, *ssq_a = nullptr, *ssq_b = nullptr;
+  float *x = nullptr, *ssq_a = nullptr, *ssq_b = nullptr;
+  uint16_t* qf = nullptr;  // attention query fragments
+  size_t qf_elems = 0;
   uint16_t *ap_x = nullptr, *ap_o = nullptr, *ap_a = nullptr;  // packed A operands
   float *logits = nullptr, *Tbuf = nullptr;
-  float* attn_ws = nullptr;
+  float* attn_wo = nullptr;   // attention chunk partials: value sums
+  float2* attn_ml = nullptr;  // attention chunk partials: (max, sum of exp)
   float2* lm_part = nullptr;
   uint64_t* ar_ws = nullptr;
   PassRows* rows = nullptr;
@@ -117,7 +120,8 @@ struct spec_ctx {
   int last_k = 0;
   bool graphs = true;
   std::map<std::vector<uint64_t>, GraphEntry> graph_cache;
-  // profiling: plain launches with hipEvent pairs around every gate/up GEMM
+  // profiling: plain launches; every gate/up GEMM carries an event pair that
+  // takes the kernel's own start and end timestamps
   bool profiling = false;
   std::vector<hipEvent_t> pool_draft, pool_verify;  // reusable events per call kind
   std::vector<hipEvent_t> prof_draft, prof_verify;  // pairs recorded by the last calls
@@ -308,8 +312,14 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   // paged KV cache: blocks of 16 tokens; the block table maps logical block i
   // to physical block n_blocks-1-i (any permutation works).
   m.n_blocks = (c->p.max_seq + kBlock - 1) / kBlock;
+  if (m.kv_layer_elems() * 2 >= (1ull << 31))
+    return fail(c, SPEC_ERR_ARG, "one layer's KV cache must stay below 2 GiB (lower max_seq)");
   HIPTRY(c, dalloc(&m.kcache, (size_t)L * m.kv_layer_elems()));
   HIPTRY(c, dalloc(&m.vcache, (size_t)L * m.kv_layer_elems()));
+  // zero-filled: attention reads whole blocks and relies on finite values in
+  // slots it gives zero weight
+  HIPTRY(c, hipMemsetAsync(m.kcache, 0, (size_t)L * m.kv_layer_elems() * 2, c->stream));
+  HIPTRY(c, hipMemsetAsync(m.vcache, 0, (size_t)L * m.kv_layer_elems() * 2, c->stream));
   std::vector<int32_t> bt(m.n_blocks);
   for (int i = 0; i < m.n_blocks; ++i) bt[i] = m.n_blocks - 1 - i;
   HIPTRY(c, dalloc(&m.block_table, (size_t)m.n_blocks));
@@ -368,7 +378,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profi
     // RMSNorm + QKV + RoPE + KV append
     GemmArgs a = gemm_base(c, m.qkv[l], c->ap_x);
     a.ssq = ssq_in; a.ssq_groups = ssq_groups; a.eps = m.eps;
-    a.out = c->q; a.ldo = m.qd;
+    a.qf = c->qf;
     a.q_dim = m.qd; a.kv_dim = m.kvd; a.head_dim = m.hd; a.n_kv = m.nkv;
     a.k_cache = m.kcache + (size_t)l * m.kv_layer_elems();
     a.v_cache = m.vcache + (size_t)l * m.kv_layer_elems();
@@ -377,9 +387,10 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profi
     if (e != hipSuccess) break;
     // causal attention over the paged cache -> packed A of the O projection
     AttnArgs at{};
-    at.q = c->q; at.k_cache = a.k_cache; at.v_cache = a.v_cache; at.block_table = m.block_table;
+    at.qf = c->qf; at.k_cache = a.k_cache; at.v_cache = a.v_cache; at.block_table = m.block_table;
+    at.qf_bytes = (uint32_t)(c->qf_elems * 2); at.kv_layer_bytes = (uint32_t)(m.kv_layer_elems() * 2);
     at.rows = c->rows; at.n_q = m.nq; at.n_kv = m.nkv; at.hd = m.hd;
-    at.max_chunks = c->attn_max_chunks; at.ws = c->attn_ws;
+    at.max_chunks = c->attn_max_chunks; at.ws_o = c->attn_wo; at.ws_ml = c->attn_ml;
     at.qg_max = (m.nq / m.nkv) * kMaxRows; at.Ap_out = c->ap_o;
     e = launch_attn(at, s);
     if (e != hipSuccess) break;
@@ -398,9 +409,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profi
       hipEvent_t e0 = nullptr, e1 = nullptr;
       e = next_event(c, &e0);
       if (e == hipSuccess) e = next_event(c, &e1);
-      if (e == hipSuccess) e = hipEventRecord(e0, s);
-      if (e == hipSuccess) e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
-      if (e == hipSuccess) e = hipEventRecord(e1, s);
+      if (e == hipSuccess) e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s, e0, e1);
       if (e == hipSuccess) {
         c->rec_events->push_back(e0);
         c->rec_events->push_back(e1);
@@ -551,8 +560,8 @@ void destroy_ctx(spec_ctx* c) {
   for (hipEvent_t ev : c->pool_verify) (void)hipEventDestroy(ev);
   free_model(c->D);
   free_model(c->T);
-  void* bufs[] = {c->x, c->q, c->ssq_a, c->ssq_b, c->ap_x, c->ap_o, c->ap_a, c->logits, c->Tbuf,
-                  c->attn_ws, c->lm_part, c->ar_ws, c->rows, c->st, c->hist};
+  void* bufs[] = {c->x, c->qf, c->ssq_a, c->ssq_b, c->ap_x, c->ap_o, c->ap_a, c->logits, c->Tbuf,
+                  c->attn_wo, c->attn_ml, c->lm_part, c->ar_ws, c->rows, c->st, c->hist};
   for (void* b : bufs) (void)hipFree(b);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
@@ -620,7 +629,7 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
 
   const Model* ms[2] = {&c->T, &c->D};
   int dmax = 0, qmax = 0, fmax = 0, V = c->T.V, lm_groups = 0, ssq_groups = 0;
-  size_t attn_ws = 0;
+  size_t attn_wo = 0, attn_ml = 0, qf_elems = 0;
   c->attn_max_chunks = (p->max_seq + kAttnChunk - 1) / kAttnChunk;
   for (const Model* m : ms) {
     dmax = std::max(dmax, m->d);
@@ -639,17 +648,20 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
     }
     if (!ok) return bail(fail(c, SPEC_ERR_ARG, "d_model too large for the RMSNorm partial fold"));
     const int qg = (m->nq / m->nkv) * kMaxRows;
-    attn_ws = std::max(attn_ws, (size_t)m->nkv * c->attn_max_chunks * qg * (m->hd + 2));
-    const size_t lds_need = attn_lds_bytes(m->hd, qg);
-    if (lds_need > kAttnMaxLds)
-      return bail(fail(c, SPEC_ERR_ARG, "attention tile exceeds the LDS of a CU"));
-    if (lds_need > 64 * 1024) TRYH(attn_reserve_lds(lds_need));
+    attn_wo = std::max(attn_wo, (size_t)m->nkv * c->attn_max_chunks * qg * ((m->hd + 15) / 16 * 16));
+    attn_ml = std::max(attn_ml, (size_t)m->nkv * c->attn_max_chunks * qg);
+    qf_elems = std::max(qf_elems, (size_t)m->nkv * ((m->nq / m->nkv + 1) / 2) *
+                                      ((m->hd + 31) / 32) * 2 * 512);
   }
   ar_choose_chunks(1, V, &c->ar_chunk, &c->ar_nchunks);
   c->sm_chunk = 4096;
   c->sm_nchunks = (V + c->sm_chunk - 1) / c->sm_chunk;
   TRYH(dalloc(&c->x, (size_t)kMaxRows * dmax));
-  TRYH(dalloc(&c->q, (size_t)kMaxRows * qmax));
+  if (qf_elems * 2 >= (1ull << 31))
+    return bail(fail(c, SPEC_ERR_ARG, "attention query fragments exceed 2 GiB"));
+  c->qf_elems = qf_elems;
+  TRYH(dalloc(&c->qf, qf_elems));
+  TRYH(hipMemsetAsync(c->qf, 0, qf_elems * 2, c->stream));
   TRYH(dalloc(&c->ssq_a, (size_t)kMaxRows * ssq_groups));
   TRYH(dalloc(&c->ssq_b, (size_t)kMaxRows * ssq_groups));
   // packed A operands: 16 bf16 rows (8 hi + 8 lo) per column
@@ -658,7 +670,8 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   TRYH(dalloc(&c->ap_a, (size_t)16 * fmax));
   TRYH(dalloc(&c->logits, (size_t)kMaxRows * V));
   TRYH(dalloc(&c->Tbuf, (size_t)kMaxRows * V));
-  TRYH(dalloc(&c->attn_ws, attn_ws));
+  TRYH(dalloc(&c->attn_wo, attn_wo));
+  TRYH(dalloc(&c->attn_ml, attn_ml));
   TRYH(dalloc(&c->lm_part, (size_t)lm_groups * kMaxRows));
   TRYH(dalloc(&c->ar_ws, (size_t)c->ar_nchunks * ar_ws_words(SPEC_K_MAX)));
   TRYH(dalloc(&c->rows, 1));
