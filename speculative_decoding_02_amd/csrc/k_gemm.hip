@@ -66,17 +66,52 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   // hides behind the weight stream, and folded in a fixed order after it.
   constexpr int P = W * 64 / kMaxRows;
   constexpr int kMaxSsq = kGemmMaxSsqPerThread;  // ssq_groups <= P * kMaxSsq
+  // The loads are unconditional (clamped indices) so they are issued without
+  // waiting for anything; entries outside the pass are dropped afterwards.
   float ssq_part = 0.0f;
   if (a.ssq != nullptr) {
     const int m = tid % kMaxRows, p0 = tid / kMaxRows;
+    const int mr = a.last_row_only ? row_base : m;  // row of the producer's partials
     float v[kMaxSsq];
 #pragma unroll
     for (int i = 0; i < kMaxSsq; ++i) {
       const int q = p0 + i * P;
-      v[i] = (q < a.ssq_groups && m < n_rows) ? a.ssq[q * kMaxRows + row_base + m] : 0.0f;
+      v[i] = a.ssq[(q < a.ssq_groups ? q : 0) * kMaxRows + (mr & (kMaxRows - 1))];
     }
 #pragma unroll
-    for (int i = 0; i < kMaxSsq; ++i) ssq_part += v[i];
+    for (int i = 0; i < kMaxSsq; ++i)
+      ssq_part += (p0 + i * P < a.ssq_groups && m < n_rows) ? v[i] : 0.0f;
+  }
+
+  // Epilogue operands that do not depend on the product, fetched now so their
+  // latency hides behind the weight stream.
+  const int col0 = g * YW;
+  constexpr int C8 = YW / 8;
+  float4 pre_x0 = make_float4(0.f, 0.f, 0.f, 0.f), pre_x1 = pre_x0;
+  uint4 pre_g = make_uint4(0, 0, 0, 0);
+  if constexpr (EPI == EPI_RESID) {
+    if (tid < kMaxRows * C8) {  // resid rows exist for all kMaxRows rows
+      const int m = tid / C8, k0 = col0 + (tid % C8) * 8;
+      const float* px = a.resid + (size_t)m * a.ldr + k0;
+      pre_x0 = *(const float4*)px;
+      pre_x1 = *(const float4*)(px + 4);
+      pre_g = *(const uint4*)(a.gain_next + k0);
+    }
+  }
+  float2 pre_rope = make_float2(1.f, 0.f);
+  int pre_blk = 0;
+  if constexpr (EPI == EPI_QKV) {
+    const int m = tid / YW, c = tid % YW;
+    const int pos = a.rows->pos0 + m;
+    const int b = g * NB + c / 16, w = c % 16;
+    const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16, half_hd = a.head_dim / 2;
+    if (m < kMaxRows && pos < a.max_seq) {
+      pre_blk = a.block_table[pos / kBlock];
+      if (b < q_blocks + k_blocks) {
+        const int bl = b < q_blocks ? b : b - q_blocks;
+        pre_rope = a.rope[(size_t)pos * half_hd + (bl * 8 + (w & 7)) % half_hd];
+      }
+    }
   }
 
   // ---- main loop: this wave's share of K ---------------------------------
@@ -153,7 +188,6 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   __syncthreads();
 
   // ---- epilogues on the [8][YW] tile ---------------------------------------
-  const int col0 = g * YW;
   if constexpr (EPI == EPI_STORE) {
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
@@ -177,17 +211,21 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     }
   } else if constexpr (EPI == EPI_RESID) {
     // x += y; next GEMM's packed A = x * gain_next; sums of squares of x
-    constexpr int C8 = YW / 8;
-    for (int idx = tid; idx < kMaxRows * C8; idx += W * 64) {
-      const int m = idx / C8, c8 = idx % C8;
+    static_assert(kMaxRows * C8 <= W * 64, "one epilogue item per thread");
+    if (tid < kMaxRows * C8) {
+      const int m = tid / C8, c8 = tid % C8;
       float sq = 0.0f;
       if (m < n_rows) {
         const int k0 = col0 + c8 * 8;
         float* px = a.resid + (size_t)m * a.ldr + k0;
-        const float4 x0 = *(const float4*)px, x1 = *(const float4*)(px + 4);
+        const float4 x0 = pre_x0, x1 = pre_x1;
         float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         float gn[8], xg[8];
-        load_gain8(a.gain_next, k0, gn);
+        {
+          const uint32_t gw[4] = {pre_g.x, pre_g.y, pre_g.z, pre_g.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gn[e] = bf16_to_f32((uint16_t)(gw[e >> 1] >> ((e & 1) * 16)));
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           x[e] += s_y[m * YW + c8 * 8 + e];
@@ -238,7 +276,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
         const int pair = bl * 8 + (w & 7), hf = w >> 3;
         const int head = pair / half_hd, jj = pair % half_hd;
         const float other = s_y[m * YW + (c ^ 8)];
-        const float2 r = a.rope[(size_t)pos * half_hd + jj];  // (cos, sin) of pos * theta^(-2jj/hd)
+        // (cos, sin) of pos * theta^(-2jj/hd); this thread's first item was prefetched
+        const float2 r = idx == tid ? pre_rope : a.rope[(size_t)pos * half_hd + jj];
         const float lo = hf ? other : mine;
         const float hi = hf ? mine : other;
         const float val = hf ? hi * r.x + lo * r.y : lo * r.x - hi * r.y;
@@ -250,7 +289,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
           a.qf[qfrag_index(head / G, G, n_es, qi, 0, dim)] = hb;
           a.qf[qfrag_index(head / G, G, n_es, qi, 1, dim)] = f32_to_bf16_rne(val - bf16_to_f32(hb));
         } else {
-          const int blk = a.block_table[pos / kBlock];
+          const int blk = idx == tid ? pre_blk : a.block_table[pos / kBlock];
           const uint16_t hb = f32_to_bf16_rne(val);
           a.k_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 0, dim)] = hb;
           a.k_cache[kv_index(blk, a.n_kv, head, pos % kBlock, a.head_dim, 1, dim)] =
@@ -259,7 +298,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
       } else {
         const int f0 = (b - q_blocks - k_blocks) * 16 + w;
         const int head = f0 / a.head_dim, dim = f0 % a.head_dim;
-        const int blk = a.block_table[pos / kBlock];
+        const int blk = idx == tid ? pre_blk : a.block_table[pos / kBlock];
         const uint16_t hb = f32_to_bf16_rne(mine);
         a.v_cache[vt_index(blk, a.n_kv, head, 0, a.head_dim, dim, pos % kBlock)] = hb;
         a.v_cache[vt_index(blk, a.n_kv, head, 1, a.head_dim, dim, pos % kBlock)] =
