@@ -12,8 +12,9 @@
 //    is one contiguous span: [group][k-block][NB][64 lanes][8 bf16].
 //  * A arrives already packed by its producer (see apack_index): bf16 high
 //    and low halves of up to 8 fp32 rows in one 16-row MFMA tile.  It is
-//    small and shared by every workgroup, so it is read from L2; rows the
-//    pass does not use are zeroed in registers.
+//    small and shared by every workgroup, so it is read from L2; lanes of
+//    rows the pass does not use are given an out-of-range buffer offset,
+//    which reads as zero without a memory access.
 //  * A workgroup owns NB 16-column blocks for the whole of K; its waves split
 //    K and are reduced through LDS in wave order (deterministic, and no
 //    workgroup ever waits for another).
@@ -44,10 +45,10 @@ template <int NB, int W, int EPI>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   constexpr int YW = NB * 16;            // columns owned by the workgroup
   constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : 4);  // k-blocks per batch of loads
-  __shared__ float s_red[W * NB * 128];
+  __shared__ float s_red[W * NB * 256];
   __shared__ float s_y[kMaxRows * YW];
   __shared__ float s_scale[kMaxRows];
-  __shared__ float s_ssq[W * 64];
+  __shared__ float s_ssq[W * kMaxRows];
   __shared__ float s_part[kMaxRows][YW / 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -118,20 +119,27 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   const int kb0 = (a.Kb * wave) / W, kb1 = (a.Kb * (wave + 1)) / W;
   const int am = lane & 7;  // activation row of this lane (hi rows 0-7, lo rows 8-15)
   const bool aload = a.last_row_only ? (am == row_base) : (am < n_rows);
-  const uint4* ap = (const uint4*)a.Ap + lane;
+  // A through a range-checked buffer resource: lanes of rows the pass does not
+  // use read at an out-of-range offset, which returns zero without a fetch.
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Ap), 0, a.Kb * 1024, 0x00020000);
+  const uint32_t a_off = aload ? (uint32_t)lane * 16 : 0x80000000u;
   const uint4* wp = (const uint4*)a.Wp + (size_t)g * a.Kb * NB * 64 + lane;
   floatx4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
   // Batches of k-blocks: all loads of a batch are issued before its first
   // MFMA (the scheduling barrier keeps the compiler from interleaving them),
-  // so each wave keeps UB*NB KiB of weights in flight.  A is loaded by every
-  // lane (always in bounds) and rows the pass does not use are zeroed after.
+  // so each wave keeps UB*NB KiB of weights in flight.
   auto batch = [&](auto ub_tag, int kb) {
     constexpr int UB = decltype(ub_tag)::value;
     uint4 av[UB], wv[UB][NB];
 #pragma unroll
-    for (int u = 0; u < UB; ++u) av[u] = ap[(size_t)(kb + u) * 64];
+    for (int u = 0; u < UB; ++u) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          rA, (int)(aload ? a_off + (uint32_t)(kb + u) * 1024 : a_off), 0, 0);
+      av[u] = make_uint4(v.x, v.y, v.z, v.w);
+    }
 #pragma unroll
     for (int u = 0; u < UB; ++u)
 #pragma unroll
@@ -139,10 +147,9 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
-      const uint4 a4 = aload ? av[u] : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a4), as_bf16x8(wv[u][j]),
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(wv[u][j]),
                                                          acc[j], 0, 0, 0);
     }
   };
@@ -155,21 +162,22 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); rows
   // 8-15 (lanes 32-63) are the low-part products of rows 0-7.
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    float4 v;  // shuffles run with every lane active
-    v.x = acc[j][0] + __shfl_down(acc[j][0], 32);
-    v.y = acc[j][1] + __shfl_down(acc[j][1], 32);
-    v.z = acc[j][2] + __shfl_down(acc[j][2], 32);
-    v.w = acc[j][3] + __shfl_down(acc[j][3], 32);
-    if (lane < 32) *(float4*)&s_red[((wave * NB + j) * 32 + lane) * 4] = v;
-  }
-  s_ssq[tid] = ssq_part;
+  for (int j = 0; j < NB; ++j)
+    *(float4*)&s_red[((wave * NB + j) * 64 + lane) * 4] =
+        make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  // sums of squares: lanes of one wave with the same row (lane % 8) first
+  float sq = ssq_part;
+  sq += __shfl_xor(sq, 8);
+  sq += __shfl_xor(sq, 16);
+  sq += __shfl_xor(sq, 32);
+  if (lane < kMaxRows) s_ssq[wave * kMaxRows + lane] = sq;
   __syncthreads();
   if (tid < kMaxRows) {
     float sc = 1.0f;
     if (a.ssq != nullptr && tid < n_rows) {
       float ss = 0.0f;
-      for (int p = 0; p < P; ++p) ss += s_ssq[p * kMaxRows + tid];
+#pragma unroll
+      for (int w = 0; w < W; ++w) ss += s_ssq[w * kMaxRows + tid];
       sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     }
     s_scale[tid] = sc;
@@ -179,7 +187,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     const int j = idx >> 7, ln = (idx >> 2) & 31, r = idx & 3;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) v += s_red[((w * NB + j) * 32 + ln) * 4 + r];
+    for (int w = 0; w < W; ++w)  // high-part rows (lanes 0-31), then low-part rows (lanes 32-63)
+      v += s_red[((w * NB + j) * 64 + ln) * 4 + r] + s_red[((w * NB + j) * 64 + ln + 32) * 4 + r];
     const int mm = 4 * (ln >> 4) + r;  // MFMA row = activation row
     // with last_row_only the one used row (row_base) becomes output row 0
     const int m = a.last_row_only ? (mm == row_base ? 0 : -1) : mm;

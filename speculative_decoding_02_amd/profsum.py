@@ -4,11 +4,12 @@ Reads what `rocprofv3 --kernel-trace --stats` or `rocprofv3 --pmc ...` wrote
 (CSV files, or the SQLite database of the default output format) and prints
 short text summaries:
 
-  trace DIR [--rounds R] [--kernel SUBSTR]
+  trace DIR [--rounds R] [--skip-last S] [--kernel SUBSTR]
       per-kernel totals over the whole run; then the steady state: the
       dispatches that follow the first commit kernel (i.e. the decoding rounds,
       without weight generation, packing or prefill), per kernel and per round
-      (span, busy time, gaps between kernels over the last R rounds).
+      (span, busy time, gaps between kernels over R rounds that end S rounds
+      before the last one, e.g. to leave out rounds run without graphs).
   pmc FETCH_DIR WRITE_DIR --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes N
       HBM traffic per launch of one kernel in the steady state from the
       FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch), each scaled by the
@@ -95,7 +96,7 @@ def short(name: str, n: int = 70) -> str:
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def trace_summary(d: str, rounds: int, kernel: str | None) -> str:
+def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0) -> str:
     rows = load_dispatches(d)
     lines = []
     tot = collections.defaultdict(lambda: [0, 0.0])
@@ -121,15 +122,16 @@ def trace_summary(d: str, rounds: int, kernel: str | None) -> str:
     lines.append(f"  {'calls':>7} {'total us':>12} {'avg us':>9}  kernel")
     for n, (c, t) in sorted(agg.items(), key=lambda x: -x[1][1])[:16]:
         lines.append(f"  {c:7d} {t:12.1f} {t / c:9.2f}  {short(n)}")
-    R = min(rounds, len(marks) - 1)
+    end = len(marks) - 1 - skip_last
+    R = min(rounds, end)
     if R > 0:
-        sel = rows[marks[-R - 1] + 1: marks[-1] + 1]
+        sel = rows[marks[end - R] + 1: marks[end] + 1]
         span = (sel[-1][3] - sel[0][2]) / 1e3
         busy = sum((e - s) / 1e3 for _, _, s, e, _ in sel)
         lines.append("")
-        lines.append(f"last {R} rounds: span {span / R:.1f} us/round, kernel busy {busy / R:.1f} "
-                     f"us/round, gaps {(span - busy) / R:.1f} us/round, {len(sel) / R:.0f} "
-                     f"kernels/round")
+        lines.append(f"{R} rounds ending {skip_last} before the last: span {span / R:.1f} us/round, "
+                     f"kernel busy {busy / R:.1f} us/round, gaps {(span - busy) / R:.1f} us/round, "
+                     f"{len(sel) / R:.0f} kernels/round")
     if kernel:
         ks = [(e - s) / 1e3 for _, n, s, e, _ in steady if kernel in n]
         if ks:
@@ -178,6 +180,7 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--rounds", type=int, default=10)
     t.add_argument("--kernel", default=None)
+    t.add_argument("--skip-last", type=int, default=0)
     p = sub.add_parser("pmc")
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
@@ -186,7 +189,7 @@ def main(argv=None):
     p.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.dir, a.rounds, a.kernel))
+        print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last))
     else:
         print(pmc_summary(a.fetch_dir, a.write_dir, a.kernel, a.copy_kernel, a.copy_bytes))
 
