@@ -267,10 +267,8 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
     prompt (prefill untimed).  Attention over an 8- instead of 1024-token
     context is ~4% of the oracle's per-row work, so this bounds the sample
     without changing what a round computes."""
-    import numpy as np
     import oracle
     import synth
-    import torch
     t0 = time.time()
     tb = synth.torch_to_bits(tw)
     db = synth.torch_to_bits(dw)
@@ -280,7 +278,6 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
     prompt = synth.prompt(tcfg.vocab, 8, seed=7)
     # untimed prefill, then timed rounds: run spec_generate twice (n rounds
     # and 0 rounds) and subtract, so the prefill is excluded.
-    n_new = 64
     t0 = time.perf_counter()
     oracle.spec_generate(T, Dm, prompt, 0, K, greedy=args.greedy, seed=synth.SEED_PHILOX)
     t_pre = time.perf_counter() - t0
@@ -302,6 +299,7 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
 def _rounds(oracle, T, Dm, prompt, K, args):
     # at least one token per round: asking for cpu_tokens tokens bounds the
     # rounds by cpu_tokens; the stats report the rounds actually run.
+    import synth
     return oracle.spec_generate(T, Dm, prompt, args.cpu_tokens, K, greedy=args.greedy,
                                 seed=synth.SEED_PHILOX)
 
