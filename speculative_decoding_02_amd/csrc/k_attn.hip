@@ -71,30 +71,26 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
   const int c = blockIdx.x, h = blockIdx.y;
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
-  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
-  const int n_keys = pos0 + n_rows;
-  const int key0 = c * kAttnChunk;
-  if (n_rows <= 0 || key0 >= n_keys) return;
-  const int QG = G * n_rows, n_qt = (QG + 15) / 16, n_qt_max = (G + 1) / 2;
+  const int n_qt_max = (G + 1) / 2;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
-  const float scale = 1.0f / sqrtf((float)hd);
-  float* wso = a.ws_o + ((size_t)h * a.max_chunks + c) * a.qg_max * E16;
-  float2* wsml = a.ws_ml + ((size_t)h * a.max_chunks + c) * a.qg_max;
+  const int key0 = c * kAttnChunk;
 
   // Buffer loads: an offset at or past the resource's size reads as zero,
-  // which masks padded dims, absent keys and unused query columns without
-  // branches, so every load of the wave is in flight at once.
+  // which masks padded dims and absent tiles without branches, so every load
+  // of the wave is in flight at once.
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.kv_layer_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.kv_layer_bytes);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf, a.qf_bytes);
+  // Query fragments.  Columns beyond this pass's query vectors hold finite
+  // values from earlier passes; their scores are masked below.
   uint4 qf[QTG][NES][2];
   auto load_q = [&](int qt0) {
 #pragma unroll
     for (int t = 0; t < QTG; ++t) {
-      const int qt = qt0 + t, qi = 16 * qt + l16;
+      const int qt = qt0 + t;
 #pragma unroll
       for (int es = 0; es < NES; ++es) {
-        const bool ok = qt < n_qt && qi < QG && 32 * es + 8 * grp < hd;
+        const bool ok = qt < n_qt_max && 32 * es + 8 * grp < hd;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const uint32_t off =
@@ -104,11 +100,21 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
       }
     }
   };
+  // Issued before the pass descriptor is read: the first query tiles and
+  // the chunk's two cache blocks (the second clamped to the table).
   load_q(0);
-
-  // cache blocks of the chunk; the second only where it holds keys
   const int blk0 = a.block_table[2 * c];
-  const int blk1 = key0 + kBlock < n_keys ? a.block_table[2 * c + 1] : blk0;
+  const int blk1_any = a.block_table[min(2 * c + 1, a.n_blocks - 1)];
+
+  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int n_keys = pos0 + n_rows;
+  if (n_rows <= 0 || key0 >= n_keys) return;
+  const int QG = G * n_rows, n_qt = (QG + 15) / 16;
+  const int blk1 = key0 + kBlock < n_keys ? blk1_any : blk0;
+  const float scale = 1.0f / sqrtf((float)hd);
+  float* wso = a.ws_o + ((size_t)h * a.max_chunks + c) * a.qg_max * E16;
+  float2* wsml = a.ws_ml + ((size_t)h * a.max_chunks + c) * a.qg_max;
+
   uint4 kf[2][NES][2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -230,11 +236,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __shared__ float s_m[4];
   const int qi = blockIdx.x, h = blockIdx.y;
   const int hd = a.hd, G = a.n_q / a.n_kv;
-  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
-  const int QG = G * n_rows;
-  if (n_rows <= 0 || qi >= QG) return;
-  const int n_keys = pos0 + n_rows;
-  const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
   const int E16 = (hd + 15) / 16 * 16;
   const int n8 = hd / 8, ncg = 256 / n8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -244,22 +245,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const float* wo = a.ws_o + ((size_t)h * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
   const bool worker = cg < ncg;
 
+  float4 v0[kMergeBatch], v1[kMergeBatch];
+  float2 mv[kMergeBatch];
+  auto load = [&](int c0) {  // chunk indices clamped to the workspace
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const size_t cl = (size_t)min(c0 + u * ncg, a.max_chunks - 1);
+      mv[u] = ml[cl * cs_ml];
+      v0[u] = *(const float4*)(wo + cl * cs_o);
+      v1[u] = *(const float4*)(wo + cl * cs_o + 4);
+    }
+  };
+  // the first batch is issued before the pass descriptor is read
+  load(worker ? cg : 0);
+
+  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int QG = G * n_rows;
+  if (n_rows <= 0 || qi >= QG) return;
+  const int n_keys = pos0 + n_rows;
+  const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
+
   MergeState st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
   for (int c0 = worker ? cg : n_active; c0 < n_active; c0 += kMergeBatch * ncg) {
-    float4 v0[kMergeBatch], v1[kMergeBatch];
-    float2 mv[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int cc = c0 + u * ncg;
-      const size_t cl = cc < n_active ? (size_t)cc : 0;
-      mv[u] = ml[cl * cs_ml];
-      v0[u] = *(const float4*)(wo + cl * cs_o);
-      v1[u] = *(const float4*)(wo + cl * cs_o + 4);
-    }
+    if (c0 != cg) load(c0);
     __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before any use
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
@@ -300,7 +312,8 @@ static void launch_partial(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv), dim3(64), 0, s, a);
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {
+  if (n_rows < 1 || n_rows > kMaxRows) return hipErrorInvalidValue;
   switch ((a.hd + 31) / 32) {
     case 1: launch_partial<1>(a, s); break;
     case 2: launch_partial<2>(a, s); break;
@@ -314,7 +327,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.qg_max, a.n_kv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_q / a.n_kv) * n_rows, a.n_kv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -93,32 +93,57 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
 // T_i = softmax(logits_i) at temperature 1 ([en] Floor 5: the target's
 // wheel).  The LM-head GEMM left per-workgroup (max, sum exp) partials; each
 // block folds them in a fixed order, then normalises its chunk of the row.
-__global__ __launch_bounds__(256) void softmax_kernel(SoftmaxArgs a) {
+// The chunk's logits and this thread's partials are loaded together at the
+// start, so the block makes one round trip to memory.
+constexpr int kSoftmaxThreads = 256;
+constexpr int kSoftmaxVec = 4;          // float4 per thread per chunk: chunk = 4096
+constexpr int kSoftmaxMaxPart = 32;     // partials per thread: G <= 8192
+
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_kernel(SoftmaxArgs a) {
   __shared__ float s_m[16], s_s[16];
-  const int r = blockIdx.y, c = blockIdx.x;
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int lo = c * a.chunk;
+  const float* lrow = a.logits + (size_t)r * a.V;
+  float4 lv[kSoftmaxVec];
+#pragma unroll
+  for (int j = 0; j < kSoftmaxVec; ++j) {
+    const int v = lo + (j * kSoftmaxThreads + tid) * 4;
+    lv[j] = v < a.V ? *(const float4*)(lrow + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float2 pv[kSoftmaxMaxPart];
+#pragma unroll
+  for (int i = 0; i < kSoftmaxMaxPart; ++i) {
+    const int g = i * kSoftmaxThreads + tid;
+    pv[i] = g < a.G ? a.part[g * kMaxRows + r] : make_float2(-INFINITY, 0.0f);
+  }
   int n_rows = a.rows->n_rows;
   if (a.last_row_only) n_rows = n_rows > 0 ? 1 : 0;
   if (r >= n_rows) return;
   float M = -INFINITY;
-#pragma unroll 8
-  for (int g = threadIdx.x; g < a.G; g += blockDim.x) M = fmaxf(M, a.part[g * kMaxRows + r].x);
+#pragma unroll
+  for (int i = 0; i < kSoftmaxMaxPart; ++i) M = fmaxf(M, pv[i].x);
   M = block_reduce(M, s_m, [](float x, float y) { return fmaxf(x, y); });
   float S = 0.0f;
-#pragma unroll 8
-  for (int g = threadIdx.x; g < a.G; g += blockDim.x) {
-    const float2 p = a.part[g * kMaxRows + r];
-    if (p.x != -INFINITY) S += p.y * expf(p.x - M);
-  }
+#pragma unroll
+  for (int i = 0; i < kSoftmaxMaxPart; ++i)
+    if (pv[i].x != -INFINITY) S += pv[i].y * expf(pv[i].x - M);
   S = block_reduce(S, s_s, [](float x, float y) { return x + y; });
   const float inv = 1.0f / S;
-  const float* l = a.logits + (size_t)r * a.V;
-  float* o = a.out + (size_t)r * a.V;
-  const int lo = c * a.chunk, hi = min(a.V, lo + a.chunk);
-  for (int v = lo + threadIdx.x; v < hi; v += blockDim.x) o[v] = expf(l[v] - M) * inv;
+  float* orow = a.out + (size_t)r * a.V;
+#pragma unroll
+  for (int j = 0; j < kSoftmaxVec; ++j) {
+    const int v = lo + (j * kSoftmaxThreads + tid) * 4;
+    if (v < a.V)
+      *(float4*)(orow + v) = make_float4(expf(lv[j].x - M) * inv, expf(lv[j].y - M) * inv,
+                                         expf(lv[j].z - M) * inv, expf(lv[j].w - M) * inv);
+  }
 }
 
-hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, hipStream_t s) {
-  hipLaunchKernelGGL(softmax_kernel, dim3(n_chunks, kMaxRows), dim3(256), 0, s, a);
+hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, int n_rows, hipStream_t s) {
+  if (a.chunk != kSoftmaxThreads * kSoftmaxVec * 4 || a.G > kSoftmaxThreads * kSoftmaxMaxPart ||
+      a.V % 4 != 0 || n_rows < 1 || n_rows > kMaxRows)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(softmax_kernel, dim3(n_chunks, n_rows), dim3(kSoftmaxThreads), 0, s, a);
   return hipGetLastError();
 }
 

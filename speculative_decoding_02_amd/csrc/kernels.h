@@ -82,13 +82,16 @@ struct AttnArgs {
   const PassRows* rows;
   int n_q, n_kv, hd;
   int max_chunks;            // grid.x of the partial kernel: ceil(max_seq / kAttnChunk)
+  int n_blocks;              // entries of block_table: ceil(max_seq / kBlock)
   float* ws_o;               // [n_kv][max_chunks][qg_max][ceil(hd/16)*16] unnormalised P V
   float2* ws_ml;             // [n_kv][max_chunks][qg_max] (max score, sum of exp)
   int qg_max;                // (n_q/n_kv) * kMaxRows
   uint16_t* Ap_out;          // packed attention output rows (K = n_q*hd) for the O projection
 };
 constexpr int kAttnChunk = 32;  // keys per partial (one wave), two cache blocks
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// n_rows: rows the pass can have (bounds the merge grid); rows beyond
+// rows->n_rows exit.
+hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s);
 
 // ------------------------------------------------------------- embedding --
 enum EmbedMode : int {
@@ -122,7 +125,8 @@ struct SoftmaxArgs {
   float* out;            // [rows][V]
   int chunk;
 };
-hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, hipStream_t s);
+// n_rows: rows the pass can have (grid.y); rows beyond rows->n_rows exit.
+hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, int n_rows, hipStream_t s);
 
 // -------------------------------------------------------- accept/reject --
 struct ArArgs {

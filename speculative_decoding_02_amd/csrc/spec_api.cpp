@@ -43,16 +43,18 @@ struct GemmPlan {
   int n_groups = 0, Kb = 0;
 };
 
-// Shapes measured on MI355X (standalone sweep over nb in {1,2,4}, waves in
-// {4,8}): two blocks per workgroup once there are enough columns to keep
-// >= ~400 workgroups, eight waves unless each wave would stream over 64 KiB.
+// Shapes measured on MI355X (graph-replayed sweep over nb in {1,2,4} and
+// waves in {4,8,16}): two blocks per workgroup once there are enough columns
+// to keep >= ~400 workgroups; four waves (more workgroups resident per CU),
+// except for narrow matrices with a long K, where only eight waves per
+// workgroup keep enough loads in flight.
 GemmPlan plan_gemm(int n_cols, int nb_min, int K) {
   GemmPlan p;
   const int n_blocks = n_cols / 16;
   p.shape.nb = std::max(nb_min, (n_blocks >= 768 && n_blocks % 2 == 0) ? 2 : 1);
   p.Kb = K / 32;
   p.n_groups = n_blocks / p.shape.nb;
-  p.shape.waves = p.Kb * p.shape.nb / 8 > 64 ? 4 : 8;
+  p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
   return p;
 }
 
@@ -369,7 +371,7 @@ hipError_t next_event(spec_ctx* c, hipEvent_t* ev) {
 // -> gate/up (norm scale, SiLU*up) -> down (+residual).  The sums of squares
 // for each RMSNorm alternate between two buffers so a producer never writes
 // the partials its own consumer-to-be is still to read.
-hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profile) {
+hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows, bool profile) {
   hipError_t e = hipSuccess;
   int ssq_groups = m.d / 64;  // produced by the embedding
   float* ssq_in = c->ssq_a;
@@ -390,9 +392,10 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, bool profi
     at.qf = c->qf; at.k_cache = a.k_cache; at.v_cache = a.v_cache; at.block_table = m.block_table;
     at.qf_bytes = (uint32_t)(c->qf_elems * 2); at.kv_layer_bytes = (uint32_t)(m.kv_layer_elems() * 2);
     at.rows = c->rows; at.n_q = m.nq; at.n_kv = m.nkv; at.hd = m.hd;
-    at.max_chunks = c->attn_max_chunks; at.ws_o = c->attn_wo; at.ws_ml = c->attn_ml;
+    at.max_chunks = c->attn_max_chunks; at.n_blocks = m.n_blocks;
+    at.ws_o = c->attn_wo; at.ws_ml = c->attn_ml;
     at.qg_max = (m.nq / m.nkv) * kMaxRows; at.Ap_out = c->ap_o;
-    e = launch_attn(at, s);
+    e = launch_attn(at, n_rows, s);
     if (e != hipSuccess) break;
     // O projection + residual; packs x * ffn_norm for gate/up
     GemmArgs b = gemm_base(c, m.o[l], c->ap_o);
@@ -435,7 +438,7 @@ int final_ssq_groups(const Model& m) { return m.dn[m.L - 1].plan.n_groups; }
 float* final_ssq(spec_ctx* c, const Model&) { return c->ssq_a; }
 
 // final norm + LM head (+ logits partials) + softmax into `dst`
-hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only,
+hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only, int n_rows,
                         float* logits_dst, float* dst) {
   GemmArgs a = gemm_base(c, m.lm, c->ap_x);
   a.ssq = final_ssq(c, m); a.ssq_groups = final_ssq_groups(m); a.eps = m.eps;
@@ -446,7 +449,7 @@ hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row
   SoftmaxArgs sm{};
   sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.n_groups; sm.V = m.V;
   sm.rows = c->rows; sm.last_row_only = last_row_only; sm.out = dst; sm.chunk = c->sm_chunk;
-  return launch_softmax(sm, c->sm_nchunks, s);
+  return launch_softmax(sm, c->sm_nchunks, last_row_only ? 1 : n_rows, s);
 }
 
 hipError_t enqueue_embed(spec_ctx* c, const Model& m, hipStream_t s, int mode, int n_rows, int pos0,
@@ -465,9 +468,10 @@ hipError_t enqueue_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32
   hipError_t e = hipSuccess;
   for (int st = 0; st < K && e == hipSuccess; ++st) {
     e = enqueue_embed(c, m, s, st == 0 ? EMB_DRAFT0 : EMB_DRAFTS, 0, 0, st, d);
-    if (e == hipSuccess) e = enqueue_layers(c, m, s, c->profiling);
+    // step 0 may carry catch-up rows; later steps have one row
+    if (e == hipSuccess) e = enqueue_layers(c, m, s, st == 0 ? kMaxRows : 1, c->profiling);
     float* drow = Dp + (size_t)st * m.V;
-    if (e == hipSuccess) e = enqueue_head(c, m, s, 1, c->logits, drow);
+    if (e == hipSuccess) e = enqueue_head(c, m, s, 1, 1, c->logits, drow);
     if (e == hipSuccess) {
       ArArgs ar{};
       ar.T = drow; ar.D = nullptr; ar.d = d; ar.B = 1; ar.K = 0; ar.V = m.V;
@@ -487,8 +491,8 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
   float* Tb = Tdst ? Tdst : c->Tbuf;
   float* Lb = Ldst ? Ldst : c->logits;
   hipError_t e = enqueue_embed(c, m, s, EMB_VERIFY, K + 1, 0, 0, d);
-  if (e == hipSuccess) e = enqueue_layers(c, m, s, c->profiling);
-  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, Lb, Tb);
+  if (e == hipSuccess) e = enqueue_layers(c, m, s, K + 1, c->profiling);
+  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, K + 1, Lb, Tb);
   if (e == hipSuccess) {
     ArArgs ar{};
     ar.T = Tb; ar.D = Dp; ar.d = d; ar.B = 1; ar.K = K; ar.V = m.V;
@@ -545,7 +549,7 @@ int prefill(spec_ctx* c, const Model& m, int pos0, int n) {
   for (int p = pos0; p < pos0 + n; p += kMaxRows) {
     const int cnt = std::min(kMaxRows, pos0 + n - p);
     HIPTRY(c, enqueue_embed(c, m, c->stream, EMB_PREFILL, cnt, p, 0, nullptr));
-    HIPTRY(c, enqueue_layers(c, m, c->stream, false));
+    HIPTRY(c, enqueue_layers(c, m, c->stream, kMaxRows, false));
   }
   return SPEC_OK;
 }
@@ -653,6 +657,8 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
     qf_elems = std::max(qf_elems, (size_t)m->nkv * ((m->nq / m->nkv + 1) / 2) *
                                       ((m->hd + 31) / 32) * 2 * 512);
   }
+  if (lm_groups > 8192)
+    return bail(fail(c, SPEC_ERR_ARG, "vocabulary too large for the softmax partial fold"));
   ar_choose_chunks(1, V, &c->ar_chunk, &c->ar_nchunks);
   c->sm_chunk = 4096;
   c->sm_nchunks = (V + c->sm_chunk - 1) / c->sm_chunk;
