@@ -184,15 +184,21 @@ int spec_get_history(spec_ctx* ctx, int32_t* host_out, int32_t n);
 
 /* With profiling on: durations in ms of the feed-forward gate/up GEMM
  * launches of the most recent spec_draft and spec_verify calls, in launch
- * order (draft launches first).  Synchronises.  *n_out = count written. */
+ * order (draft launches first).  A duration is the launch's slice of the
+ * back-to-back kernel stream: from the end of the O projection launched just
+ * before it to its own end, each end being the latest of the per-workgroup
+ * stamps the kernels write from the device wall clock.  It is therefore
+ * measured inside the replayed graphs and includes the launch overhead.  -1
+ * marks a launch whose stamps are missing.  Synchronises.  *n_out = count
+ * written. */
 int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out);
 
-/* Profiling switch.  When on, spec_draft and spec_verify launch their
- * kernels directly (no graph replay) and launch the feed-forward gate/up GEMM
- * with a hipEvent pair that takes that kernel's own start and end timestamps
- * (hipExtLaunchKernel), read back by spec_kernel_times;
- * kernels and results are the same as with graphs.  Synchronises.  Also set
- * at creation by spec_init_params.profile_kernels. */
+/* Profiling switch.  When on, spec_draft and spec_verify replay graphs
+ * captured with the stamp slots of the gate/up GEMMs and the O projections
+ * before them set (a separate graph cache from the plain one), after
+ * resetting those slots on the stream; kernels and results are the same as
+ * with profiling off.  Synchronises.
+ * Also set at creation by spec_init_params.profile_kernels. */
 int spec_set_profiling(spec_ctx* ctx, int32_t enable);
 
 /* Stateless accept/reject over a batch of independent sequences (the rule of

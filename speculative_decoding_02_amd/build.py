@@ -9,6 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "libspec")
 LIB = os.path.join(HERE, "libspec.so")
+RUNNER = os.path.join(HERE, "spec_run")   # native driver of the C ABI (no Python in the process)
 SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_accept.hip", "spec_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -47,6 +48,15 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    # the native driver links the library by its in-tree path
+    cmd = [HIPCC, *FLAGS, "-x", "hip", os.path.join(CSRC, "spec_run.cpp"), "-x", "none",
+           "-L", HERE, "-lspec", "-Wl,-rpath,$ORIGIN", "-o", RUNNER + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for spec_run.cpp:\n{r.stdout}\n{r.stderr}")
+    os.replace(RUNNER + ".tmp", RUNNER)
     return LIB
 
 

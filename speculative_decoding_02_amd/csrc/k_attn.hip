@@ -9,7 +9,9 @@
 // key and value.
 //
 // Two launches, no inter-block waiting:
-//  (1) partial kernel, one wave per (32-key chunk, kv head).  Everything
+//  (1) partial kernel, one wave per (32-key chunk, kv head, 16-query tile):
+//      the tiles of one chunk run as separate waves (on the same XCD, so the
+//      second reads the chunk's keys and values from L2).  Everything
 //      lives in registers: the wave issues all its loads at once (key
 //      fragments, value fragments, query fragments), then
 //        S^T = K Q^T  and  O^T = V^T P^T   on v_mfma_f32_16x16x32_bf16
@@ -66,10 +68,9 @@ SPEC_DEVICE uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // 4-key runs of the transposed value cache).
 template <int NES>
 __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
-  constexpr int QTG = NES <= 4 ? 2 : 1;  // 16-query tiles per register group
   constexpr int NET = 2 * NES;            // e-tiles of 16 covering 32*NES dims
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z;
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
   const int n_qt_max = (G + 1) / 2;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
@@ -81,28 +82,21 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.kv_layer_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.kv_layer_bytes);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf, a.qf_bytes);
-  // Query fragments.  Columns beyond this pass's query vectors hold finite
-  // values from earlier passes; their scores are masked below.
-  uint4 qf[QTG][NES][2];
-  auto load_q = [&](int qt0) {
+  // Query fragments of this wave's tile.  Columns beyond this pass's query
+  // vectors hold finite values from earlier passes; their scores are masked
+  // below.  Issued before the pass descriptor is read, with the chunk's two
+  // cache blocks (the second clamped to the table).
+  uint4 qf[NES][2];
 #pragma unroll
-    for (int t = 0; t < QTG; ++t) {
-      const int qt = qt0 + t;
+  for (int es = 0; es < NES; ++es) {
+    const bool ok = qt < n_qt_max && 32 * es + 8 * grp < hd;
 #pragma unroll
-      for (int es = 0; es < NES; ++es) {
-        const bool ok = qt < n_qt_max && 32 * es + 8 * grp < hd;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint32_t off =
-              (uint32_t)((((((size_t)h * n_qt_max + qt) * n_es + es) * 2 + p) * 64 + lane) * 16);
-          qf[t][es][p] = load16(rq, ok ? off : kOOB);
-        }
-      }
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t off =
+          (uint32_t)((((((size_t)h * n_qt_max + qt) * n_es + es) * 2 + p) * 64 + lane) * 16);
+      qf[es][p] = load16(rq, ok ? off : kOOB);
     }
-  };
-  // Issued before the pass descriptor is read: the first query tiles and
-  // the chunk's two cache blocks (the second clamped to the table).
-  load_q(0);
+  }
   const int blk0 = a.block_table[2 * c];
   const int blk1_any = a.block_table[min(2 * c + 1, a.n_blocks - 1)];
 
@@ -110,6 +104,7 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   const int n_keys = pos0 + n_rows;
   if (n_rows <= 0 || key0 >= n_keys) return;
   const int QG = G * n_rows, n_qt = (QG + 15) / 16;
+  if (qt >= n_qt) return;
   const int blk1 = key0 + kBlock < n_keys ? blk1_any : blk0;
   const float scale = 1.0f / sqrtf((float)hd);
   float* wso = a.ws_o + ((size_t)h * a.max_chunks + c) * a.qg_max * E16;
@@ -144,69 +139,61 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     }
   }
 
-  for (int qt0 = 0; qt0 < n_qt; qt0 += QTG) {
-    if (qt0 > 0) load_q(qt0);
+  // ---- scores S^T = K Q^T for the 32 keys -----------------------------
+  floatx4 s[2];
 #pragma unroll
-    for (int t = 0; t < QTG; ++t) {
-      const int qt = qt0 + t;
-      if (qt >= n_qt) continue;  // wave-uniform
-      // ---- scores S^T = K Q^T for the 32 keys -----------------------------
-      floatx4 s[2];
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int es = 0; es < NES; ++es) {
-          s[kt] = mfma16(kf[kt][es][0], qf[t][es][0], s[kt]);
-          s[kt] = mfma16(kf[kt][es][0], qf[t][es][1], s[kt]);
-          s[kt] = mfma16(kf[kt][es][1], qf[t][es][0], s[kt]);
-        }
-      }
-      const int qi = 16 * qt + l16;
-      const int limit = pos0 + qi / G;  // last key row qi's position sees
-      float sc[2][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 16 * kt + 4 * grp + r;
-          const bool vis = qi < QG && key < n_keys && key <= limit;
-          sc[kt][r] = vis ? s[kt][r] * scale : -INFINITY;
-          mx = fmaxf(mx, sc[kt][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float lsum = 0.0f;
-      uint16_t ph[8], pl[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = sc[j >> 2][j & 3];
-        const float pv = x == -INFINITY ? 0.0f : expf(x - mx);
-        lsum += pv;
-        ph[j] = f32_to_bf16_rne(pv);
-        pl[j] = f32_to_bf16_rne(pv - bf16_to_f32(ph[j]));
-      }
-      lsum += __shfl_xor(lsum, 16);
-      lsum += __shfl_xor(lsum, 32);
-      const uint4 pfh = make_uint4(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
-                                   pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7]));
-      const uint4 pfl = make_uint4(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]),
-                                   pack_bf16x2(pl[4], pl[5]), pack_bf16x2(pl[6], pl[7]));
-      // ---- unnormalised value sums O^T = V^T P^T --------------------------
-#pragma unroll
-      for (int et = 0; et < NET; ++et) {
-        if (et >= n_et) continue;  // wave-uniform
-        floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
-        o = mfma16(vf[et][0], pfh, o);
-        o = mfma16(vf[et][0], pfl, o);
-        o = mfma16(vf[et][1], pfh, o);
-        if (qi < QG)
-          *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      if (grp == 0 && qi < QG) wsml[qi] = make_float2(mx, lsum);
+    for (int es = 0; es < NES; ++es) {
+      s[kt] = mfma16(kf[kt][es][0], qf[es][0], s[kt]);
+      s[kt] = mfma16(kf[kt][es][0], qf[es][1], s[kt]);
+      s[kt] = mfma16(kf[kt][es][1], qf[es][0], s[kt]);
     }
   }
+  const int qi = 16 * qt + l16;
+  const int limit = pos0 + qi / G;  // last key row qi's position sees
+  float sc[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 * kt + 4 * grp + r;
+      const bool vis = qi < QG && key < n_keys && key <= limit;
+      sc[kt][r] = vis ? s[kt][r] * scale : -INFINITY;
+      mx = fmaxf(mx, sc[kt][r]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float lsum = 0.0f;
+  uint16_t ph[8], pl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float x = sc[j >> 2][j & 3];
+    const float pv = x == -INFINITY ? 0.0f : expf(x - mx);
+    lsum += pv;
+    ph[j] = f32_to_bf16_rne(pv);
+    pl[j] = f32_to_bf16_rne(pv - bf16_to_f32(ph[j]));
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const uint4 pfh = make_uint4(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                               pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7]));
+  const uint4 pfl = make_uint4(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]),
+                               pack_bf16x2(pl[4], pl[5]), pack_bf16x2(pl[6], pl[7]));
+  // ---- unnormalised value sums O^T = V^T P^T --------------------------
+#pragma unroll
+  for (int et = 0; et < NET; ++et) {
+    if (et >= n_et) continue;  // wave-uniform
+    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+    o = mfma16(vf[et][0], pfh, o);
+    o = mfma16(vf[et][0], pfl, o);
+    o = mfma16(vf[et][1], pfh, o);
+    if (qi < QG)
+      *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+  if (grp == 0 && qi < QG) wsml[qi] = make_float2(mx, lsum);
 }
 
 // Merge of the chunk partials of query vector qi of kv head h.  Thread
@@ -309,7 +296,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 template <int NES>
 static void launch_partial(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv), dim3(64), 0, s, a);
+  const int n_qt_max = (a.n_q / a.n_kv + 1) / 2;  // 16-query tiles of kMaxRows rows
+  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv, n_qt_max), dim3(64), 0,
+                     s, a);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {

@@ -23,8 +23,6 @@
 //    squares published by the producer.
 #include <type_traits>
 
-#include <hip/hip_ext.h>
-
 #include "kernels.h"
 
 namespace spec {
@@ -315,31 +313,23 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
       }
     }
   }
-}
-
-// Plain launch, or (ev0 != null) a launch whose start/stop events take the
-// kernel's own start and end timestamps.
-template <typename Kern>
-static void launch_one(Kern k, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a,
-                       hipEvent_t ev0, hipEvent_t ev1) {
-  if (ev0)
-    hipExtLaunchKernelGGL(k, grid, block, 0, s, ev0, ev1, 0, a);
-  else
-    hipLaunchKernelGGL(k, grid, block, 0, s, a);
+  if (a.ts_end != nullptr) {
+    __syncthreads();
+    if (tid == 0) a.ts_end[g] = (unsigned long long)wall_clock64();
+  }
 }
 
 template <int NB, int W>
-static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s, hipEvent_t ev0,
-                             hipEvent_t ev1) {
+static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.n_groups), block(W * 64);
   switch (epi) {
-    case EPI_STORE: launch_one(gemm_skinny<NB, W, EPI_STORE>, grid, block, s, a, ev0, ev1); break;
-    case EPI_RESID: launch_one(gemm_skinny<NB, W, EPI_RESID>, grid, block, s, a, ev0, ev1); break;
-    case EPI_QKV: launch_one(gemm_skinny<NB, W, EPI_QKV>, grid, block, s, a, ev0, ev1); break;
-    case EPI_LOGITS: launch_one(gemm_skinny<NB, W, EPI_LOGITS>, grid, block, s, a, ev0, ev1); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE>), grid, block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID>), grid, block, 0, s, a); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV>), grid, block, 0, s, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS>), grid, block, 0, s, a); break;
     case EPI_SILU:
       if constexpr (NB % 2 == 0) {
-        launch_one(gemm_skinny<NB, W, EPI_SILU>, grid, block, s, a, ev0, ev1);
+        hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -348,16 +338,15 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s, hipEvent
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s, hipEvent_t ev0,
-                       hipEvent_t ev1) {
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) {
   if (sh.waves == 4) {
-    if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s, ev0, ev1);
-    if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s, ev0, ev1);
-    if (sh.nb == 4) return launch_epi<4, 4>(epi, a, s, ev0, ev1);
+    if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s);
+    if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s);
+    if (sh.nb == 4) return launch_epi<4, 4>(epi, a, s);
   } else if (sh.waves == 8) {
-    if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s, ev0, ev1);
-    if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s, ev0, ev1);
-    if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s, ev0, ev1);
+    if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s);
+    if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s);
+    if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s);
   }
   return hipErrorInvalidValue;
 }

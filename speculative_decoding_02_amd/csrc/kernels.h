@@ -53,16 +53,17 @@ struct GemmArgs {
   const int32_t* block_table;
   const float2* rope;      // [max_seq][head_dim/2] (cos, sin)
   int max_seq;
+  // Optional end stamps: workgroup g writes the device wall clock to
+  // ts_end[g] once all its threads have issued their last stores (a plain
+  // store per workgroup, no atomics).  Null: off.
+  unsigned long long* ts_end;
 };
 
 struct GemmShape {
   int nb;      // 16-column blocks per workgroup
   int waves;   // waves per workgroup, splitting K
 };
-// With ev0/ev1 non-null the two events take the kernel's own start and end
-// timestamps (hipExtLaunchKernel), for per-kernel timing on the stream.
-hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s,
-                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
 // Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
 constexpr int kGemmMaxSsqPerThread = 16;
 

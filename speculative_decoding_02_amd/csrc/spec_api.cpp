@@ -43,15 +43,16 @@ struct GemmPlan {
   int n_groups = 0, Kb = 0;
 };
 
-// Shapes measured on MI355X (graph-replayed sweep over nb in {1,2,4} and
-// waves in {4,8,16}): two blocks per workgroup once there are enough columns
-// to keep >= ~400 workgroups; four waves (more workgroups resident per CU),
-// except for narrow matrices with a long K, where only eight waves per
-// workgroup keep enough loads in flight.
+// Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4} and
+// waves in {4,8,16}, weights cold): two blocks per workgroup once that still
+// leaves >= 192 workgroups (fewer, longer workgroups stream better than
+// many short ones above that count, worse below it); four waves (more
+// workgroups resident per CU), except for narrow matrices with a long K,
+// where only eight waves per workgroup keep enough loads in flight.
 GemmPlan plan_gemm(int n_cols, int nb_min, int K) {
   GemmPlan p;
   const int n_blocks = n_cols / 16;
-  p.shape.nb = std::max(nb_min, (n_blocks >= 768 && n_blocks % 2 == 0) ? 2 : 1);
+  p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
   p.Kb = K / 32;
   p.n_groups = n_blocks / p.shape.nb;
   p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
@@ -122,14 +123,21 @@ struct spec_ctx {
   int last_k = 0;
   bool graphs = true;
   std::map<std::vector<uint64_t>, GraphEntry> graph_cache;
-  // profiling: plain launches; every gate/up GEMM carries an event pair that
-  // takes the kernel's own start and end timestamps
+  // profiling: each feed-forward gate/up GEMM and the O projection launched
+  // just before it write per-workgroup end stamps (device wall clock) into
+  // slot i of ts: [i][0][g] for the O projection, [i][1][g] for gate/up.  The
+  // gate/up launch's duration is the latest gate/up end minus the latest O
+  // end, i.e. its slice of the back-to-back stream, launch overhead
+  // included.  Draft launches use slots [0, k_max * draft layers), verify
+  // launches the target-layer slots after them.  Graphs are captured
+  // separately with profiling on (the kernels are the same).
   bool profiling = false;
-  std::vector<hipEvent_t> pool_draft, pool_verify;  // reusable events per call kind
-  std::vector<hipEvent_t> prof_draft, prof_verify;  // pairs recorded by the last calls
-  std::vector<hipEvent_t>* rec_events = nullptr;    // where profiled launches record
-  std::vector<hipEvent_t>* rec_pool = nullptr;
-  size_t rec_used = 0;
+  unsigned long long* ts = nullptr;
+  int ts_cap = 0;
+  int ts_groups = 0;            // workgroups per stamp row (largest O / gate/up grid)
+  int ts_next = 0;              // next slot while enqueueing a pass
+  int prof_draft_n = 0, prof_verify_n = 0;  // slots written by the last calls
+  int wall_khz = 0;             // wall-clock counter rate
 };
 
 namespace {
@@ -355,18 +363,6 @@ GemmArgs gemm_base(spec_ctx* c, const Mat& w, const uint16_t* ap) {
   return a;
 }
 
-hipError_t next_event(spec_ctx* c, hipEvent_t* ev) {
-  std::vector<hipEvent_t>& pool = *c->rec_pool;
-  if (c->rec_used == pool.size()) {
-    hipEvent_t e = nullptr;
-    hipError_t r = hipEventCreate(&e);
-    if (r != hipSuccess) return r;
-    pool.push_back(e);
-  }
-  *ev = pool[c->rec_used++];
-  return hipSuccess;
-}
-
 // Per layer: QKV (norm scale, RoPE, KV append) -> attention -> O (+residual)
 // -> gate/up (norm scale, SiLU*up) -> down (+residual).  The sums of squares
 // for each RMSNorm alternate between two buffers so a producer never writes
@@ -401,6 +397,8 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     GemmArgs b = gemm_base(c, m.o[l], c->ap_o);
     b.resid = c->x; b.ldr = m.d; b.gain_next = m.ffn_norm(l); b.Ap_out = c->ap_x;
     b.ssq_out = ssq_other;
+    const bool stamp = profile && c->ts_next < c->ts_cap;
+    if (stamp) b.ts_end = c->ts + (size_t)c->ts_next * 2 * c->ts_groups;
     e = launch_gemm(m.o[l].plan.shape, EPI_RESID, b, s);
     if (e != hipSuccess) break;
     std::swap(ssq_in, ssq_other);
@@ -408,18 +406,8 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     // RMSNorm + gate/up + SiLU*mul -> packed A of the down projection
     GemmArgs g = gemm_base(c, m.gu[l], c->ap_x);
     g.ssq = ssq_in; g.ssq_groups = ssq_groups; g.eps = m.eps; g.Ap_out = c->ap_a;
-    if (profile && c->rec_events) {
-      hipEvent_t e0 = nullptr, e1 = nullptr;
-      e = next_event(c, &e0);
-      if (e == hipSuccess) e = next_event(c, &e1);
-      if (e == hipSuccess) e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s, e0, e1);
-      if (e == hipSuccess) {
-        c->rec_events->push_back(e0);
-        c->rec_events->push_back(e1);
-      }
-    } else {
-      e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
-    }
+    if (stamp) g.ts_end = c->ts + ((size_t)c->ts_next++ * 2 + 1) * c->ts_groups;
+    e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
     if (e != hipSuccess) break;
     // down projection + residual; packs x * (next attn_norm or final norm)
     GemmArgs dn = gemm_base(c, m.dn[l], c->ap_a);
@@ -506,26 +494,31 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
 }
 
 // Runs `body` either through a cached graph captured on the capture stream,
-// or (no graphs, or profiling) directly on the context stream.
+// or (no graphs) directly on the context stream.  With profiling on, the
+// pass's timestamp slots [slot0, slot0 + n_slots) are reset on the stream
+// first (outside any graph) and the graph is keyed separately.
 template <typename F>
-int run_pass(spec_ctx* c, const std::vector<uint64_t>& key, std::vector<hipEvent_t>* prof_events,
-             std::vector<hipEvent_t>* pool, F body) {
-  if (!c->graphs || c->profiling) {
-    prof_events->clear();
-    c->rec_events = prof_events;
-    c->rec_pool = pool;
-    c->rec_used = 0;
-    hipError_t e = body(c->stream);
-    c->rec_events = nullptr;
-    c->rec_pool = nullptr;
-    HIPTRY(c, e);
+int run_pass(spec_ctx* c, std::vector<uint64_t> key, int slot0, int n_slots, F body) {
+  if (c->profiling) {
+    n_slots = std::min(n_slots, c->ts_cap - slot0);
+    HIPTRY(c, hipMemsetAsync(c->ts + (size_t)slot0 * 2 * c->ts_groups, 0,
+                             (size_t)n_slots * 2 * c->ts_groups * sizeof(unsigned long long),
+                             c->stream));
+    key.push_back(0x70726f66ull);  // separate graphs with the timestamp slots baked in
+  }
+  auto enqueue = [&](hipStream_t s) {
+    c->ts_next = slot0;
+    return body(s);
+  };
+  if (!c->graphs) {
+    HIPTRY(c, enqueue(c->stream));
     return SPEC_OK;
   }
   auto it = c->graph_cache.find(key);
   if (it == c->graph_cache.end()) {
     GraphEntry ge;
     HIPTRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeRelaxed));
-    hipError_t e = body(c->cap_stream);
+    hipError_t e = enqueue(c->cap_stream);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(c->cap_stream, &g);
     if (e == hipSuccess) e = e2;
@@ -560,8 +553,7 @@ void destroy_ctx(spec_ctx* c) {
   if (c->stream) (void)hipStreamSynchronize(c->stream);
   for (auto& kv : c->graph_cache)
     if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
-  for (hipEvent_t ev : c->pool_draft) (void)hipEventDestroy(ev);
-  for (hipEvent_t ev : c->pool_verify) (void)hipEventDestroy(ev);
+  (void)hipFree(c->ts);
   free_model(c->D);
   free_model(c->T);
   void* bufs[] = {c->x, c->qf, c->ssq_a, c->ssq_b, c->ap_x, c->ap_o, c->ap_a, c->logits, c->Tbuf,
@@ -682,6 +674,13 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   TRYH(dalloc(&c->ar_ws, (size_t)c->ar_nchunks * ar_ws_words(SPEC_K_MAX)));
   TRYH(dalloc(&c->rows, 1));
   TRYH(dalloc(&c->st, 1));
+  c->ts_cap = p->k_max * c->D.L + c->T.L;
+  for (const Model* m : ms)
+    for (int l = 0; l < m->L; ++l)
+      c->ts_groups = std::max({c->ts_groups, m->o[l].plan.n_groups, m->gu[l].plan.n_groups});
+  TRYH(dalloc(&c->ts, (size_t)c->ts_cap * 2 * c->ts_groups));
+  TRYH(hipDeviceGetAttribute(&c->wall_khz, hipDeviceAttributeWallClockRate, c->device));
+  if (c->wall_khz <= 0) return bail(fail(c, SPEC_ERR_HIP, "device reports no wall-clock rate"));
   TRYH(hipMemsetAsync(c->ap_x, 0, (size_t)32 * dmax, c->stream));
   TRYH(hipMemsetAsync(c->ap_o, 0, (size_t)32 * qmax, c->stream));
   TRYH(hipMemsetAsync(c->ap_a, 0, (size_t)32 * fmax, c->stream));
@@ -731,9 +730,10 @@ int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_d
   }
   std::vector<uint64_t> key = {1, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev};
-  int r = run_pass(c, key, &c->prof_draft, &c->pool_draft,
+  int r = run_pass(c, key, 0, K * c->D.L,
                    [&](hipStream_t s) { return enqueue_draft(c, s, K, seed, d_dev, D_dev); });
   if (r) return r;
+  c->prof_draft_n = c->profiling ? std::min(K * c->D.L, c->ts_cap) : 0;
   c->drafted_k = K;
   return SPEC_OK;
 }
@@ -762,10 +762,12 @@ int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, con
                                (uint64_t)(uintptr_t)n_acc_dev,
                                (uint64_t)(uintptr_t)T_dev,
                                (uint64_t)(uintptr_t)logits_dev};
-  int r = run_pass(c, key, &c->prof_verify, &c->pool_verify, [&](hipStream_t s) {
+  const int vslot0 = c->p.k_max * c->D.L;
+  int r = run_pass(c, key, vslot0, c->T.L, [&](hipStream_t s) {
     return enqueue_verify(c, s, K, seed, d_dev, D_dev, out_dev, n_acc_dev, T_dev, logits_dev);
   });
   if (r) return r;
+  c->prof_verify_n = c->profiling ? std::min(c->T.L, c->ts_cap - vslot0) : 0;
   c->verify_pending = true;
   c->last_k = K;
   return SPEC_OK;
@@ -822,20 +824,31 @@ int spec_get_history(spec_ctx* c, int32_t* host_out, int32_t n) {
 }
 
 int spec_kernel_times(spec_ctx* c, float* ms_out, int32_t cap, int32_t* n_out) {
-  if (!c || !n_out || (cap > 0 && !ms_out)) return fail(c, SPEC_ERR_ARG, "spec_kernel_times: bad argument");
+  if (!c || !n_out || cap < 0 || (cap > 0 && !ms_out))
+    return fail(c, SPEC_ERR_ARG, "spec_kernel_times: bad argument");
   HIPTRY(c, hipStreamSynchronize(c->stream));
+  std::vector<unsigned long long> h((size_t)c->ts_cap * 2 * c->ts_groups);
+  if (!h.empty())
+    HIPTRY(c, hipMemcpy(h.data(), c->ts, h.size() * sizeof(unsigned long long),
+                        hipMemcpyDeviceToHost));
   int n = 0;
-  auto take = [&](const std::vector<hipEvent_t>& ev) -> int {
-    for (size_t i = 0; i + 1 < ev.size(); i += 2) {
-      float ms = 0.f;
-      HIPTRY(c, hipEventElapsedTime(&ms, ev[i], ev[i + 1]));
+  // a stamp of 0 is a workgroup that did not write (the slot was reset)
+  auto take = [&](int slot0, int cnt, const Model& m, int layer0) {
+    for (int i = slot0; i < slot0 + cnt; ++i) {
+      const int l = (layer0 + i - slot0) % m.L;
+      const unsigned long long* o = &h[(size_t)i * 2 * c->ts_groups];
+      const unsigned long long* g = o + c->ts_groups;
+      unsigned long long o_end = 0, g_end = 0;
+      bool ok = true;
+      for (int w = 0; w < m.o[l].plan.n_groups; ++w) { ok = ok && o[w] != 0; o_end = std::max(o_end, o[w]); }
+      for (int w = 0; w < m.gu[l].plan.n_groups; ++w) { ok = ok && g[w] != 0; g_end = std::max(g_end, g[w]); }
+      const float ms = ok && g_end > o_end ? (float)((double)(g_end - o_end) / c->wall_khz) : -1.0f;
       if (n < cap) ms_out[n] = ms;
       ++n;
     }
-    return SPEC_OK;
   };
-  if (int r = take(c->prof_draft)) return r;
-  if (int r = take(c->prof_verify)) return r;
+  take(0, c->prof_draft_n, c->D, 0);
+  take(c->p.k_max * c->D.L, c->prof_verify_n, c->T, 0);
   *n_out = std::min(n, cap);
   return SPEC_OK;
 }

@@ -144,6 +144,19 @@ def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0) -
                          f"avg {sum(ks) / len(ks):.2f} us")
             for g, v in sorted(by_grid.items()):
                 lines.append(f"  grid_x {g}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+        if skip_last > 0:
+            tail = rows[marks[len(marks) - 1 - skip_last] + 1: marks[-1] + 1]
+            by_grid = collections.defaultdict(list)
+            for _, n, s, e, g in tail:
+                if kernel in n:
+                    by_grid[g].append((e - s) / 1e3)
+            allv = [x for v in by_grid.values() for x in v]
+            if allv:
+                lines.append("")
+                lines.append(f"kernel '{kernel}' in the last {skip_last} rounds: {len(allv)} launches, "
+                             f"avg {sum(allv) / len(allv):.2f} us")
+                for g, v in sorted(by_grid.items()):
+                    lines.append(f"  grid_x {g}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
     return "\n".join(lines)
 
 

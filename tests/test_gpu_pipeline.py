@@ -99,6 +99,34 @@ def test_graph_and_eager_agree_and_repeat(toy):
                 np.testing.assert_array_equal(a[k], c[k], err_msg=k)
 
 
+def test_profiling_rounds_match_and_time(toy):
+    """With profiling on, the graphs carry the gate/up GEMM's timestamp slots:
+    tokens and rows are the same as without, and every draft and verify
+    gate/up launch reports a positive duration, in launch order."""
+    import speculative_decoding_02_amd as sd
+    tw, dw = toy
+    prompt = synth.prompt(synth.TOY.vocab, 20, seed=6)
+    K = 3
+    runs = []
+    for prof in (False, True):
+        ctx, keep = make_ctx(tw, dw, prompt, K, False)
+        if prof:
+            sd.spec_set_profiling(ctx, True)
+        b = Buffers(K, synth.TOY.vocab)
+        rounds = []
+        for _ in range(4):
+            rounds.append(gpu_round(sd, ctx, K, 31, b))
+            if prof:
+                t = sd.spec_kernel_times(ctx)
+                assert len(t) == K * synth.TOY_DRAFT.n_layers + synth.TOY.n_layers
+                assert np.all(t > 0) and np.all(t < 50.0), t
+        runs.append(rounds)
+        sd.spec_destroy(ctx)
+    for a, c in zip(runs[0], runs[1]):
+        for k in ("d", "out", "D", "T", "logits"):
+            np.testing.assert_array_equal(a[k], c[k], err_msg=k)
+
+
 def test_external_drafts_and_state_errors(toy):
     """Verify with drafts that did not come from spec_draft (one-hot D rows:
     a deterministic drafter), commit without draft, then a draft call that
