@@ -80,6 +80,8 @@ def lib():
         L.orc_rmsnorm.argtypes = [_p, _i32, _p, C.c_double, _p]
         L.orc_attend.argtypes = [_p, _p, _p, _i32, _i32, _p]
         L.orc_draft_sample_batch.argtypes = [_p, _i32, _i32, _u64, _p, _u64, _i32, _p]
+        L.orc_ngram_draft.argtypes = [_p, _i32, _i32, _i32, _p]
+        L.orc_ngram_draft.restype = _i32
         _lib = L
     return _lib
 
@@ -187,6 +189,18 @@ def draft_sample_batch(D, seed: int, pos, c: int = 0, greedy: bool = False) -> n
     out = np.zeros(B, np.int32)
     lib().orc_draft_sample_batch(_ptr(Da), B, V, seed, _ptr(pa), c, int(bool(greedy)), _ptr(out))
     return out
+
+
+def ngram_draft(hist, L: int, K: int, n_max: int):
+    """(draft tokens [K], match length) from orc_ngram_draft on hist[0..L]."""
+    h = _c(hist, np.int32)
+    if not 0 <= L < len(h):
+        raise ValueError("L outside the history")
+    d = np.zeros(K, np.int32)
+    n = lib().orc_ngram_draft(_ptr(h), L, K, n_max, _ptr(d))
+    if n < 0:
+        raise ValueError(f"orc_ngram_draft error {n}")
+    return d, int(n)
 
 
 def icdf_histogram(q) -> np.ndarray:

@@ -632,3 +632,23 @@ int orc_draft_sample_batch(const float* D, int32_t B, int32_t V, uint64_t seed, 
     out[b] = orc_draft_sample(D + (size_t)b * V, V, seed, pos[b], (uint64_t)b, c, greedy);
   return ORC_OK;
 }
+
+/* ---- prompt-lookup (n-gram) drafter ([en] Floor 6: prompt lookup searches
+ * the preceding text for a chunk likely to repeat and drafts what followed).
+ * Longest key first, latest occurrence first: a plain double loop. */
+int32_t orc_ngram_draft(const int32_t* hist, int32_t L, int32_t K, int32_t n_max, int32_t* d) {
+  if (!hist || !d || L < 0 || K < 1 || n_max < 1) return ORC_EARG;
+  for (int32_t n = n_max < L ? n_max : L; n >= 1; n--) {
+    for (int32_t j = L - 1; j >= n - 1; j--) {
+      int32_t same = 1;
+      for (int32_t t = 0; t < n && same; t++) same = hist[j - t] == hist[L - t];
+      if (same) {
+        const int32_t p = L - j;
+        for (int32_t i = 0; i < K; i++) d[i] = hist[j + 1 + i % p];
+        return n;
+      }
+    }
+  }
+  for (int32_t i = 0; i < K; i++) d[i] = hist[L];
+  return 0;
+}

@@ -145,6 +145,18 @@ void orc_attend(const double* q, const double* k, const double* v, int32_t n_key
 int orc_draft_sample_batch(const float* D, int32_t B, int32_t V, uint64_t seed, const uint64_t* pos,
                            uint64_t c, int32_t greedy, int32_t* out);
 
+/* ---- prompt-lookup (n-gram) drafter ---------------------------------------
+ * [en] Floor 6 (and [zh] Level 6): n-gram approaches such as prompt lookup
+ * draft by searching the preceding text for a chunk that repeats and
+ * proposing what followed it; the verification rule is unchanged.
+ * hist[0..L] is the committed text, hist[L] the pending token.  For
+ * n = n_max down to 1 (n <= L), take the latest j in [n-1, L-1] with
+ * hist[j-n+1..j] == hist[L-n+1..L]; the first n that has one is used.  The
+ * draft is the text that followed, repeated with period p = L - j:
+ * d[i] = hist[j + 1 + (i mod p)], i = 0..K-1.  Without any match,
+ * d[i] = hist[L].  Returns the match length used (0: none) or ORC_EARG. */
+int32_t orc_ngram_draft(const int32_t* hist, int32_t L, int32_t K, int32_t n_max, int32_t* d);
+
 int32_t orc_num_threads(void);
 
 #ifdef __cplusplus
