@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--pair", default="8b", choices=["toy", "1.3b", "8b", "31b"])
     ap.add_argument("--prompt-len", type=int, default=None)
     ap.add_argument("--greedy", action="store_true")
+    ap.add_argument("--drafter", default="model", choices=["model", "ngram"],
+                    help="draft model (default) or the prompt-lookup drafter (spec_draft_ngram)")
+    ap.add_argument("--ngram-n", type=int, default=3, help="longest key of the n-gram drafter")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
@@ -154,7 +157,10 @@ def main():
     def one_round(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sd.spec_draft(ctx, K, seed, d, D)
+        if args.drafter == "ngram":
+            sd.spec_draft_ngram(ctx, K, args.ngram_n, d, D)
+        else:
+            sd.spec_draft(ctx, K, seed, d, D)
         if ev is not None:
             ev[1].record(stream)
         sd.spec_verify(ctx, K, seed, d, D, out, nacc)
@@ -188,7 +194,9 @@ def main():
     L_mid = plen + tokens // 2 + st0["target_len"] - plen
     vbytes = verify_pass_bytes(tcfg, K, L_mid)
     vgbs = vbytes / (np.median(verify_ms) / 1e3) / 1e9
-    dbytes = K * draft_step_bytes(dcfg, L_mid)
+    # the prompt-lookup drafter reads the history and writes K one-hot rows
+    dbytes = (K * draft_step_bytes(dcfg, L_mid) if args.drafter == "model"
+              else K * V * 4 + (L_mid + 1) * 4)
     dgbs = dbytes / (np.median(draft_ms) / 1e3) / 1e9
 
     # dominant kernel: the feed-forward gate/up GEMM.  A second timed region
@@ -206,7 +214,7 @@ def main():
             one_round()
             kts.append(sd.spec_kernel_times(ctx))
         sd.spec_set_profiling(ctx, False)
-        n_draft = K * dcfg.n_layers
+        n_draft = K * dcfg.n_layers if args.drafter == "model" else 0
         kt_d = np.concatenate([k[:n_draft] for k in kts])
         kt_t = np.concatenate([k[n_draft:] for k in kts])
         b_d = gateup_bytes(dcfg, 1) * len(kt_d)
@@ -244,7 +252,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{tcfg.name} target + {dcfg.name} draft, batch 1, K={K}, prompt {plen}, "
+            "workload": f"{tcfg.name} target + "
+                        + (f"{dcfg.name} draft" if args.drafter == "model"
+                           else f"prompt-lookup drafter (keys up to {args.ngram_n} tokens)")
+                        + f", batch 1, K={K}, prompt {plen}, "
                         f"{'greedy' if args.greedy else 'temperature-1 sampling'}, random-init bf16",
             "K": K, "batch": 1, "prompt_len": plen, "mode": "greedy" if args.greedy else "sampling",
         },
@@ -262,7 +273,7 @@ def main():
     log(json.dumps({k: res[k] for k in ("value", "ms_per_step", "verify_pass", "draft_loop",
                                          "tokens_per_round")}))
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.drafter == "model":
         res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr)
     sd.spec_destroy(ctx)
     print(json.dumps(res), flush=True)

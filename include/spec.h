@@ -121,6 +121,22 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
  * SPEC_ERR_STATE (the draft cache lags by more than 7 tokens). */
 int spec_draft(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev);
 
+/* Prompt-lookup drafter ([en] Floor 6, [zh] Level 6: n-gram approaches such
+ * as prompt lookup draft by searching the preceding text for a chunk likely
+ * to repeat; verification is unchanged), run on the device with no draft
+ * model.  The committed history hist[0..L] (hist[L] the pending token) is
+ * searched for the latest earlier occurrence of its last n tokens, the
+ * longest n <= n_max first; the K drafts are the tokens that followed it,
+ * repeated with its period p = L - j when fewer than K follow, or the pending
+ * token K times when nothing repeats.  D_dev receives one-hot rows (a
+ * deterministic drafter), so spec_verify's rule accepts d_i with probability
+ * T_i(d_i) and otherwise samples T_i without d_i.  The draft model's cache is
+ * left as it is (a later spec_draft catches it up).
+ *   d_dev: int32 [K]; D_dev: fp32 [K][vocab] (may be NULL in greedy mode).
+ * Errors: SPEC_ERR_ARG (K outside 1..k_max, n_max outside 1..8, null
+ * pointers). */
+int spec_draft_ngram(spec_ctx* ctx, int32_t K, int32_t n_max, int32_t* d_dev, float* D_dev);
+
 /* Verify pass plus accept/reject ([int] algorithm core, Steps 2-4; [en]
  * Floors 3-5).  One target pass over the K+1 rows [pending, d_1..d_K] at
  * positions L..L+K gives T_1..T_{K+1}; their keys/values are appended to the

@@ -70,6 +70,7 @@ def lib():
         L.spec_init.argtypes = [C.POINTER(SpecInitParams), _p, _i32, C.POINTER(_p)]
         L.spec_draft.argtypes = [_p, _i32, _u64, _p, _p]
         L.spec_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
+        L.spec_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
         L.spec_commit.argtypes = [_p, _p, _p]
         L.spec_destroy.argtypes = [_p]
         L.spec_last_error.argtypes = [_p]
@@ -87,7 +88,7 @@ def lib():
     return _lib
 
 
-EXPORTED = ("spec_init", "spec_draft", "spec_verify", "spec_commit", "spec_destroy",
+EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
             "spec_kernel_times", "spec_set_profiling", "spec_accept_reject")
 
@@ -151,6 +152,10 @@ def spec_init(target_cfg, target_w, draft_cfg, draft_w, prompt, *, k_max: int, m
 
 def spec_draft(ctx: Ctx, K: int, seed: int, d, D) -> None:
     _check(lib().spec_draft(ctx.handle, K, seed, _ptr(d), _ptr(D)), ctx)
+
+
+def spec_draft_ngram(ctx: Ctx, K: int, n_max: int, d, D=None) -> None:
+    _check(lib().spec_draft_ngram(ctx.handle, K, n_max, _ptr(d), _ptr(D)), ctx)
 
 
 def spec_verify(ctx: Ctx, K: int, seed: int, d, D, out, n_acc, T=None, logits=None) -> None:

@@ -262,8 +262,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before any use
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
+      // slots past the active chunks were loaded from clamped indices: their
+      // workspace contents may be anything (not even finite), so they are
+      // replaced, not weighted by zero
       const bool ok = c0 + u * ncg < n_active;
-      const float o[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+      const float o[8] = {ok ? v0[u].x : 0.f, ok ? v0[u].y : 0.f, ok ? v0[u].z : 0.f,
+                          ok ? v0[u].w : 0.f, ok ? v1[u].x : 0.f, ok ? v1[u].y : 0.f,
+                          ok ? v1[u].z : 0.f, ok ? v1[u].w : 0.f};
       merge_in(st, ok ? mv[u].x : -INFINITY, ok ? mv[u].y : 0.0f, o);
     }
   }

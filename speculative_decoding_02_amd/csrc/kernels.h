@@ -151,6 +151,19 @@ void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks);
 // Two launches: chunk partials, then one finishing block per sequence.
 hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
 
+// ------------------------------------------------------ n-gram drafter --
+constexpr int kNgramMaxN = 8;   // longest key searched
+constexpr int kNgramMaxK = 8;   // drafts per call (>= SPEC_K_MAX)
+struct NgramArgs {
+  const DevState* st;     // LT: position of the pending token
+  const int32_t* hist;    // committed history [hist_cap]
+  int hist_cap;
+  int K, n_max, V;
+  int32_t* d;             // [K] draft tokens
+  float* D;               // [K][V] one-hot draft rows, or null
+};
+hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- commit --
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
                          const int32_t* n_acc, int drafted_k, hipStream_t s);

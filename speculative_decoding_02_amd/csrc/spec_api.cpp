@@ -738,6 +738,27 @@ int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_d
   return SPEC_OK;
 }
 
+int spec_draft_ngram(spec_ctx* c, int32_t K, int32_t n_max, int32_t* d_dev, float* D_dev) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_draft_ngram: null context");
+  if (K < 1 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..k_max", K));
+  if (n_max < 1 || n_max > kNgramMaxN)
+    return fail(c, SPEC_ERR_ARG, fmt("n_max=%d outside 1..%d", n_max, kNgramMaxN));
+  if (!d_dev || (!D_dev && !c->p.greedy)) return fail(c, SPEC_ERR_ARG, "spec_draft_ngram: null output");
+  HIPTRY(c, hipSetDevice(c->device));
+  std::vector<uint64_t> key = {3, (uint64_t)K, (uint64_t)n_max, (uint64_t)(uintptr_t)d_dev,
+                               (uint64_t)(uintptr_t)D_dev};
+  int r = run_pass(c, key, 0, 0, [&](hipStream_t s) {
+    NgramArgs a{};
+    a.st = c->st; a.hist = c->hist; a.hist_cap = c->hist_cap;
+    a.K = K; a.n_max = n_max; a.V = c->T.V; a.d = d_dev; a.D = D_dev;
+    return launch_ngram_draft(a, s);
+  });
+  if (r) return r;
+  c->drafted_k = 0;  // no draft-model rows were computed: the draft cache keeps its length
+  c->prof_draft_n = 0;
+  return SPEC_OK;
+}
+
 int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
                 int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev) {
   if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_verify: null context");
