@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--drafter", default="model", choices=["model", "ngram"],
                     help="draft model (default) or the prompt-lookup drafter (spec_draft_ngram)")
     ap.add_argument("--ngram-n", type=int, default=3, help="longest key of the n-gram drafter")
+    ap.add_argument("--adaptive-k", action="store_true",
+                    help="choose K every few rounds from the measured acceptance rate "
+                         "(spec_alpha_from_tokens + spec_choose_k) instead of a fixed K")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
@@ -142,6 +145,9 @@ def main():
     log(f"weights generated in {time.time() - t0:.1f}s")
     prompt = synth.prompt(tcfg.vocab, plen)
     t0 = time.time()
+    if args.adaptive_k:
+        K = sd.SPEC_K_MAX
+        max_seq = plen + (K + 1) * (rounds_total + 3 * K + 8) + 16
     ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=args.greedy,
                        use_graphs=True, profile_kernels=False)
     log(f"spec_init (pack + prefill {plen} tokens) in {time.time() - t0:.1f}s")
@@ -167,6 +173,12 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         sd.spec_commit(ctx, out, nacc)
+
+    if args.adaptive_k:
+        res = adaptive_k_run(sd, torch, ctx, stream, d, D, out, nacc, seed, args, tcfg, dcfg, plen)
+        sd.spec_destroy(ctx)
+        print(json.dumps(res), flush=True)
+        return
 
     for _ in range(args.warmup):
         one_round()
@@ -265,6 +277,12 @@ def main():
         "draft_loop": {"ms_median": round(float(np.median(draft_ms)), 4),
                        "algorithmic_GB": round(dbytes / 1e9, 4), "GB_s": round(dgbs, 1)},
         "tokens_per_round": round(tpr, 4),
+        # what the measured round time would give at the acceptance rates of
+        # the pages' examples ([en] Floor 6): a projection, not a measurement
+        "projection_tokens_per_s": {
+            f"alpha_{a}": round(sd.spec_expected_tokens(a, K)
+                                / ((np.median(draft_ms) + np.median(verify_ms)) / 1e3), 1)
+            for a in (0.5, 0.7, 0.8)},
         "target_passes_per_token": round(args.steps / max(tokens, 1), 4),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
@@ -277,6 +295,73 @@ def main():
         res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr)
     sd.spec_destroy(ctx)
     print(json.dumps(res), flush=True)
+
+
+def adaptive_k_run(sd, torch, ctx, stream, d, D, out, nacc, seed, args, tcfg, dcfg, plen):
+    """Rounds with K chosen every 8 rounds: the acceptance rate is estimated
+    from the tokens the last window committed (spec_alpha_from_tokens, the
+    inverse of [en] Floor 6's mean), smoothed, and K is the value that
+    maximises tokens per unit time under the measured draft-step and verify
+    times (spec_choose_k)."""
+    import numpy as np
+    k_max = sd.SPEC_K_MAX
+
+    def rnd(K, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sd.spec_draft(ctx, K, seed, d, D)
+        if ev is not None:
+            ev[1].record(stream)
+        sd.spec_verify(ctx, K, seed, d, D, out, nacc)
+        if ev is not None:
+            ev[2].record(stream)
+        sd.spec_commit(ctx, out, nacc)
+
+    for K in range(1, k_max + 1):  # capture every K's graphs before timing
+        rnd(K)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(5)]
+    for e in evs:
+        rnd(4, e)
+    sd.spec_sync(ctx)
+    t_draft = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) / 4
+    t_verify = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    W, K, alpha = 8, 4, None
+    traj = []
+    st0 = sd.spec_get_state(ctx)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    last = st0["target_len"]
+    for w in range(max(1, args.steps // W)):
+        for _ in range(W):
+            rnd(K)
+        st = sd.spec_get_state(ctx)
+        a = sd.spec_alpha_from_tokens((st["target_len"] - last) / W, K)
+        last = st["target_len"]
+        alpha = a if alpha is None else 0.5 * alpha + 0.5 * a
+        traj.append(K)
+        K = sd.spec_choose_k(alpha, t_draft, t_verify, k_max)
+    t1.record(stream)
+    sd.spec_sync(ctx)
+    st1 = sd.spec_get_state(ctx)
+    assert st1["device_error"] == 0, st1
+    ms = t0.elapsed_time(t1)
+    tokens = st1["target_len"] - st0["target_len"]
+    rounds = W * len(traj)
+    return {
+        "metric": "accepted tokens/s at batch 1, K=4; verify-pass HBM GB/s as % of MI355X peak",
+        "value": round(tokens / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": rounds,
+        "warmup": k_max + 5, "ms_per_step": round(ms / rounds, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{tcfg.name} target + {dcfg.name} draft, batch 1, K chosen every "
+                               f"{W} rounds from the measured acceptance, prompt {plen}, "
+                               f"{'greedy' if args.greedy else 'temperature-1 sampling'}, "
+                               f"random-init bf16", "K": "adaptive", "batch": 1,
+                   "prompt_len": plen},
+        "adaptive_k": {"t_draft_step_ms": round(t_draft, 4), "t_verify_ms": round(t_verify, 4),
+                       "alpha_estimate": round(alpha, 4), "k_per_window": traj,
+                       "tokens_per_round": round(tokens / rounds, 4)},
+        "roofline": None, "cpu_baseline": None,
+    }
 
 
 def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):

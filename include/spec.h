@@ -217,6 +217,23 @@ int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out)
  * Also set at creation by spec_init_params.profile_kernels. */
 int spec_set_profiling(spec_ctx* ctx, int32_t enable);
 
+/* Choosing K from the measured acceptance rate (host-side helpers; no
+ * context, no device work).
+ * spec_expected_tokens: mean tokens one round yields when each of its K
+ * drafts passes independently with probability alpha, 1 + alpha + ... +
+ * alpha^K = (1 - alpha^(K+1)) / (1 - alpha) ([en] Floor 6; [zh] Level 6).
+ * spec_alpha_from_tokens: the alpha at which that mean equals a measured
+ * tokens-per-round figure for a given K (bisection; 0 at or below 1 token,
+ * 1 at or above K+1).
+ * spec_choose_k: the K in 1..k_max that maximises tokens per unit time,
+ * spec_expected_tokens(alpha, K) / (K * t_draft_step + t_verify), with the
+ * round cost of [int] "speedup" (K draft steps plus one target pass); ties go
+ * to the smaller K.  Returns SPEC_ERR_ARG for alpha outside [0, 1], negative
+ * times, both times 0, or k_max < 1. */
+double spec_expected_tokens(double alpha, int32_t K);
+double spec_alpha_from_tokens(double tokens_per_round, int32_t K);
+int32_t spec_choose_k(double alpha, double t_draft_step, double t_verify, int32_t k_max);
+
 /* Stateless accept/reject over a batch of independent sequences (the rule of
  * spec_verify without the forward pass).
  *   T_dev: fp32 [B][K+1][V]; D_dev: fp32 [B][K][V] (unused if greedy);

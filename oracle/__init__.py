@@ -82,6 +82,10 @@ def lib():
         L.orc_draft_sample_batch.argtypes = [_p, _i32, _i32, _u64, _p, _u64, _i32, _p]
         L.orc_ngram_draft.argtypes = [_p, _i32, _i32, _i32, _p]
         L.orc_ngram_draft.restype = _i32
+        L.orc_expected_tokens.argtypes = [C.c_double, _i32]
+        L.orc_expected_tokens.restype = C.c_double
+        L.orc_choose_k.argtypes = [C.c_double, C.c_double, C.c_double, _i32]
+        L.orc_choose_k.restype = _i32
         _lib = L
     return _lib
 
@@ -201,6 +205,19 @@ def ngram_draft(hist, L: int, K: int, n_max: int):
     if n < 0:
         raise ValueError(f"orc_ngram_draft error {n}")
     return d, int(n)
+
+
+def expected_tokens(alpha: float, K: int) -> float:
+    """orc_expected_tokens: 1 + a + ... + a^K ([en] Floor 6)."""
+    return float(lib().orc_expected_tokens(alpha, K))
+
+
+def choose_k(alpha: float, t_draft: float, t_verify: float, k_max: int) -> int:
+    """orc_choose_k: the K in 1..k_max with the most tokens per unit time."""
+    k = lib().orc_choose_k(alpha, t_draft, t_verify, k_max)
+    if k < 0:
+        raise ValueError(f"orc_choose_k error {k}")
+    return int(k)
 
 
 def icdf_histogram(q) -> np.ndarray:

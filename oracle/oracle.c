@@ -652,3 +652,30 @@ int32_t orc_ngram_draft(const int32_t* hist, int32_t L, int32_t K, int32_t n_max
   for (int32_t i = 0; i < K; i++) d[i] = hist[L];
   return 0;
 }
+
+/* ---- K choice ([en] Floor 6 expected tokens; [int] "speedup" cost model) */
+double orc_expected_tokens(double a, int32_t K) {
+  /* the sum 1 + a + ... + a^K, term by term */
+  double sum = 0.0, term = 1.0;
+  for (int32_t j = 0; j <= K; j++) {
+    sum += term;
+    term *= a;
+  }
+  return sum;
+}
+
+int32_t orc_choose_k(double a, double t_draft, double t_verify, int32_t k_max) {
+  if (!(a >= 0.0 && a <= 1.0) || !(t_draft >= 0.0) || !(t_verify >= 0.0) || k_max < 1 ||
+      t_draft + t_verify <= 0.0)
+    return ORC_EARG;
+  int32_t best = 1;
+  double best_rate = -1.0;
+  for (int32_t K = 1; K <= k_max; K++) {
+    const double rate = orc_expected_tokens(a, K) / (K * t_draft + t_verify);
+    if (rate > best_rate) {
+      best_rate = rate;
+      best = K;
+    }
+  }
+  return best;
+}

@@ -157,6 +157,16 @@ int orc_draft_sample_batch(const float* D, int32_t B, int32_t V, uint64_t seed, 
  * d[i] = hist[L].  Returns the match length used (0: none) or ORC_EARG. */
 int32_t orc_ngram_draft(const int32_t* hist, int32_t L, int32_t K, int32_t n_max, int32_t* d);
 
+/* ---- choosing K from the acceptance rate --------------------------------
+ * [en] Floor 6: with each draft passing independently with probability a, a
+ * round yields (1 - a^(K+1)) / (1 - a) tokens on average (K + 1 at a = 1).
+ * [int] "speedup": a round costs about K draft steps plus one target pass.
+ * orc_choose_k returns the K in 1..k_max with the most tokens per unit of
+ * round time, E(a, K) / (K t_draft + t_verify); ties go to the smaller K.
+ * Returns ORC_EARG for a outside [0,1], negative times or k_max < 1. */
+double orc_expected_tokens(double a, int32_t K);
+int32_t orc_choose_k(double a, double t_draft, double t_verify, int32_t k_max);
+
 int32_t orc_num_threads(void);
 
 #ifdef __cplusplus

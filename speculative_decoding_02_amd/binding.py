@@ -71,6 +71,12 @@ def lib():
         L.spec_draft.argtypes = [_p, _i32, _u64, _p, _p]
         L.spec_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
         L.spec_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
+        L.spec_expected_tokens.argtypes = [C.c_double, _i32]
+        L.spec_expected_tokens.restype = C.c_double
+        L.spec_alpha_from_tokens.argtypes = [C.c_double, _i32]
+        L.spec_alpha_from_tokens.restype = C.c_double
+        L.spec_choose_k.argtypes = [C.c_double, C.c_double, C.c_double, _i32]
+        L.spec_choose_k.restype = _i32
         L.spec_commit.argtypes = [_p, _p, _p]
         L.spec_destroy.argtypes = [_p]
         L.spec_last_error.argtypes = [_p]
@@ -90,7 +96,8 @@ def lib():
 
 EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
-            "spec_kernel_times", "spec_set_profiling", "spec_accept_reject")
+            "spec_kernel_times", "spec_set_profiling", "spec_accept_reject", "spec_expected_tokens",
+            "spec_alpha_from_tokens", "spec_choose_k")
 
 
 def _check(rc: int, ctx=None):
@@ -156,6 +163,20 @@ def spec_draft(ctx: Ctx, K: int, seed: int, d, D) -> None:
 
 def spec_draft_ngram(ctx: Ctx, K: int, n_max: int, d, D=None) -> None:
     _check(lib().spec_draft_ngram(ctx.handle, K, n_max, _ptr(d), _ptr(D)), ctx)
+
+
+def spec_expected_tokens(alpha: float, K: int) -> float:
+    return float(lib().spec_expected_tokens(alpha, K))
+
+
+def spec_alpha_from_tokens(tokens_per_round: float, K: int) -> float:
+    return float(lib().spec_alpha_from_tokens(tokens_per_round, K))
+
+
+def spec_choose_k(alpha: float, t_draft_step: float, t_verify: float, k_max: int) -> int:
+    k = lib().spec_choose_k(alpha, t_draft_step, t_verify, k_max)
+    _check(0 if k > 0 else k)
+    return int(k)
 
 
 def spec_verify(ctx: Ctx, K: int, seed: int, d, D, out, n_acc, T=None, logits=None) -> None:

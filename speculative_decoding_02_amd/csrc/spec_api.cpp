@@ -881,6 +881,45 @@ int spec_set_profiling(spec_ctx* c, int32_t enable) {
   return SPEC_OK;
 }
 
+// ---------------------------------------------------------- choosing K --
+// [en] Floor 6: mean tokens per round with iid acceptance; [int] "speedup":
+// a round costs K draft steps plus one target pass.
+double spec_expected_tokens(double alpha, int32_t K) {
+  double total = 0.0, power = 1.0;  // alpha^j for j = 0..K
+  for (int32_t j = 0; j <= K; ++j) {
+    total += power;
+    power *= alpha;
+  }
+  return total;
+}
+
+double spec_alpha_from_tokens(double tokens_per_round, int32_t K) {
+  if (K < 1 || !(tokens_per_round > 1.0)) return 0.0;
+  if (tokens_per_round >= K + 1.0) return 1.0;
+  double lo = 0.0, hi = 1.0;  // spec_expected_tokens is increasing in alpha
+  for (int it = 0; it < 100; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    (spec_expected_tokens(mid, K) < tokens_per_round ? lo : hi) = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+int32_t spec_choose_k(double alpha, double t_draft_step, double t_verify, int32_t k_max) {
+  if (!(alpha >= 0.0 && alpha <= 1.0) || !(t_draft_step >= 0.0) || !(t_verify >= 0.0) ||
+      t_draft_step + t_verify <= 0.0 || k_max < 1)
+    return fail(nullptr, SPEC_ERR_ARG, "spec_choose_k: bad argument");
+  int32_t best_k = 1;
+  double best = -1.0;
+  for (int32_t K = 1; K <= k_max; ++K) {
+    const double per_time = spec_expected_tokens(alpha, K) / (K * t_draft_step + t_verify);
+    if (per_time > best) {
+      best = per_time;
+      best_k = K;
+    }
+  }
+  return best_k;
+}
+
 // -------------------------------------------------- stateless accept/reject --
 namespace {
 struct ArWorkspace {
