@@ -91,7 +91,9 @@ __global__ __launch_bounds__(kArThreads) void ar_partial_kernel(ArArgs a) {
   __shared__ int32_t s_j, s_err;
   __shared__ uint64_t s_red[4];
   const int tid = threadIdx.x;
-  const int c = blockIdx.x, b = blockIdx.y;
+  // one block per (chunk, sequence), flattened in x (grid.y is too narrow
+  // for large batches)
+  const int c = (int)(blockIdx.x % (unsigned)a.n_chunks), b = (int)(blockIdx.x / (unsigned)a.n_chunks);
   const int K = a.K, V = a.V;
   const uint64_t P = seq_pos(a, b);
   const float* Tb = a.T + (size_t)b * (K + 1) * V;
@@ -271,8 +273,10 @@ void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks) {
 }
 
 hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s) {
-  if (a.n_chunks > kArMaxChunks || a.K > 63) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ar_partial_kernel, dim3(a.n_chunks, a.B), dim3(kArThreads), 0, s, a);
+  if (a.n_chunks > kArMaxChunks || a.K > 63 || (long long)a.n_chunks * a.B > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ar_partial_kernel, dim3((unsigned)(a.n_chunks * a.B)), dim3(kArThreads), 0, s,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ar_finish_kernel, dim3(a.B), dim3(kArThreads), 0, s, a);

@@ -944,6 +944,8 @@ int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_
   HIPTRY(nullptr, hipGetDevice(&dev));
   int chunk, nch;
   ar_choose_chunks(B, V, &chunk, &nch);
+  if ((long long)B * nch > 0x7fffffffLL)
+    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: batch too large for one launch");
   const size_t words = (size_t)B * nch * ar_ws_words(K);
   std::lock_guard<std::mutex> lk(g_ar_mu);
   ArWorkspace& w = g_ar[dev];
