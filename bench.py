@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--drafter", default="model", choices=["model", "ngram"],
                     help="draft model (default) or the prompt-lookup drafter (spec_draft_ngram)")
     ap.add_argument("--ngram-n", type=int, default=3, help="longest key of the n-gram drafter")
+    ap.add_argument("--gemm-sweep", action="store_true",
+                    help="batched verify: time the weight-streaming GEMM (spec_mat_mul) on the "
+                         "8B-shaped matrices for M = B(K+1) = 1..128 rows")
     ap.add_argument("--adaptive-k", action="store_true",
                     help="choose K every few rounds from the measured acceptance rate "
                          "(spec_alpha_from_tokens + spec_choose_k) instead of a fixed K")
@@ -120,6 +123,10 @@ def main():
     import torch
     import speculative_decoding_02_amd as sd
     import synth
+
+    if args.gemm_sweep:
+        print(json.dumps(gemm_sweep(sd, torch, np)), flush=True)
+        return
 
     tcfg, dcfg = synth.PAIRS[args.pair]
     K = args.k
@@ -295,6 +302,56 @@ def main():
         res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr)
     sd.spec_destroy(ctx)
     print(json.dumps(res), flush=True)
+
+
+def gemm_sweep(sd, torch, np):
+    """Batched verify: one weight-streaming GEMM (spec_mat_mul) per shape for
+    M = B(K+1) activation rows.  Weights rotate over copies (>= 1 GB in
+    total) so every launch streams them from HBM.  Reported per M: time,
+    weight GB/s, useful TFLOP/s (2 M N K) and the matrix-core work issued
+    (16 MFMA rows per 8 activation rows, high and low parts)."""
+    shapes = {"8b gate/up": (28672, 4096), "8b down": (4096, 14336), "8b qkv": (6144, 4096)}
+    Ms = (1, 5, 8, 16, 32, 64, 96, 128)
+    res = {}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for name, (N, K) in shapes.items():
+        copies = max(2, -(-(1 << 30) // (N * K * 2)))
+        mats, keep = [], []
+        for _ in range(copies):
+            W = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            mats.append(sd.Mat(W))
+            keep.append(W)
+        del keep
+        rows = []
+        for M in Ms:
+            X = torch.randn(M, K, device="cuda", generator=g)
+            Y = torch.empty(M, N, device="cuda")
+            for m in mats:
+                m.mul(X, Y)
+            reps = 4 * copies
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                mats[i % copies].mul(X, Y)
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rt = 1
+            while 8 * rt < M:
+                rt *= 2
+            rows.append({"M": M, "us": round(us, 2),
+                         "weight_GB_s": round(N * K * 2 / (us * 1e-6) / 1e9, 1),
+                         "useful_TFLOP_s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2),
+                         "mfma_TFLOP_s": round(2 * 16 * rt * N * K / (us * 1e-6) / 1e12, 1)})
+        res[name] = rows
+        log(f"gemm sweep {name}: " + ", ".join(f"M={r['M']}: {r['us']} us" for r in rows))
+        del mats
+        torch.cuda.empty_cache()
+    return {"metric": "batched verify GEMM (spec_mat_mul) time vs activation rows M = B(K+1)",
+            "unit": "us per launch", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+            "peak_hbm_GB_s": PEAK_HBM_GBS, "peak_bf16_dense_TFLOP_s": 2500.0,
+            "config": {"workload": "8B-shaped weight matrices, M activation rows, weights cold"},
+            "sweep": res}
 
 
 def adaptive_k_run(sd, torch, ctx, stream, d, D, out, nacc, seed, args, tcfg, dcfg, plen):

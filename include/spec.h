@@ -217,6 +217,26 @@ int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out)
  * Also set at creation by spec_init_params.profile_kernels. */
 int spec_set_profiling(spec_ctx* ctx, int32_t enable);
 
+/* A packed weight matrix multiplied by a batch of activation rows: the
+ * verify pass's weight-streaming GEMM for M = B * (K+1) rows of B sequences
+ * ([en] Floor 6, "crowded tower days": with a large batch every weight read
+ * serves many rows, the work turns compute-bound and extra draft positions
+ * stop being free).  The bytes streamed do not depend on M; the matrix-core
+ * work grows with it.  Activations enter as bf16 high and low parts (as in
+ * the verify pass), products accumulate in fp32.
+ * spec_mat_create: packs W (device, bf16 [N][K], row-major; may be freed
+ * after the call) into the stream layout; N % 16 == 0, K % 32 == 0.
+ * Synchronises.  Errors: SPEC_ERR_ARG, SPEC_ERR_OOM, SPEC_ERR_HIP.
+ * spec_mat_mul: Y = X W^T with X fp32 [M][K], Y fp32 [M][N] (device,
+ * caller-owned), 1 <= M <= 128, enqueued on hip_stream (NULL: default).  The
+ * matrix owns one activation workspace: calls on one matrix must not overlap
+ * (keep them on one stream).  Errors: SPEC_ERR_ARG, SPEC_ERR_HIP.
+ * spec_mat_destroy: synchronises the device and frees; NULL accepted. */
+typedef struct spec_mat spec_mat;
+int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out);
+int spec_mat_mul(spec_mat* m, const float* X_dev, int32_t M, float* Y_dev, void* hip_stream);
+int spec_mat_destroy(spec_mat* m);
+
 /* Choosing K from the measured acceptance rate (host-side helpers; no
  * context, no device work).
  * spec_expected_tokens: mean tokens one round yields when each of its K

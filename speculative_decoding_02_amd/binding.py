@@ -71,6 +71,9 @@ def lib():
         L.spec_draft.argtypes = [_p, _i32, _u64, _p, _p]
         L.spec_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
         L.spec_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
+        L.spec_mat_create.argtypes = [_p, _i32, _i32, C.POINTER(_p)]
+        L.spec_mat_mul.argtypes = [_p, _p, _i32, _p, _p]
+        L.spec_mat_destroy.argtypes = [_p]
         L.spec_expected_tokens.argtypes = [C.c_double, _i32]
         L.spec_expected_tokens.restype = C.c_double
         L.spec_alpha_from_tokens.argtypes = [C.c_double, _i32]
@@ -97,7 +100,8 @@ def lib():
 EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
             "spec_kernel_times", "spec_set_profiling", "spec_accept_reject", "spec_expected_tokens",
-            "spec_alpha_from_tokens", "spec_choose_k")
+            "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
+            "spec_mat_destroy")
 
 
 def _check(rc: int, ctx=None):
@@ -163,6 +167,40 @@ def spec_draft(ctx: Ctx, K: int, seed: int, d, D) -> None:
 
 def spec_draft_ngram(ctx: Ctx, K: int, n_max: int, d, D=None) -> None:
     _check(lib().spec_draft_ngram(ctx.handle, K, n_max, _ptr(d), _ptr(D)), ctx)
+
+
+def spec_mat_create(W) -> int:
+    """Packs a contiguous 2-D bf16 device tensor W [N][K]; returns the handle."""
+    import torch
+    if W.dtype != torch.bfloat16 or not W.is_cuda or not W.is_contiguous() or W.dim() != 2:
+        raise ValueError("W must be a contiguous 2-D bf16 device tensor")
+    h = _p()
+    _check(lib().spec_mat_create(W.data_ptr(), W.shape[0], W.shape[1], C.byref(h)))
+    return h.value
+
+
+def spec_mat_mul(handle: int, X, Y, stream: int = 0) -> None:
+    _check(lib().spec_mat_mul(handle, _ptr(X), X.shape[0], _ptr(Y), stream))
+
+
+def spec_mat_destroy(handle: int) -> None:
+    _check(lib().spec_mat_destroy(handle))
+
+
+class Mat:
+    """A packed weight matrix (spec_mat) for batched-row products."""
+
+    def __init__(self, W):
+        self.handle = spec_mat_create(W)
+        self.N, self.K = W.shape
+
+    def mul(self, X, Y, stream: int = 0) -> None:
+        spec_mat_mul(self.handle, X, Y, stream)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            spec_mat_destroy(self.handle)
+            self.handle = None
 
 
 def spec_expected_tokens(alpha: float, K: int) -> float:

@@ -151,6 +151,18 @@ void ar_choose_chunks(int B, int V, int* chunk, int* n_chunks);
 // Two launches: chunk partials, then one finishing block per sequence.
 hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
 
+// --------------------------------------------- GEMM for a batch of rows --
+constexpr int kRowsMaxM = 128;  // 16 row tiles of 8 activation rows (hi/lo)
+struct RowsGemmArgs {
+  const uint16_t* Wp;     // packed weights (launch_pack layout, NB = nb)
+  int N, K, nb;
+  const float* X;         // [M][K] fp32 activations
+  int M;
+  uint16_t* A;            // workspace: [K/32][ceil(M/8) rounded to a power of 2][64][8] bf16
+  float* Y;               // [M][N] fp32
+};
+hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s);
+
 // ------------------------------------------------------ n-gram drafter --
 constexpr int kNgramMaxN = 8;   // longest key searched
 constexpr int kNgramMaxK = 8;   // drafts per call (>= SPEC_K_MAX)

@@ -881,6 +881,69 @@ int spec_set_profiling(spec_ctx* c, int32_t enable) {
   return SPEC_OK;
 }
 
+// ------------------------------------------- packed matrix, batched rows --
+struct spec_mat {
+  int device = 0;
+  int N = 0, K = 0, nb = 1;
+  uint16_t* Wp = nullptr;
+  uint16_t* A = nullptr;  // activation workspace for up to kRowsMaxM rows
+};
+
+int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
+  if (!out) return fail(nullptr, SPEC_ERR_ARG, "spec_mat_create: null output");
+  *out = nullptr;
+  if (!W_dev || N < 16 || K < 32 || N % 16 || K % 32)
+    return fail(nullptr, SPEC_ERR_ARG, "spec_mat_create: need N % 16 == 0, K % 32 == 0");
+  spec_mat* m = new spec_mat();
+  m->N = N;
+  m->K = K;
+  const GemmPlan plan = plan_gemm(N, 1, K);
+  m->nb = plan.shape.nb;
+  hipError_t e = hipGetDevice(&m->device);
+  std::vector<const uint16_t*> rows(N);
+  for (int n = 0; n < N; ++n) rows[n] = (const uint16_t*)W_dev + (size_t)n * K;
+  const uint16_t** drows = nullptr;
+  if (e == hipSuccess) e = dalloc(&m->Wp, (size_t)N * K);
+  if (e == hipSuccess) e = dalloc(&m->A, (size_t)(K / 32) * (kRowsMaxM / 8) * 64 * 8);
+  if (e == hipSuccess) e = dalloc(&drows, (size_t)N);
+  if (e == hipSuccess)
+    e = hipMemcpy(drows, rows.data(), (size_t)N * sizeof(void*), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = launch_pack(drows, K, m->nb, N / (16 * m->nb), m->Wp, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipFree(drows);
+  if (e != hipSuccess) {
+    (void)hipFree(m->Wp);
+    (void)hipFree(m->A);
+    delete m;
+    return fail(nullptr, e == hipErrorOutOfMemory ? SPEC_ERR_OOM : SPEC_ERR_HIP,
+                fmt("spec_mat_create: %s", hipGetErrorString(e)));
+  }
+  *out = m;
+  return SPEC_OK;
+}
+
+int spec_mat_mul(spec_mat* m, const float* X_dev, int32_t M, float* Y_dev, void* hip_stream) {
+  if (!m || !X_dev || !Y_dev) return fail(nullptr, SPEC_ERR_ARG, "spec_mat_mul: null argument");
+  if (M < 1 || M > kRowsMaxM)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("spec_mat_mul: M=%d outside 1..%d", M, kRowsMaxM));
+  RowsGemmArgs a{};
+  a.Wp = m->Wp; a.N = m->N; a.K = m->K; a.nb = m->nb;
+  a.X = X_dev; a.M = M; a.A = m->A; a.Y = Y_dev;
+  HIPTRY(nullptr, hipSetDevice(m->device));
+  HIPTRY(nullptr, launch_gemm_rows(a, (hipStream_t)hip_stream));
+  return SPEC_OK;
+}
+
+int spec_mat_destroy(spec_mat* m) {
+  if (!m) return SPEC_OK;
+  (void)hipSetDevice(m->device);
+  (void)hipDeviceSynchronize();
+  (void)hipFree(m->Wp);
+  (void)hipFree(m->A);
+  delete m;
+  return SPEC_OK;
+}
+
 // ---------------------------------------------------------- choosing K --
 // [en] Floor 6: mean tokens per round with iid acceptance; [int] "speedup":
 // a round costs K draft steps plus one target pass.

@@ -1,0 +1,58 @@
+"""GPU parity of the batched-row weight-streaming GEMM (spec_mat_create /
+spec_mat_mul): Y = X W^T for M = 1..128 activation rows (B sequences' K+1
+verify rows), against numpy's fp64 product of the same bf16 weights.
+
+The bound is the arithmetic's own: activations enter as bf16 high and low
+parts (|x - hi - lo| <= 2^-17 |x|), bf16 x bf16 products are exact in fp32,
+and fp32 accumulation over K terms (plus the split-K and hi/lo sums) adds at
+most (K + 8) 2^-24 of sum |x w| -- so every output must satisfy
+|y - ref| <= (2^-16 + (K + 8) 2^-24) * sum_k |x_k w_nk|."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _case(N, K, Ms, seed):
+    import speculative_decoding_02_amd as sd
+    g = torch.Generator().manual_seed(seed)
+    W = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
+    Wd = W.cuda().contiguous()
+    mat = sd.Mat(Wd)
+    W64 = W.to(torch.float64).numpy()
+    for M in Ms:
+        X = torch.randn(M, K, generator=g, dtype=torch.float32)
+        Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        mat.mul(X.cuda(), Y)
+        torch.cuda.synchronize()
+        y = Y.cpu().numpy().astype(np.float64)
+        X64 = X.numpy().astype(np.float64)
+        ref = X64 @ W64.T
+        bound = (2.0 ** -16 + (K + 8) * 2.0 ** -24) * (np.abs(X64) @ np.abs(W64).T)
+        err = np.abs(y - ref)
+        assert np.all(np.isfinite(y)), M
+        assert np.all(err <= bound), (M, float((err / bound).max()))
+
+
+def test_rows_narrow():
+    _case(512, 1024, [1, 5, 8, 9, 16, 31, 64, 100, 128], seed=1)
+
+
+def test_rows_wide_two_blocks_per_workgroup():
+    _case(12288, 512, [1, 7, 33, 128], seed=2)
+
+
+def test_rows_errors():
+    import speculative_decoding_02_amd as sd
+    W = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    mat = sd.Mat(W)
+    Y = torch.zeros(129, 64, device="cuda")
+    for M in (0, 129):
+        X = torch.zeros(max(M, 1), 64, device="cuda")
+        with pytest.raises(sd.SpecError) as e:
+            sd.spec_mat_mul(mat.handle, X[:M] if M else X[:0], Y)
+        assert e.value.code == sd.SPEC_ERR_ARG
+    with pytest.raises(sd.SpecError) as e:
+        sd.spec_mat_create(torch.zeros(24, 64, dtype=torch.bfloat16, device="cuda"))
+    assert e.value.code == sd.SPEC_ERR_ARG
