@@ -109,6 +109,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--kernel-rounds", type=int, default=5)
+    ap.add_argument("--plain-steps", type=int, default=40,
+                    help="plain decode steps (verify with K = 0) timed after the rounds")
+    ap.add_argument("--ceiling-gib", type=int, default=16,
+                    help="buffer size of the streaming-read ceiling (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run a plain copy of 1 GiB three times (calibrates HBM counters)")
     args = ap.parse_args()
@@ -132,7 +136,7 @@ def main():
     K = args.k
     plen = args.prompt_len or {"toy": 32, "1.3b": 512, "8b": 1024, "31b": 2048}[args.pair]
     rounds_total = args.steps + args.warmup
-    max_seq = plen + (K + 1) * (rounds_total + args.kernel_rounds) + 16
+    max_seq = plen + (K + 1) * (rounds_total + args.kernel_rounds) + args.plain_steps + 24
     torch.cuda.set_device(0)
     if args.copy_calib:
         # a plain elementwise copy (negation): COPY_CALIB_BYTES read and written per launch
@@ -257,6 +261,57 @@ def main():
                 "draft_launch_us": round(float(kt_d.mean()) * 1e3, 2),
                 "draft_GBs": round(gateup_bytes(dcfg, 1) / (float(kt_d.mean()) / 1e3) / 1e9, 1)}
 
+    # acceptance record of the timed rounds: the context counts every commit
+    # by (K, n_acc); alpha_i = P(d_i accepted | d_1..d_{i-1} accepted)
+    acc = st1["accept_counts"][K] - st0["accept_counts"][K]
+    reach = [int(acc[i:].sum()) for i in range(K + 1)]
+    acceptance = {"rounds": reach[0],
+                  "n_acc_histogram": [int(x) for x in acc[: K + 1]],
+                  "alpha_per_position": [round(reach[i + 1] / reach[i], 4) if reach[i] else None
+                                         for i in range(K)]}
+
+    # plain decoding on the same kernels: verify with K = 0 (one row, the
+    # next token from T_1) and commit, back to back
+    plain = None
+    if args.plain_steps > 0:
+        pout = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pn = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def plain_step():
+            sd.spec_verify(ctx, 0, seed, None, None, pout, pn)
+            sd.spec_commit(ctx, pout, pn)
+
+        for _ in range(3):
+            plain_step()
+        sd.spec_sync(ctx)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(args.plain_steps):
+            plain_step()
+        p1.record(stream)
+        sd.spec_sync(ctx)
+        assert sd.spec_get_state(ctx)["device_error"] == 0
+        pms = p0.elapsed_time(p1) / args.plain_steps
+        pbytes = verify_pass_bytes(tcfg, 0, L_mid)
+        plain = {"steps": args.plain_steps, "ms_per_token": round(pms, 4),
+                 "tokens_per_s": round(1e3 / pms, 2),
+                 "one_row_pass_GB_s": round(pbytes / (pms / 1e3) / 1e9, 1)}
+
+    # streaming-read ceiling over a buffer far larger than the 256 MB MALL
+    ceiling = None
+    if args.ceiling_gib > 0:
+        buf = torch.zeros(args.ceiling_gib << 30, dtype=torch.uint8, device="cuda")
+        c_gbs = sd.spec_read_ceiling(buf, reps=2)
+        del buf
+        torch.cuda.empty_cache()
+        ceiling = {"GB_s": round(c_gbs, 1), "bytes": args.ceiling_gib << 30,
+                   "frac_of_peak": round(c_gbs / PEAK_HBM_GBS, 4),
+                   "verify_frac_of_ceiling": round(vgbs / c_gbs, 4),
+                   "roofline_frac_of_ceiling": round(roof["achieved"] / c_gbs, 4) if roof else None}
+
+    proj = {f"alpha_{a}": round(sd.spec_expected_tokens(a, K)
+                                / ((np.median(draft_ms) + np.median(verify_ms)) / 1e3), 1)
+            for a in (0.5, 0.7, 0.8)}
     res = {
         "metric": "accepted tokens/s at batch 1, K=4; verify-pass HBM GB/s as % of MI355X peak",
         "value": round(tok_per_s, 2),
@@ -286,11 +341,14 @@ def main():
         "tokens_per_round": round(tpr, 4),
         # what the measured round time would give at the acceptance rates of
         # the pages' examples ([en] Floor 6): a projection, not a measurement
-        "projection_tokens_per_s": {
-            f"alpha_{a}": round(sd.spec_expected_tokens(a, K)
-                                / ((np.median(draft_ms) + np.median(verify_ms)) / 1e3), 1)
-            for a in (0.5, 0.7, 0.8)},
+        "projection_tokens_per_s": proj,
+        "projection_speedup_vs_plain": ({k: round(v / plain["tokens_per_s"], 3) for k, v in proj.items()}
+                                        if plain else None),
         "target_passes_per_token": round(args.steps / max(tokens, 1), 4),
+        "acceptance": acceptance,
+        "plain_decode": plain,
+        "speedup_vs_plain": round(tok_per_s / plain["tokens_per_s"], 4) if plain else None,
+        "read_ceiling": ceiling,
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
         "cpu_baseline": None,

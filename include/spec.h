@@ -149,7 +149,10 @@ int spec_draft_ngram(spec_ctx* ctx, int32_t K, int32_t n_max, int32_t* d_dev, fl
  * the lowest-index argmax of T_i; the first mismatch emits that argmax; the
  * bonus is the argmax of T_{K+1}.  Drafts may come from any source: D rows
  * are only read in sampling mode (one-hot rows describe a deterministic
- * drafter).
+ * drafter).  K = 0 is one step of plain decoding with the same kernels: a
+ * one-row pass over the pending token and the next token drawn from T_1 (w2
+ * at its position, or the argmax in greedy mode); d_dev and D_dev are not
+ * read and may be NULL.
  *   d_dev: int32 [K]; D_dev: fp32 [K][vocab] (may be NULL in greedy mode);
  *   out_dev: int32 [K+1] receives the n_acc+1 emitted tokens, -1 after them;
  *   n_acc_dev: int32 [1] receives n_acc in 0..K, or -1 if an input that the
@@ -157,8 +160,8 @@ int spec_draft_ngram(spec_ctx* ctx, int32_t K, int32_t n_max, int32_t* d_dev, fl
  *   draft id outside [0, vocab)) -- then out_dev is all -1;
  *   T_dev (nullable): fp32 [K+1][vocab] receives the target rows;
  *   logits_dev (nullable): fp32 [K+1][vocab] receives the target logits.
- * Errors: SPEC_ERR_ARG, SPEC_ERR_CAPACITY (L+K+1 > max_seq), SPEC_ERR_STATE
- * (a verify is already awaiting its commit). */
+ * Errors: SPEC_ERR_ARG (K outside 0..k_max, null pointers), SPEC_ERR_CAPACITY
+ * (L+K+1 > max_seq), SPEC_ERR_STATE (a verify is already awaiting its commit). */
 int spec_verify(spec_ctx* ctx, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
                 int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev);
 
@@ -190,6 +193,11 @@ typedef struct spec_state {
   int32_t draft_len;    /* tokens in the draft KV cache */
   int32_t pending;      /* pending token id */
   int32_t device_error; /* sticky device-side error bits (0 = none) */
+  /* acceptance record: accept_counts[K][n] = committed verifies of K drafts
+   * that accepted n of them (K = 0 counts plain decode steps).  The number of
+   * accepted tokens per round and the per-position acceptance rates of the
+   * pages' analysis ([int] "how many tokens per round") follow from it. */
+  int32_t accept_counts[SPEC_K_MAX + 1][SPEC_K_MAX + 1];
 } spec_state;
 
 /* Synchronises and reads the device-side state. */
@@ -253,6 +261,15 @@ int spec_mat_destroy(spec_mat* m);
 double spec_expected_tokens(double alpha, int32_t K);
 double spec_alpha_from_tokens(double tokens_per_round, int32_t K);
 int32_t spec_choose_k(double alpha, double t_draft_step, double t_verify, int32_t k_max);
+
+/* Measurement helper, not a step of the method: the rate of a plain streaming
+ * read (16-byte non-temporal loads, nothing else), the HBM ceiling that the
+ * verify pass's GB/s is set against.  Reads bytes (a multiple of 16, at least
+ * 1 MiB) of buf_dev reps times at each of three grid sizes and returns the
+ * best rate in GB/s (1e9 bytes/s), timed with HIP events on hip_stream.
+ * Synchronises the stream.  Errors: SPEC_ERR_ARG, SPEC_ERR_HIP. */
+int spec_read_ceiling(const void* buf_dev, uint64_t bytes, int32_t reps, void* hip_stream,
+                      double* gb_per_s);
 
 /* Stateless accept/reject over a batch of independent sequences (the rule of
  * spec_verify without the forward pass).

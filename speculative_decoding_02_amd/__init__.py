@@ -7,5 +7,5 @@ from .binding import (  # noqa: F401
     spec_init, spec_draft, spec_draft_ngram, spec_verify, spec_commit, spec_destroy, spec_last_error, spec_sync,
     spec_stream, spec_get_state, spec_get_history, spec_kernel_times, spec_set_profiling,
     spec_accept_reject, spec_expected_tokens, spec_alpha_from_tokens, spec_choose_k,
-    spec_mat_create, spec_mat_mul, spec_mat_destroy,
+    spec_mat_create, spec_mat_mul, spec_mat_destroy, spec_read_ceiling,
 )

@@ -53,9 +53,12 @@ class SpecInitParams(C.Structure):
     ]
 
 
+K_BINS = 8  # SPEC_K_MAX + 1
+
+
 class SpecState(C.Structure):
     _fields_ = [("target_len", _i32), ("draft_len", _i32), ("pending", _i32),
-                ("device_error", _i32)]
+                ("device_error", _i32), ("accept_counts", (_i32 * K_BINS) * K_BINS)]
 
 
 _lib = None
@@ -93,6 +96,7 @@ def lib():
         L.spec_set_profiling.argtypes = [_p, _i32]
         L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
                                          _p, _p]
+        L.spec_read_ceiling.argtypes = [_p, _u64, _i32, _p, C.POINTER(C.c_double)]
         _lib = L
     return _lib
 
@@ -101,7 +105,7 @@ EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_verify", "spec_
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
             "spec_kernel_times", "spec_set_profiling", "spec_accept_reject", "spec_expected_tokens",
             "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
-            "spec_mat_destroy")
+            "spec_mat_destroy", "spec_read_ceiling")
 
 
 def _check(rc: int, ctx=None):
@@ -248,8 +252,10 @@ def spec_stream(ctx: Ctx) -> int:
 def spec_get_state(ctx: Ctx) -> dict:
     s = SpecState()
     _check(lib().spec_get_state(ctx.handle, C.byref(s)), ctx)
+    counts = np.array([[s.accept_counts[k][n] for n in range(K_BINS)] for k in range(K_BINS)],
+                      np.int64)
     return {"target_len": s.target_len, "draft_len": s.draft_len, "pending": s.pending,
-            "device_error": s.device_error}
+            "device_error": s.device_error, "accept_counts": counts}
 
 
 def spec_get_history(ctx: Ctx, n: int) -> np.ndarray:
@@ -267,6 +273,15 @@ def spec_kernel_times(ctx: Ctx, cap: int = 4096) -> np.ndarray:
 
 def spec_set_profiling(ctx: Ctx, enable: bool) -> None:
     _check(lib().spec_set_profiling(ctx.handle, int(bool(enable))), ctx)
+
+
+def spec_read_ceiling(buf, reps: int = 3, stream: int = 0) -> float:
+    """Streaming-read rate (GB/s) over the device tensor buf (measurement
+    helper: the HBM ceiling the verify pass is set against)."""
+    gbs = C.c_double(0.0)
+    _check(lib().spec_read_ceiling(_ptr(buf), buf.numel() * buf.element_size(), reps,
+                                   stream or None, C.byref(gbs)))
+    return gbs.value
 
 
 def spec_accept_reject(T, D, d, seed: int, pos, stream_id: int, greedy: bool, out, n_acc,

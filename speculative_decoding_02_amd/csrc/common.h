@@ -21,11 +21,14 @@ enum : int32_t {
 };
 
 // Device-resident decoding state (one per context).
+constexpr int kAcceptBins = kMaxRows;  // K = 0..7, n_acc = 0..7
 struct DevState {
   int32_t LT;        // tokens in the target cache; hist[LT] is the pending token
   int32_t LD;        // tokens in the draft cache
   int32_t err;       // sticky error bits
   int32_t pad;
+  // committed verifies by (K, n_acc): the acceptance record of the context
+  int32_t accept_counts[kAcceptBins][kAcceptBins];
 };
 
 // Row descriptor of one forward pass, written by the embedding kernel and

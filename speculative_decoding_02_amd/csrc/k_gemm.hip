@@ -42,7 +42,7 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
 template <int NB, int W, int EPI>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   constexpr int YW = NB * 16;            // columns owned by the workgroup
-  constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : 4);  // k-blocks per batch of loads
+  constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : (NB <= 4 ? 4 : 2));  // k-blocks per batch
   __shared__ float s_red[W * NB * 256];
   __shared__ float s_y[kMaxRows * YW];
   __shared__ float s_scale[kMaxRows];
@@ -252,19 +252,18 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
       a.ssq_out[g * kMaxRows + tid] = s;
     }
   } else if constexpr (EPI == EPI_SILU) {
-    static_assert(NB % 2 == 0, "gate/up epilogue pairs blocks");
-    // blocks 2p / 2p+1 hold gate / up of features (g*NB/2 + p)*16 + 0..15
+    // block b = g*NB + j: columns 0-7 are the gate and 8-15 the up outputs of
+    // features 8b .. 8b+7
     for (int idx = tid; idx < n_rows * NB; idx += W * 64) {
-      const int m = idx / NB, rest = idx % NB;
-      const int p = rest >> 1, half = rest & 1;
+      const int m = idx / NB, j = idx % NB;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float gt = s_y[m * YW + (2 * p) * 16 + half * 8 + e];
-        const float up = s_y[m * YW + (2 * p + 1) * 16 + half * 8 + e];
+        const float gt = s_y[m * YW + j * 16 + e];
+        const float up = s_y[m * YW + j * 16 + 8 + e];
         v[e] = gt / (1.0f + expf(-gt)) * up;
       }
-      apack_store8(a.Ap_out, m, (g * (NB / 2) + p) * 16 + half * 8, v);
+      apack_store8(a.Ap_out, m, (g * NB + j) * 8, v);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
@@ -327,12 +326,7 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID>), grid, block, 0, s, a); break;
     case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV>), grid, block, 0, s, a); break;
     case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS>), grid, block, 0, s, a); break;
-    case EPI_SILU:
-      if constexpr (NB % 2 == 0) {
-        hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a);
-        break;
-      }
-      return hipErrorInvalidValue;
+    case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -347,6 +341,7 @@ hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) 
     if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s);
     if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s);
     if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s);
+    if (sh.nb == 7) return launch_epi<7, 8>(epi, a, s);
   }
   return hipErrorInvalidValue;
 }

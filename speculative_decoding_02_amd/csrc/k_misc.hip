@@ -153,11 +153,12 @@ hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, int n_rows, hipStr
 // after the first reject are torn up).  The draft cache keeps the rows whose
 // tokens were committed: it processed [pending, d_1..d_{K-1}], so it is
 // valid up to position LT + min(n, K-1).
+// The verify's (K, n_acc) pair is counted in the state's acceptance record.
 __global__ void commit_kernel(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                              const int32_t* n_acc, int drafted_k) {
+                              const int32_t* n_acc, int drafted_k, int verified_k) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   const int n = *n_acc;
-  if (n < 0) return;
+  if (n < 0 || n > verified_k) return;
   const int LT = st->LT;
   if (LT + 1 + n >= hist_cap) {
     atomicOr(&st->err, kErrCapacity);
@@ -166,12 +167,47 @@ __global__ void commit_kernel(DevState* st, int32_t* hist, int hist_cap, const i
   for (int i = 0; i <= n; ++i) hist[LT + 1 + i] = out[i];
   if (drafted_k > 0) st->LD = LT + (n + 1 < drafted_k ? n + 1 : drafted_k);
   st->LT = LT + n + 1;
+  st->accept_counts[verified_k][n] += 1;
 }
 
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                         const int32_t* n_acc, int drafted_k, hipStream_t s) {
+                         const int32_t* n_acc, int drafted_k, int verified_k, hipStream_t s) {
+  if (verified_k < 0 || verified_k >= kAcceptBins) return hipErrorInvalidValue;
   hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, st, hist, hist_cap, out, n_acc,
-                     drafted_k);
+                     drafted_k, verified_k);
+  return hipGetLastError();
+}
+
+// ============================================================ read ceiling ==
+// Plain streaming read of a buffer (16-byte non-temporal loads, four in
+// flight per thread, grid-stride): the HBM read rate a kernel that does
+// nothing else reaches, against which the verify pass's rate is read.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* p, size_t n, uint32_t* sink) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4_t v0 = __builtin_nontemporal_load((const u32x4_t*)(p + i));
+    const u32x4_t v1 = __builtin_nontemporal_load((const u32x4_t*)(p + i + stride));
+    const u32x4_t v2 = __builtin_nontemporal_load((const u32x4_t*)(p + i + 2 * stride));
+    const u32x4_t v3 = __builtin_nontemporal_load((const u32x4_t*)(p + i + 3 * stride));
+    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
+    acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // the data must be used; this store almost never happens
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
+                              hipStream_t s) {
+  if (bytes % 16 || grid < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)buf, bytes / 16,
+                     sink);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ enum Epi : int {
   EPI_STORE = 0,   // out[m][n] = y (fp32)
   EPI_RESID = 1,   // resid[m][n] += y; packed (resid * gain_next) for the next GEMM;
                    // per-workgroup sums of squares for the next RMSNorm
-  EPI_SILU = 2,    // packed silu(gate) * up for the down projection (blocks alternate gate/up)
+  EPI_SILU = 2,    // packed silu(gate) * up for the down projection (8 gate, 8 up columns per block)
   EPI_QKV = 3,     // RoPE on q/k; q -> attention query fragments, k/v -> paged KV cache
   EPI_LOGITS = 4,  // out[m][n] = logit; per-workgroup (max, sum exp) partials
 };
@@ -178,7 +178,10 @@ hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- commit --
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                         const int32_t* n_acc, int drafted_k, hipStream_t s);
+                         const int32_t* n_acc, int drafted_k, int verified_k, hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16) with `grid` blocks of 256.
+hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
+                              hipStream_t s);
 // RoPE table: (cos, sin) of p * theta^(-2j/hd) for p < max_seq, j < hd/2,
 // evaluated in fp64 and stored as fp32.
 hipError_t launch_rope_table(float2* dst, int max_seq, int hd, double theta, hipStream_t s);

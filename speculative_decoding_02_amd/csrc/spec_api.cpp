@@ -43,17 +43,31 @@ struct GemmPlan {
   int n_groups = 0, Kb = 0;
 };
 
-// Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4} and
-// waves in {4,8,16}, weights cold): two blocks per workgroup once that still
-// leaves >= 192 workgroups (fewer, longer workgroups stream better than
-// many short ones above that count, worse below it); four waves (more
-// workgroups resident per CU), except for narrow matrices with a long K,
-// where only eight waves per workgroup keep enough loads in flight.
-GemmPlan plan_gemm(int n_cols, int nb_min, int K) {
+// Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4,7} and
+// waves in {4,8,16}, weights cold, with per-workgroup start/end stamps).
+// A streaming GEMM is fastest when every CU gets the same number of weight
+// bytes and all its workgroups are resident from the start: waves of one CU
+// are served oldest first, so on CUs holding one workgroup more than others
+// the last one streams alone at the end (896 gate/up workgroups of the 8B
+// shape end between 14 and 39 us; 256 workgroups of 7 blocks all end
+// together, 37.0 instead of 40.1 us).  So when the column blocks divide
+// evenly over the CUs (n_cu > 0) a workgroup takes n_blocks / n_cu of them
+// (up to 7, eight waves from four blocks on).  Otherwise: two blocks per
+// workgroup once that still leaves >= 192 workgroups, four waves, except
+// for narrow matrices with a long K, where only eight waves per workgroup
+// keep enough loads in flight.
+GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu) {
   GemmPlan p;
   const int n_blocks = n_cols / 16;
-  p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
   p.Kb = K / 32;
+  const int q = n_cu > 0 && n_blocks % n_cu == 0 ? n_blocks / n_cu : 0;
+  if ((q == 2 || q == 4 || q == 7) && q >= nb_min) {
+    p.shape.nb = q;
+    p.n_groups = n_cu;
+    p.shape.waves = q >= 4 ? 8 : 4;
+    return p;
+  }
+  p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
   p.n_groups = n_blocks / p.shape.nb;
   p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
   return p;
@@ -221,17 +235,19 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   m.qd = m.nq * m.hd; m.kvd = m.nkv * m.hd;
   m.theta = md.rope_theta; m.eps = md.rms_eps;
   const int L = m.L, d = m.d;
-  auto mk = [](int N, int nb, int K) {
+  int n_cu = 0;
+  HIPTRY(c, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
+  auto mk = [n_cu](int N, int K) {
     Mat x;
     x.N = N; x.K = K;
-    x.plan = plan_gemm(N, nb, K);
+    x.plan = plan_gemm(N, 1, K, n_cu);
     return x;
   };
-  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, 1, d));
-  m.o.assign(L, mk(d, 1, m.qd));
-  m.gu.assign(L, mk(2 * m.F, 2, d));
-  m.dn.assign(L, mk(d, 1, m.F));
-  m.lm = mk(m.V, 1, d);
+  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, d));
+  m.o.assign(L, mk(d, m.qd));
+  m.gu.assign(L, mk(2 * m.F, d));
+  m.dn.assign(L, mk(d, m.F));
+  m.lm = mk(m.V, d);
   m.lm_shared = share_from && share_desc && md.lm_head == share_desc->lm_head &&
                 md.d_model == share_desc->d_model && md.vocab == share_desc->vocab;
   m.embed_shared = share_from && share_desc && md.embed == share_desc->embed &&
@@ -281,18 +297,12 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
     rows.assign((size_t)m.o[l].plan.n_groups * m.o[l].plan.shape.nb * 16, nullptr);
     for (int n = 0; n < d; ++n) rows[n] = wo + ((size_t)l * d + n) * m.qd;
     if (int r = pack_rows(c, rows, m.o[l])) return r;
-    // gate/up: within a group of nb blocks, block 2p holds gate rows and
-    // block 2p+1 the up rows of the same 16 features (g*nb/2 + p)*16 + w
-    {
-      const int nbg = m.gu[l].plan.shape.nb;
-      rows.assign((size_t)m.gu[l].plan.n_groups * nbg * 16, nullptr);
-      for (int g = 0; g < m.gu[l].plan.n_groups; ++g)
-        for (int p2 = 0; p2 < nbg / 2; ++p2)
-          for (int w = 0; w < 16; ++w) {
-            const size_t f = (size_t)(g * (nbg / 2) + p2) * 16 + w;
-            rows[(size_t)(g * nbg + 2 * p2) * 16 + w] = wg + ((size_t)l * m.F + f) * d;
-            rows[(size_t)(g * nbg + 2 * p2 + 1) * 16 + w] = wu + ((size_t)l * m.F + f) * d;
-          }
+    // gate/up: 16-column block b holds the gate rows of features 8b..8b+7
+    // in its columns 0-7 and the up rows of the same features in 8-15
+    rows.assign((size_t)m.gu[l].plan.n_groups * m.gu[l].plan.shape.nb * 16, nullptr);
+    for (int n = 0; n < 2 * m.F; ++n) {
+      const size_t f = (size_t)(n / 16) * 8 + (n % 8);
+      rows[n] = ((n % 16) < 8 ? wg : wu) + ((size_t)l * m.F + f) * d;
     }
     if (int r = pack_rows(c, rows, m.gu[l])) return r;
     rows.assign((size_t)m.dn[l].plan.n_groups * m.dn[l].plan.shape.nb * 16, nullptr);
@@ -689,7 +699,7 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   TRYH(hipMemsetAsync(c->x, 0, (size_t)kMaxRows * dmax * 4, c->stream));
   TRYH(hipMemsetAsync(c->hist, 0, (size_t)c->hist_cap * 4, c->stream));
   TRYH(hipMemcpyAsync(c->hist, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, c->stream));
-  DevState hs{0, 0, 0, 0};
+  DevState hs{};
   TRYH(hipMemcpyAsync(c->st, &hs, sizeof hs, hipMemcpyHostToDevice, c->stream));
   TRYH(hipStreamSynchronize(c->stream));
 
@@ -762,9 +772,10 @@ int spec_draft_ngram(spec_ctx* c, int32_t K, int32_t n_max, int32_t* d_dev, floa
 int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
                 int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev) {
   if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_verify: null context");
-  if (K < 1 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..k_max", K));
-  if (!d_dev || !out_dev || !n_acc_dev || (!D_dev && !c->p.greedy))
+  if (K < 0 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 0..k_max", K));
+  if (!out_dev || !n_acc_dev || (K > 0 && (!d_dev || (!D_dev && !c->p.greedy))))
     return fail(c, SPEC_ERR_ARG, "spec_verify: null argument");
+  if (K == 0) d_dev = nullptr, D_dev = nullptr;  // not read: a plain decode step
   if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_verify: previous verify not committed");
   HIPTRY(c, hipSetDevice(c->device));
   if (c->LT_ub + K + 1 > c->p.max_seq) {
@@ -799,7 +810,8 @@ int spec_commit(spec_ctx* c, const int32_t* out_dev, const int32_t* n_acc_dev) {
   if (!out_dev || !n_acc_dev) return fail(c, SPEC_ERR_ARG, "spec_commit: null argument");
   if (!c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_commit: no verify pending");
   HIPTRY(c, hipSetDevice(c->device));
-  HIPTRY(c, launch_commit(c->st, c->hist, c->hist_cap, out_dev, n_acc_dev, c->drafted_k, c->stream));
+  HIPTRY(c, launch_commit(c->st, c->hist, c->hist_cap, out_dev, n_acc_dev, c->drafted_k, c->last_k,
+                         c->stream));
   c->LT_ub += c->last_k + 1;
   c->lag_ub = c->drafted_k > 0 ? 1 : c->lag_ub + c->last_k + 1;
   c->drafted_k = 0;
@@ -833,6 +845,9 @@ int spec_get_state(spec_ctx* c, spec_state* out) {
   out->draft_len = hs.LD;
   out->pending = pend;
   out->device_error = hs.err;
+  static_assert(kAcceptBins == SPEC_K_MAX + 1, "acceptance record covers K = 0..SPEC_K_MAX");
+  for (int k = 0; k < kAcceptBins; ++k)
+    for (int n = 0; n < kAcceptBins; ++n) out->accept_counts[k][n] = hs.accept_counts[k][n];
   return SPEC_OK;
 }
 
@@ -897,7 +912,7 @@ int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
   spec_mat* m = new spec_mat();
   m->N = N;
   m->K = K;
-  const GemmPlan plan = plan_gemm(N, 1, K);
+  const GemmPlan plan = plan_gemm(N, 1, K, 0);  // the rows GEMM takes nb 1 or 2
   m->nb = plan.shape.nb;
   hipError_t e = hipGetDevice(&m->device);
   std::vector<const uint16_t*> rows(N);
@@ -1027,6 +1042,39 @@ int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_
   a.greedy = greedy; a.word = 2; a.chunk = chunk; a.n_chunks = nch;
   a.out = out_dev; a.n_acc = n_acc_dev; a.ws = w.ws;
   HIPTRY(nullptr, launch_accept_reject(a, s));
+  return SPEC_OK;
+}
+
+int spec_read_ceiling(const void* buf_dev, uint64_t bytes, int32_t reps, void* hip_stream,
+                      double* gb_per_s) {
+  if (!buf_dev || !gb_per_s || bytes < (1u << 20) || bytes % 16 || reps < 1)
+    return fail(nullptr, SPEC_ERR_ARG, "spec_read_ceiling: bad argument");
+  hipStream_t s = (hipStream_t)hip_stream;
+  int dev = 0, n_cu = 0;
+  HIPTRY(nullptr, hipGetDevice(&dev));
+  HIPTRY(nullptr, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  uint32_t* sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = dalloc(&sink, 1);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  double best = 0.0;
+  for (int mult : {4, 8, 16}) {
+    const int grid = n_cu * mult;
+    if (e == hipSuccess) e = launch_stream_read(buf_dev, bytes, grid, sink, s);  // warm-up
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch_stream_read(buf_dev, bytes, grid, sink, s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess && ms > 0.f) best = std::max(best, (double)bytes * reps / (ms * 1e-3) / 1e9);
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
+  HIPTRY(nullptr, e);
+  *gb_per_s = best;
   return SPEC_OK;
 }
 

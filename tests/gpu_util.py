@@ -42,6 +42,16 @@ class Buffers:
         self.nacc = torch.zeros(1, dtype=torch.int32, device="cuda")
 
 
+def gpu_plain_step(sd, ctx, seed, b: Buffers):
+    """One plain decode step through the same boundary: verify with K = 0
+    (no drafts) and commit."""
+    sd.spec_verify(ctx, 0, seed, None, None, b.out, b.nacc, b.T, b.logits)
+    sd.spec_commit(ctx, b.out, b.nacc)
+    sd.spec_sync(ctx)
+    return {"out": b.out.cpu().numpy().copy(), "nacc": int(b.nacc.cpu().numpy()[0]),
+            "T": b.T.cpu().numpy().copy(), "logits": b.logits.cpu().numpy().copy()}
+
+
 def gpu_round(sd, ctx, K, seed, b: Buffers, with_rows=True):
     sd.spec_draft(ctx, K, seed, b.d, b.D)
     sd.spec_verify(ctx, K, seed, b.d, b.D, b.out, b.nacc, b.T if with_rows else None,
@@ -77,7 +87,42 @@ class Shadow:
         self.max_prob_err = 0.0
         self.max_draft_prob_err = 0.0
 
+    def catch_up_draft(self):
+        """The library's draft catch-up: when more committed rows lag than
+        one draft step can carry (after plain steps or n-gram rounds), the
+        draft cache is prefilled with them first."""
+        if self.LT - self.LD > 7:
+            oracle.forward(self.D, self.kvD, self.hist[self.LD: self.LT], self.LD, want_logits=False)
+            self.LD = self.LT
+
+    def check_plain(self, g):
+        """One plain decode step (verify with K = 0): the row of the pending
+        token, T_1 within tolerance, and the emitted token bit-exact on the
+        GPU's own row (argmax, or inverse CDF with w2 at the new position)."""
+        LT = self.LT
+        lg = oracle.forward(self.T, self.kvT, [self.hist[LT]], LT)
+        lerr = float(np.abs(lg - g["logits"]).max())
+        self.max_logit_err = max(self.max_logit_err, lerr)
+        assert lerr <= LOGIT_TOL, ("logits", lerr)
+        Tor = oracle.softmax_f32(lg[0])
+        perr = float(np.abs(Tor - g["T"][0]).max())
+        self.max_prob_err = max(self.max_prob_err, perr)
+        assert perr <= PROB_TOL, ("target row", perr)
+        row = g["T"][0]
+        if self.greedy:
+            ref = oracle.argmax_low(row)
+        else:
+            u = oracle.u24(oracle.uniform_words(self.seed, LT + 1, 0, self.c)[2])
+            ref = oracle.sample_icdf([oracle.fix(float(x)) for x in row], u)
+            if ref < 0:
+                ref = oracle.argmax_low(row)
+        assert g["nacc"] == 0 and int(g["out"][0]) == ref, (g["nacc"], int(g["out"][0]), ref)
+        self.hist.append(ref)
+        self.LT = LT + 1
+        return ref
+
     def check_round(self, g):
+        self.catch_up_draft()
         K, LT, LD = self.K, self.LT, self.LD
         d = g["d"]
         # draft steps: rows, probabilities, samples
