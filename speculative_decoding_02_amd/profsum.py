@@ -4,12 +4,15 @@ Reads what `rocprofv3 --kernel-trace --stats` or `rocprofv3 --pmc ...` wrote
 (CSV files, or the SQLite database of the default output format) and prints
 short text summaries:
 
-  trace DIR [--rounds R] [--skip-last S] [--kernel SUBSTR]
+  trace DIR [--rounds R] [--skip-last S] [--kernel SUBSTR] [--kernel-window N]
       per-kernel totals over the whole run; then the steady state: the
       dispatches that follow the first commit kernel (i.e. the decoding rounds,
       without weight generation, packing or prefill), per kernel and per round
       (span, busy time, gaps between kernels over R rounds that end S rounds
-      before the last one, e.g. to leave out rounds run without graphs).
+      before the last one, e.g. to leave out steps that follow the timed
+      rounds); with --kernel, the matching launches' average over the steady
+      state and over the N rounds that end S rounds before the last, by kernel
+      name and by grid size.
   pmc FETCH_DIR WRITE_DIR --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes N
       HBM traffic per launch of one kernel in the steady state from the
       FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch), each scaled by the
@@ -96,7 +99,21 @@ def short(name: str, n: int = 70) -> str:
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0) -> str:
+def _by_name_and_grid(sel, kernel: str, lines: list) -> None:
+    by_name = collections.defaultdict(list)
+    by_grid = collections.defaultdict(list)
+    for _, n, s, e, g in sel:
+        if kernel in n:
+            by_name[n].append((e - s) / 1e3)
+            by_grid[g].append((e - s) / 1e3)
+    for n, v in sorted(by_name.items()):
+        lines.append(f"  {short(n)}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+    for g, v in sorted(by_grid.items()):
+        lines.append(f"  grid_x {g}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+
+
+def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0,
+                  kernel_window: int = 0) -> str:
     rows = load_dispatches(d)
     lines = []
     tot = collections.defaultdict(lambda: [0, 0.0])
@@ -135,28 +152,19 @@ def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0) -
     if kernel:
         ks = [(e - s) / 1e3 for _, n, s, e, _ in steady if kernel in n]
         if ks:
-            by_grid = collections.defaultdict(list)
-            for _, n, s, e, g in steady:
-                if kernel in n:
-                    by_grid[g].append((e - s) / 1e3)
             lines.append("")
             lines.append(f"kernel '{kernel}' in the steady state: {len(ks)} launches, "
                          f"avg {sum(ks) / len(ks):.2f} us")
-            for g, v in sorted(by_grid.items()):
-                lines.append(f"  grid_x {g}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
-        if skip_last > 0:
-            tail = rows[marks[len(marks) - 1 - skip_last] + 1: marks[-1] + 1]
-            by_grid = collections.defaultdict(list)
-            for _, n, s, e, g in tail:
-                if kernel in n:
-                    by_grid[g].append((e - s) / 1e3)
-            allv = [x for v in by_grid.values() for x in v]
-            if allv:
+            _by_name_and_grid(steady, kernel, lines)
+        W = min(kernel_window, end)
+        if W > 0:
+            win = rows[marks[end - W] + 1: marks[end] + 1]
+            kw = [(e - s) / 1e3 for _, n, s, e, _ in win if kernel in n]
+            if kw:
                 lines.append("")
-                lines.append(f"kernel '{kernel}' in the last {skip_last} rounds: {len(allv)} launches, "
-                             f"avg {sum(allv) / len(allv):.2f} us")
-                for g, v in sorted(by_grid.items()):
-                    lines.append(f"  grid_x {g}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+                lines.append(f"kernel '{kernel}' in the {W} rounds ending {skip_last} before the "
+                             f"last: {len(kw)} launches, avg {sum(kw) / len(kw):.2f} us")
+                _by_name_and_grid(win, kernel, lines)
     return "\n".join(lines)
 
 
@@ -194,6 +202,7 @@ def main(argv=None):
     t.add_argument("--rounds", type=int, default=10)
     t.add_argument("--kernel", default=None)
     t.add_argument("--skip-last", type=int, default=0)
+    t.add_argument("--kernel-window", type=int, default=0)
     p = sub.add_parser("pmc")
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
@@ -202,7 +211,7 @@ def main(argv=None):
     p.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last))
+        print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last, a.kernel_window))
     else:
         print(pmc_summary(a.fetch_dir, a.write_dir, a.kernel, a.copy_kernel, a.copy_bytes))
 
