@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE, WRITE_SIZE) of this script, with the hash of the kernel sources
 # they were taken with; used only while the sources still hash the same.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_8b_k4_traffic.txt")
-KERNEL_SOURCES = ("k_gemm.hip", "common.h", "kernels.h", "spec_api.cpp")
+KERNEL_SOURCES = ("k_gemm.hip", "k_gemm.h", "common.h")  # the GEMM kernels and their launch plans
 COPY_CALIB_BYTES = 1 << 30
 
 

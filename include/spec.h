@@ -265,7 +265,8 @@ int32_t spec_choose_k(double alpha, double t_draft_step, double t_verify, int32_
 /* Measurement helper, not a step of the method: the rate of a plain streaming
  * read (16-byte non-temporal loads, nothing else), the HBM ceiling that the
  * verify pass's GB/s is set against.  Reads bytes (a multiple of 16, at least
- * 1 MiB) of buf_dev reps times at each of three grid sizes and returns the
+ * 1 MiB) of buf_dev reps times with 1, 2 and 4 workgroups per CU (each
+ * workgroup one contiguous slice, 8 loads per lane in flight) and returns the
  * best rate in GB/s (1e9 bytes/s), timed with HIP events on hip_stream.
  * Synchronises the stream.  Errors: SPEC_ERR_ARG, SPEC_ERR_HIP. */
 int spec_read_ceiling(const void* buf_dev, uint64_t bytes, int32_t reps, void* hip_stream,

@@ -1,0 +1,114 @@
+// k_gemm.h -- launch arguments, launchers and launch plans of the
+// weight-streaming skinny GEMM (k_gemm.hip).  Everything that decides the
+// GEMM kernels' code and launch shapes lives in k_gemm.hip, this header and
+// common.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace spec {
+
+// ------------------------------------------------------------------ GEMM --
+// Epilogue kinds of the skinny GEMM Y[m][n] = sum_k A[m][k] W[n][k].
+enum Epi : int {
+  EPI_STORE = 0,   // out[m][n] = y (fp32)
+  EPI_RESID = 1,   // resid[m][n] += y; packed (resid * gain_next) for the next GEMM;
+                   // per-workgroup sums of squares for the next RMSNorm
+  EPI_SILU = 2,    // packed silu(gate) * up for the down projection (8 gate, 8 up columns per block)
+  EPI_QKV = 3,     // RoPE on q/k; q -> attention query fragments, k/v -> paged KV cache
+  EPI_LOGITS = 4,  // out[m][n] = logit; per-workgroup (max, sum exp) partials
+};
+
+struct GemmArgs {
+  // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16]
+  const uint16_t* Wp;
+  int n_groups;      // one workgroup per group of NB 16-column blocks
+  int Kb;            // K / 32
+  int K;
+  // A operand: packed rows (see apack_index) of length K
+  const uint16_t* Ap;
+  const PassRows* rows;
+  int last_row_only;  // use only row n_rows-1 (written as output row 0)
+  // RMSNorm of the consumer: y[m][.] *= 1/sqrt(sum_g ssq[g][m] / K + eps)
+  const float* ssq;   // [ssq_groups][8] or null (no norm)
+  int ssq_groups;
+  float eps;
+  // epilogue
+  float* out;
+  int ldo;
+  float* resid;       // EPI_RESID: fp32 residual rows [8][ldr]
+  int ldr;
+  const uint16_t* gain_next;  // EPI_RESID: gain of the next RMSNorm (bf16 [N])
+  uint16_t* Ap_out;   // EPI_RESID / EPI_SILU: packed A rows for the next GEMM
+  float* ssq_out;     // EPI_RESID: [n_groups][8]
+  float2* lm_part;    // EPI_LOGITS: [n_groups][8]
+  int n_valid;        // EPI_LOGITS: valid columns (vocab)
+  // EPI_QKV: q -> query fragments, k/v -> paged caches
+  uint16_t* qf;
+  int q_dim, kv_dim, head_dim, n_kv;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* block_table;
+  const float2* rope;      // [max_seq][head_dim/2] (cos, sin)
+  int max_seq;
+  // Optional end stamps: workgroup g writes the device wall clock to
+  // ts_end[g] once all its threads have issued their last stores (a plain
+  // store per workgroup, no atomics).  Null: off.
+  unsigned long long* ts_end;
+};
+
+struct GemmShape {
+  int nb;      // 16-column blocks per workgroup
+  int waves;   // waves per workgroup, splitting K
+};
+hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
+// Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
+constexpr int kGemmMaxSsqPerThread = 16;
+
+// Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
+// layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
+hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, uint16_t* out,
+                       hipStream_t s);
+
+// ------------------------------------------------------------ GEMM plans --
+// One workgroup per group of `nb` 16-column blocks, `waves` waves splitting K.
+struct GemmPlan {
+  GemmShape shape{1, 4};
+  int n_groups = 0, Kb = 0;
+};
+
+// Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4,7} and
+// waves in {4,8,16}, weights cold, with per-workgroup start/end stamps).
+// A streaming GEMM is fastest when every CU gets the same number of weight
+// bytes and all its workgroups are resident from the start: waves of one CU
+// are served oldest first, so on CUs holding one workgroup more than others
+// the last one streams alone at the end (896 gate/up workgroups of the 8B
+// shape end between 14 and 39 us; 256 workgroups of 7 blocks all end
+// together, 37.0 instead of 40.1 us).  So when the column blocks divide
+// evenly over the CUs (n_cu > 0) a workgroup takes n_blocks / n_cu of them
+// (up to 7, eight waves from four blocks on).  Otherwise: two blocks per
+// workgroup once that still leaves >= 192 workgroups, four waves, except
+// for narrow matrices with a long K, where only eight waves per workgroup
+// keep enough loads in flight.
+inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu) {
+  GemmPlan p;
+  const int n_blocks = n_cols / 16;
+  p.Kb = K / 32;
+  const int q = n_cu > 0 && n_blocks % n_cu == 0 ? n_blocks / n_cu : 0;
+  if ((q == 2 || q == 4 || q == 7) && q >= nb_min) {
+    p.shape.nb = q;
+    p.n_groups = n_cu;
+    p.shape.waves = q >= 4 ? 8 : 4;
+    return p;
+  }
+  p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
+  p.n_groups = n_blocks / p.shape.nb;
+  p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
+  return p;
+}
+
+}  // namespace spec

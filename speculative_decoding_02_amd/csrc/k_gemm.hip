@@ -23,7 +23,7 @@
 //    squares published by the producer.
 #include <type_traits>
 
-#include "kernels.h"
+#include "k_gemm.h"
 
 namespace spec {
 

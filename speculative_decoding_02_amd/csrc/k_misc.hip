@@ -182,20 +182,27 @@ hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_
 // Plain streaming read of a buffer (16-byte non-temporal loads, four in
 // flight per thread, grid-stride): the HBM read rate a kernel that does
 // nothing else reaches, against which the verify pass's rate is read.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* p, size_t n, uint32_t* sink) {
+// Streaming read: workgroup g reads the contiguous slice [n g / G, n (g+1) / G)
+// of 16-byte words; its 512 lanes keep 8 non-temporal loads each in flight,
+// the waves interleaved over 8 KiB steps.
+constexpr int kReadThreads = 512;
+constexpr int kReadDepth = 8;
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4* p, size_t n,
+                                                                  uint32_t* sink) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t G = gridDim.x, g = blockIdx.x;
+  const size_t b = n * g / G, e = n * (g + 1) / G;
+  constexpr size_t step = kReadThreads;
+  size_t i = b + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4_t v0 = __builtin_nontemporal_load((const u32x4_t*)(p + i));
-    const u32x4_t v1 = __builtin_nontemporal_load((const u32x4_t*)(p + i + stride));
-    const u32x4_t v2 = __builtin_nontemporal_load((const u32x4_t*)(p + i + 2 * stride));
-    const u32x4_t v3 = __builtin_nontemporal_load((const u32x4_t*)(p + i + 3 * stride));
-    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-    acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  for (; i + (kReadDepth - 1) * step < e; i += kReadDepth * step) {
+    u32x4_t v[kReadDepth];
+#pragma unroll
+    for (int u = 0; u < kReadDepth; ++u) v[u] = __builtin_nontemporal_load((const u32x4_t*)(p + i + u * step));
+#pragma unroll
+    for (int u = 0; u < kReadDepth; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n; i += stride) {
+  for (; i < e; i += step) {
     const uint4 v = p[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -206,8 +213,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* p, size_t
 hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
                               hipStream_t s) {
   if (bytes % 16 || grid < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)buf, bytes / 16,
-                     sink);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kReadThreads), 0, s, (const uint4*)buf,
+                     bytes / 16, sink);
   return hipGetLastError();
 }
 

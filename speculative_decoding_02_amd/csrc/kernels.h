@@ -7,70 +7,9 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "k_gemm.h"
 
 namespace spec {
-
-// ------------------------------------------------------------------ GEMM --
-// Epilogue kinds of the skinny GEMM Y[m][n] = sum_k A[m][k] W[n][k].
-enum Epi : int {
-  EPI_STORE = 0,   // out[m][n] = y (fp32)
-  EPI_RESID = 1,   // resid[m][n] += y; packed (resid * gain_next) for the next GEMM;
-                   // per-workgroup sums of squares for the next RMSNorm
-  EPI_SILU = 2,    // packed silu(gate) * up for the down projection (8 gate, 8 up columns per block)
-  EPI_QKV = 3,     // RoPE on q/k; q -> attention query fragments, k/v -> paged KV cache
-  EPI_LOGITS = 4,  // out[m][n] = logit; per-workgroup (max, sum exp) partials
-};
-
-struct GemmArgs {
-  // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16]
-  const uint16_t* Wp;
-  int n_groups;      // one workgroup per group of NB 16-column blocks
-  int Kb;            // K / 32
-  int K;
-  // A operand: packed rows (see apack_index) of length K
-  const uint16_t* Ap;
-  const PassRows* rows;
-  int last_row_only;  // use only row n_rows-1 (written as output row 0)
-  // RMSNorm of the consumer: y[m][.] *= 1/sqrt(sum_g ssq[g][m] / K + eps)
-  const float* ssq;   // [ssq_groups][8] or null (no norm)
-  int ssq_groups;
-  float eps;
-  // epilogue
-  float* out;
-  int ldo;
-  float* resid;       // EPI_RESID: fp32 residual rows [8][ldr]
-  int ldr;
-  const uint16_t* gain_next;  // EPI_RESID: gain of the next RMSNorm (bf16 [N])
-  uint16_t* Ap_out;   // EPI_RESID / EPI_SILU: packed A rows for the next GEMM
-  float* ssq_out;     // EPI_RESID: [n_groups][8]
-  float2* lm_part;    // EPI_LOGITS: [n_groups][8]
-  int n_valid;        // EPI_LOGITS: valid columns (vocab)
-  // EPI_QKV: q -> query fragments, k/v -> paged caches
-  uint16_t* qf;
-  int q_dim, kv_dim, head_dim, n_kv;
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  const int32_t* block_table;
-  const float2* rope;      // [max_seq][head_dim/2] (cos, sin)
-  int max_seq;
-  // Optional end stamps: workgroup g writes the device wall clock to
-  // ts_end[g] once all its threads have issued their last stores (a plain
-  // store per workgroup, no atomics).  Null: off.
-  unsigned long long* ts_end;
-};
-
-struct GemmShape {
-  int nb;      // 16-column blocks per workgroup
-  int waves;   // waves per workgroup, splitting K
-};
-hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
-// Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
-constexpr int kGemmMaxSsqPerThread = 16;
-
-// Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
-// layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
-hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, uint16_t* out,
-                       hipStream_t s);
 
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
@@ -179,7 +118,8 @@ hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s);
 // ---------------------------------------------------------------- commit --
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
                          const int32_t* n_acc, int drafted_k, int verified_k, hipStream_t s);
-// Streaming read of `bytes` (a multiple of 16) with `grid` blocks of 256.
+// Streaming read of `bytes` (a multiple of 16): `grid` workgroups of 512 threads, each reading one
+// contiguous slice.
 hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
                               hipStream_t s);
 // RoPE table: (cos, sin) of p * theta^(-2j/hd) for p < max_seq, j < hd/2,

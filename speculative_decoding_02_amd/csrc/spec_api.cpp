@@ -36,43 +36,6 @@ std::string fmt(const char* f, ...) {
   return buf;
 }
 
-// ------------------------------------------------------------ GEMM plans --
-// One workgroup per group of `nb` 16-column blocks, `waves` waves splitting K.
-struct GemmPlan {
-  GemmShape shape{1, 4};
-  int n_groups = 0, Kb = 0;
-};
-
-// Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4,7} and
-// waves in {4,8,16}, weights cold, with per-workgroup start/end stamps).
-// A streaming GEMM is fastest when every CU gets the same number of weight
-// bytes and all its workgroups are resident from the start: waves of one CU
-// are served oldest first, so on CUs holding one workgroup more than others
-// the last one streams alone at the end (896 gate/up workgroups of the 8B
-// shape end between 14 and 39 us; 256 workgroups of 7 blocks all end
-// together, 37.0 instead of 40.1 us).  So when the column blocks divide
-// evenly over the CUs (n_cu > 0) a workgroup takes n_blocks / n_cu of them
-// (up to 7, eight waves from four blocks on).  Otherwise: two blocks per
-// workgroup once that still leaves >= 192 workgroups, four waves, except
-// for narrow matrices with a long K, where only eight waves per workgroup
-// keep enough loads in flight.
-GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu) {
-  GemmPlan p;
-  const int n_blocks = n_cols / 16;
-  p.Kb = K / 32;
-  const int q = n_cu > 0 && n_blocks % n_cu == 0 ? n_blocks / n_cu : 0;
-  if ((q == 2 || q == 4 || q == 7) && q >= nb_min) {
-    p.shape.nb = q;
-    p.n_groups = n_cu;
-    p.shape.waves = q >= 4 ? 8 : 4;
-    return p;
-  }
-  p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
-  p.n_groups = n_blocks / p.shape.nb;
-  p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
-  return p;
-}
-
 struct Mat {
   uint16_t* p = nullptr;  // packed (inside the model arena)
   GemmPlan plan;
@@ -1059,7 +1022,7 @@ int spec_read_ceiling(const void* buf_dev, uint64_t bytes, int32_t reps, void* h
   if (e == hipSuccess) e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
   double best = 0.0;
-  for (int mult : {4, 8, 16}) {
+  for (int mult : {1, 2, 4}) {  // workgroups per CU
     const int grid = n_cu * mult;
     if (e == hipSuccess) e = launch_stream_read(buf_dev, bytes, grid, sink, s);  // warm-up
     if (e == hipSuccess) e = hipEventRecord(e0, s);
