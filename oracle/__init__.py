@@ -72,7 +72,11 @@ def lib():
         L.orc_kv_new.restype = _p
         L.orc_kv_free.argtypes = [_p]
         L.orc_forward.argtypes = [_p, _p, _p, _i32, _i32, _p]
+        L.orc_forward_hidden.argtypes = [_p, _p, _p, _i32, _i32, _p, _p]
         L.orc_softmax_f32.argtypes = [_p, _i32, _p]
+        L.orc_heads_draft.argtypes = [_p, _p, _i32, _p, _i32, _i32, _u64, _u64, _u64, _p, _p]
+        L.orc_spec_generate_heads.argtypes = [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _u64,
+                                              _u64, _p, _p, _p, _p]
         L.orc_generate.argtypes = [_p, _p, _i32, _i32, _i32, _u64, _u64, _p]
         L.orc_spec_generate.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _u64, _u64, _p, _p, _p]
         L.orc_num_threads.restype = _i32
@@ -311,6 +315,53 @@ def forward(model: Model, kv: KV, tokens, pos0: int, want_logits: bool = True):
     if rc != OK:
         raise ValueError(f"orc_forward rc={rc}")
     return lg
+
+
+def forward_hidden(model: Model, kv: KV, tokens, pos0: int, want_logits: bool = True):
+    """(logits [n][V] or None, final normed states [n][d]) of orc_forward_hidden."""
+    t = _c(tokens, np.int32)
+    n = len(t)
+    lg = np.zeros((n, model.vocab), np.float64) if want_logits else None
+    hid = np.zeros((n, model.cfg.d_model), np.float64)
+    rc = lib().orc_forward_hidden(model.ref(), kv._h, _ptr(t), n, pos0,
+                                  _ptr(lg) if want_logits else None, _ptr(hid))
+    if rc != OK:
+        raise ValueError(f"orc_forward_hidden rc={rc}")
+    return lg, hid
+
+
+def heads_draft(model: Model, W_heads, h, K: int, greedy: bool, seed: int, P: int, c: int = 0):
+    """orc_heads_draft: (D [K][V] fp32, drafts [K]) from the final normed
+    state h [d] and head matrices W_heads [n_heads][d][d] (bf16 bits)."""
+    W = _c(W_heads, np.uint16)
+    ha = _c(h, np.float64)
+    n_heads = W.shape[0]
+    D = np.zeros((K, model.vocab), np.float32)
+    d = np.zeros(K, np.int32)
+    rc = lib().orc_heads_draft(model.ref(), _ptr(W), n_heads, _ptr(ha), K, int(bool(greedy)),
+                               seed, P, c, _ptr(D), _ptr(d))
+    if rc != OK:
+        raise ValueError(f"orc_heads_draft rc={rc}")
+    return D, d
+
+
+def spec_generate_heads(target: Model, W_heads, prompt, n_new: int, K: int, greedy: bool,
+                        seed: int = 0, c: int = 0):
+    """(tokens [n_new], n_acc per round, drafts per round [rounds][K], stats)."""
+    W = _c(W_heads, np.uint16)
+    pr = _c(prompt, np.int32)
+    out = np.zeros(n_new, np.int32)
+    nacc = np.full(max(n_new, 1), -1, np.int32)
+    drafts = np.full((max(n_new, 1), K), -1, np.int32)
+    st = _Stats()
+    rc = lib().orc_spec_generate_heads(target.ref(), _ptr(W), W.shape[0], _ptr(pr), len(pr), n_new,
+                                       K, int(bool(greedy)), seed, c, _ptr(out), _ptr(nacc),
+                                       _ptr(drafts), C.byref(st))
+    if rc != OK:
+        raise ValueError(f"orc_spec_generate_heads rc={rc}")
+    stats = {"rounds": st.rounds, "target_passes": st.target_passes,
+             "draft_passes": st.draft_passes, "accepted": st.accepted, "emitted": st.emitted}
+    return out, nacc[: st.rounds], drafts[: st.rounds], stats
 
 
 def softmax_f32(logits) -> np.ndarray:

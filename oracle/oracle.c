@@ -402,8 +402,10 @@ static void attend_head(const double* qv, const double* kbase, const double* vba
   }
 }
 
-int orc_forward(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n, int32_t pos0,
-                double* logits) {
+/* The forward pass of n rows; `hidden` (nullable) receives each row's final
+ * normed state RMSNorm(x) * g_final, the vector the LM head scores. */
+static int forward_impl(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n,
+                        int32_t pos0, double* logits, double* hidden) {
   if (n <= 0) return ORC_OK;
   if (pos0 < 0 || pos0 + n > kv->max_seq) return ORC_ECAPACITY;
   const int32_t d = m->d_model, H = m->n_heads, Hkv = m->n_kv_heads, hd = m->head_dim;
@@ -465,13 +467,24 @@ int orc_forward(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n
     matmul_rows(g, n, F, m->wd + (size_t)l * d * F, d, y);
     for (size_t i = 0; i < (size_t)n * d; i++) x[i] += y[i];
   }
-  if (logits) {
+  if (logits || hidden) {
     for (int32_t r = 0; r < n; r++)
       rmsnorm_row(x + (size_t)r * d, d, m->final_norm, m->rms_eps, h + (size_t)r * d);
-    matmul_rows(h, n, d, m->lm_head, V, logits);
+    if (hidden) memcpy(hidden, h, sizeof(double) * (size_t)n * d);
+    if (logits) matmul_rows(h, n, d, m->lm_head, V, logits);
   }
   free(x); free(h); free(q); free(k); free(v); free(o); free(y); free(g); free(u); free(sc);
   return ORC_OK;
+}
+
+int orc_forward(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n, int32_t pos0,
+                double* logits) {
+  return forward_impl(m, kv, tokens, n, pos0, logits, NULL);
+}
+
+int orc_forward_hidden(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n,
+                       int32_t pos0, double* logits, double* hidden) {
+  return forward_impl(m, kv, tokens, n, pos0, logits, hidden);
 }
 
 /* Temperature-1 softmax with max subtraction, in fp64, rounded to fp32. */
@@ -600,6 +613,106 @@ int orc_spec_generate(const orc_model* target, const orc_model* draft, const int
   if (st) *st = s0;
   orc_kv_free(kvT); orc_kv_free(kvD);
   free(hist); free(lgD); free(lgT); free(Dp); free(Tp); free(dr); free(rows); free(ob);
+  return rc;
+}
+
+/* ======================================================================= */
+/* Multi-token-prediction heads as the drafter ([int] "variants": MTP gives  */
+/* the target K extra output heads, head k predicting the token k places    */
+/* ahead, so no separate drafter model is needed).  The pages fix no head   */
+/* architecture; the reading used here: head k takes the target's final     */
+/* normed state h of the last position it processed, z_k = h + silu(W_k h)  */
+/* with its own [d][d] matrix, and scores z_k with the target's own LM head. */
+/* The position right after h is the pending token, already decided by the  */
+/* rule, so the K heads draft the K positions after it.                      */
+/* ======================================================================= */
+int orc_heads_draft(const orc_model* m, const uint16_t* W_heads, int32_t n_heads, const double* h,
+                    int32_t K, int32_t greedy, uint64_t seed, uint64_t P, uint64_t c, float* D,
+                    int32_t* d) {
+  if (!m || !W_heads || !h || !D || !d || K < 1 || K > n_heads) return ORC_EARG;
+  const int32_t dm = m->d_model, V = m->vocab;
+  double* y = (double*)malloc(sizeof(double) * (size_t)dm);
+  double* z = (double*)malloc(sizeof(double) * (size_t)dm);
+  double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+  int rc = (y && z && lg) ? ORC_OK : ORC_ENOMEM;
+  for (int32_t k = 0; rc == ORC_OK && k < K; k++) {
+    matmul_rows(h, 1, dm, W_heads + (size_t)k * dm * dm, dm, y);
+    for (int32_t i = 0; i < dm; i++) z[i] = h[i] + silu(y[i]);
+    matmul_rows(z, 1, dm, m->lm_head, V, lg);
+    float* Dk = D + (size_t)k * V;
+    orc_softmax_f32(lg, V, Dk);
+    /* d_k decides position P + k, drawn like any draft token (word 0) */
+    const int32_t t = orc_draft_sample(Dk, V, seed, P + (uint64_t)k, 0, c, greedy);
+    if (t < 0) rc = ORC_EBADPROB;
+    else d[k] = t;
+  }
+  free(y); free(z); free(lg);
+  return rc;
+}
+
+/* Speculative decoding with the heads as the drafter: the prompt prefill
+ * keeps the normed state of its last row; each round drafts K tokens from
+ * the kept state, runs the (K+1)-row verify pass and the rule, commits, and
+ * keeps the state of the last committed row of the pass (row n_acc: the
+ * pending token or the last accepted draft), whose successor is the new
+ * pending token.  drafts_per_round (nullable, capacity n_new*K) receives
+ * each round's drafts. */
+int orc_spec_generate_heads(const orc_model* target, const uint16_t* W_heads, int32_t n_heads,
+                            const int32_t* prompt, int32_t n_prompt, int32_t n_new, int32_t K,
+                            int32_t greedy, uint64_t seed, uint64_t c, int32_t* out,
+                            int32_t* nacc_per_round, int32_t* drafts_per_round,
+                            orc_spec_stats* st) {
+  if (n_prompt < 2 || n_new < 0 || K < 1 || K > n_heads || !W_heads) return ORC_EARG;
+  const int32_t V = target->vocab, dm = target->d_model;
+  const int32_t cap = n_prompt + n_new + K + 2;
+  orc_kv* kvT = orc_kv_new(target, cap);
+  int32_t* hist = (int32_t*)malloc(sizeof(int32_t) * (size_t)cap);
+  double* hid = (double*)malloc(sizeof(double) * (size_t)(n_prompt > K + 1 ? n_prompt : K + 1) * dm);
+  double* hlast = (double*)malloc(sizeof(double) * (size_t)dm);
+  double* lgT = (double*)malloc(sizeof(double) * (size_t)(K + 1) * V);
+  float* Dp = (float*)malloc(sizeof(float) * (size_t)K * V);
+  float* Tp = (float*)malloc(sizeof(float) * (size_t)(K + 1) * V);
+  int32_t* dr = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+  int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K + 1));
+  int32_t* ob = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K + 1));
+  orc_spec_stats s0 = {0, 0, 0, 0, 0};
+  int rc = (kvT && hist && hid && hlast && lgT && Dp && Tp && dr && rows && ob) ? ORC_OK
+                                                                                : ORC_ENOMEM;
+  if (rc == ORC_OK) {
+    memcpy(hist, prompt, sizeof(int32_t) * (size_t)n_prompt);
+    rc = forward_impl(target, kvT, prompt, n_prompt - 1, 0, NULL, hid);
+    if (rc == ORC_OK) memcpy(hlast, hid + (size_t)(n_prompt - 2) * dm, sizeof(double) * dm);
+  }
+  int32_t LT = n_prompt - 1, emitted = 0;
+  while (rc == ORC_OK && emitted < n_new) {
+    rc = orc_heads_draft(target, W_heads, n_heads, hlast, K, greedy, seed, (uint64_t)(LT + 1), c,
+                         Dp, dr);
+    if (rc != ORC_OK) break;
+    s0.draft_passes++;
+    if (drafts_per_round && s0.rounds < n_new)
+      memcpy(drafts_per_round + (size_t)s0.rounds * K, dr, sizeof(int32_t) * K);
+    rows[0] = hist[LT];
+    for (int32_t i = 0; i < K; i++) rows[i + 1] = dr[i];
+    rc = forward_impl(target, kvT, rows, K + 1, LT, lgT, hid);
+    if (rc != ORC_OK) break;
+    s0.target_passes++;
+    for (int32_t i = 0; i <= K; i++) orc_softmax_f32(lgT + (size_t)i * V, V, Tp + (size_t)i * V);
+    int32_t n;
+    if (greedy) rc = orc_verify_greedy(Tp, dr, K, V, ob, &n);
+    else rc = orc_verify_sample(Tp, Dp, dr, K, V, seed, 0, c, (uint64_t)(LT + 1), ob, &n);
+    if (rc != ORC_OK) break;
+    for (int32_t i = 0; i <= n; i++) hist[LT + 1 + i] = ob[i];
+    memcpy(hlast, hid + (size_t)n * dm, sizeof(double) * dm);
+    LT += n + 1;
+    if (nacc_per_round && s0.rounds < n_new) nacc_per_round[s0.rounds] = n;
+    s0.rounds++;
+    s0.accepted += n;
+    s0.emitted += n + 1;
+    for (int32_t i = 0; i <= n && emitted < n_new; i++) out[emitted++] = ob[i];
+  }
+  if (st) *st = s0;
+  orc_kv_free(kvT);
+  free(hist); free(hid); free(hlast); free(lgT); free(Dp); free(Tp); free(dr); free(rows); free(ob);
   return rc;
 }
 

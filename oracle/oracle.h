@@ -112,6 +112,10 @@ void orc_kv_free(orc_kv* kv);
  * logits.  Rows attend to keys 0..pos0+r. */
 int orc_forward(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n, int32_t pos0,
                 double* logits);
+/* orc_forward that also returns each row's final normed state
+ * RMSNorm(x) * g_final ([n][d_model] fp64, nullable), the input of the LM head. */
+int orc_forward_hidden(const orc_model* m, orc_kv* kv, const int32_t* tokens, int32_t n,
+                       int32_t pos0, double* logits, double* hidden);
 /* softmax of one fp64 logit row, rounded to fp32 */
 void orc_softmax_f32(const double* logits, int32_t V, float* p);
 
@@ -166,6 +170,30 @@ int32_t orc_ngram_draft(const int32_t* hist, int32_t L, int32_t K, int32_t n_max
  * Returns ORC_EARG for a outside [0,1], negative times or k_max < 1. */
 double orc_expected_tokens(double a, int32_t K);
 int32_t orc_choose_k(double a, double t_draft, double t_verify, int32_t k_max);
+
+/* ---- multi-token-prediction heads as the drafter -------------------------
+ * [int] "variants" (MTP): the target carries K extra output heads, head k
+ * predicting the token k places ahead; no separate drafter model.  Reading
+ * (the pages fix no head architecture): head k maps the target's final normed
+ * state h of the last position it processed to z_k = h + silu(W_k h), W_k a
+ * [d][d] matrix (W_heads = [n_heads][d][d] bf16), scored by the target's LM
+ * head: D_k = softmax(lm_head z_k).  The position after h holds the pending
+ * token, already decided by the rule, so the K heads draft positions
+ * P .. P+K-1 (P = position of d_1); d_k is drawn from D_k with word 0 at
+ * P + k (argmax in greedy mode).  D: [K][V] fp32, d: [K].  K <= n_heads. */
+int orc_heads_draft(const orc_model* m, const uint16_t* W_heads, int32_t n_heads, const double* h,
+                    int32_t K, int32_t greedy, uint64_t seed, uint64_t P, uint64_t c, float* D,
+                    int32_t* d);
+/* Speculative decoding with the heads as the drafter (n_prompt >= 2: the
+ * prefill must process at least one row).  Each round drafts from the kept
+ * state, verifies K+1 rows, applies the rule and keeps the state of the last
+ * committed row of the pass.  drafts_per_round (nullable, capacity n_new*K)
+ * receives each round's drafts; the other outputs as in orc_spec_generate. */
+int orc_spec_generate_heads(const orc_model* target, const uint16_t* W_heads, int32_t n_heads,
+                            const int32_t* prompt, int32_t n_prompt, int32_t n_new, int32_t K,
+                            int32_t greedy, uint64_t seed, uint64_t c, int32_t* out,
+                            int32_t* nacc_per_round, int32_t* drafts_per_round,
+                            orc_spec_stats* st);
 
 int32_t orc_num_threads(void);
 

@@ -20,6 +20,7 @@ SEED_PROMPT = 1002
 SEED_PHILOX = 1003
 SEED_LOGITS = 1004
 SEED_DIRICHLET = 1005
+SEED_HEADS = 1006
 
 WEIGHT_NAMES = ("embed", "attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd",
                 "final_norm", "lm_head")
@@ -159,6 +160,24 @@ def weights_torch(cfg: ModelConfig, seed: int = SEED_WEIGHTS, device="cuda", std
     if cfg.tied_head:
         out["lm_head"] = out["embed"]
     return out
+
+
+def heads_np(cfg: ModelConfig, n_heads: int, seed: int = SEED_HEADS, std: float = 0.02) -> np.ndarray:
+    """Drafting-head matrices [n_heads][d][d] as bf16 bit patterns, N(0, std)."""
+    rng = np.random.default_rng(_sub_seed(seed, f"{cfg.name}/heads/{n_heads}"))
+    shp = (n_heads, cfg.d_model, cfg.d_model)
+    return f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
+
+
+def heads_torch(cfg: ModelConfig, n_heads: int, seed: int = SEED_HEADS, device="cuda",
+                std: float = 0.02):
+    """Drafting-head matrices [n_heads][d][d] as a torch.bfloat16 device tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(zlib.crc32(f"{seed}/{cfg.name}/heads/{n_heads}".encode()))
+    t = torch.randn((n_heads, cfg.d_model, cfg.d_model), generator=g, device=device,
+                    dtype=torch.float32) * std
+    return t.to(torch.bfloat16)
 
 
 def torch_to_bits(weights) -> Dict[str, np.ndarray]:
