@@ -137,6 +137,37 @@ int spec_draft(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D
  * pointers). */
 int spec_draft_ngram(spec_ctx* ctx, int32_t K, int32_t n_max, int32_t* d_dev, float* D_dev);
 
+/* Multi-token-prediction heads as the drafter ("Speculative decoding
+ * internals", variants: MTP -- the target carries extra output heads, head k
+ * predicting the token k places ahead, and needs no separate drafter model).
+ * The pages fix no head architecture; here head k maps the target's final
+ * normed state h of the last position it processed to z_k = h + silu(W_k h)
+ * and the target's own LM head scores z_k.  spec_heads_init packs the head
+ * matrices into context-owned memory (the caller may free W_dev afterwards);
+ * a second call replaces them.
+ *   W_dev: bf16 [n_heads][d_model][d_model] (row-major, output-major) device
+ *   memory of the target's width; n_heads in 1..7.
+ * Synchronises the context stream.  Errors: SPEC_ERR_ARG (null pointers,
+ * n_heads out of range), SPEC_ERR_STATE (a verify is pending), SPEC_ERR_OOM,
+ * SPEC_ERR_HIP. */
+int spec_heads_init(spec_ctx* ctx, const void* W_dev, int32_t n_heads);
+
+/* K drafts from the heads: the state is the target's final residual at the
+ * last committed position (kept by the prompt prefill and by every
+ * spec_commit), so no draft model runs and the draft cache is left as it is.
+ * The position after that state holds the pending token, so head k (k = 0..
+ * K-1) drafts the token after it at position LT+1+k: D_dev[k] = softmax of
+ * the LM head on z_k, d_dev[k] drawn from it by inverse CDF on the 2^-40 grid
+ * with Philox word w0 at that position (seed, stream_id), or its top token in
+ * greedy mode -- the same draw spec_draft makes.  Each D row depends on the
+ * committed prefix only, not on the earlier drafts of the round; spec_verify
+ * takes the pair unchanged.  Asynchronous on the context stream.
+ *   d_dev: int32 [K]; D_dev: fp32 [K][vocab].
+ * Errors: SPEC_ERR_ARG (K outside 1..min(n_heads, k_max), null pointers),
+ * SPEC_ERR_STATE (no heads; a verify is pending; a one-token prompt and no
+ * commit yet, so no position has been processed), SPEC_ERR_CAPACITY. */
+int spec_draft_heads(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev);
+
 /* Verify pass plus accept/reject ([int] algorithm core, Steps 2-4; [en]
  * Floors 3-5).  One target pass over the K+1 rows [pending, d_1..d_K] at
  * positions L..L+K gives T_1..T_{K+1}; their keys/values are appended to the

@@ -74,6 +74,8 @@ def lib():
         L.spec_draft.argtypes = [_p, _i32, _u64, _p, _p]
         L.spec_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
         L.spec_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
+        L.spec_heads_init.argtypes = [_p, _p, _i32]
+        L.spec_draft_heads.argtypes = [_p, _i32, _u64, _p, _p]
         L.spec_mat_create.argtypes = [_p, _i32, _i32, C.POINTER(_p)]
         L.spec_mat_mul.argtypes = [_p, _p, _i32, _p, _p]
         L.spec_mat_destroy.argtypes = [_p]
@@ -101,7 +103,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_verify", "spec_commit", "spec_destroy",
+EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_heads_init", "spec_draft_heads",
+            "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
             "spec_kernel_times", "spec_set_profiling", "spec_accept_reject", "spec_expected_tokens",
             "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
@@ -171,6 +174,15 @@ def spec_draft(ctx: Ctx, K: int, seed: int, d, D) -> None:
 
 def spec_draft_ngram(ctx: Ctx, K: int, n_max: int, d, D=None) -> None:
     _check(lib().spec_draft_ngram(ctx.handle, K, n_max, _ptr(d), _ptr(D)), ctx)
+
+
+def spec_heads_init(ctx: Ctx, W, n_heads: int) -> None:
+    """W: bf16 device tensor [n_heads][d_model][d_model] of the target's width."""
+    _check(lib().spec_heads_init(ctx.handle, _ptr(W), n_heads), ctx)
+
+
+def spec_draft_heads(ctx: Ctx, K: int, seed: int, d, D) -> None:
+    _check(lib().spec_draft_heads(ctx.handle, K, seed, _ptr(d), _ptr(D)), ctx)
 
 
 def spec_mat_create(W) -> int:

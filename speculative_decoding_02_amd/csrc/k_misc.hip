@@ -154,16 +154,22 @@ hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, int n_rows, hipStr
 // tokens were committed: it processed [pending, d_1..d_{K-1}], so it is
 // valid up to position LT + min(n, K-1).
 // The verify's (K, n_acc) pair is counted in the state's acceptance record.
-__global__ void commit_kernel(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                              const int32_t* n_acc, int drafted_k, int verified_k) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+__global__ __launch_bounds__(256) void commit_kernel(DevState* st, int32_t* hist, int hist_cap,
+                                                    const int32_t* out, const int32_t* n_acc,
+                                                    int drafted_k, int verified_k,
+                                                    const float* x_rows, int d, float* h_last) {
+  if (blockIdx.x != 0) return;
   const int n = *n_acc;
   if (n < 0 || n > verified_k) return;
   const int LT = st->LT;
   if (LT + 1 + n >= hist_cap) {
-    atomicOr(&st->err, kErrCapacity);
+    if (threadIdx.x == 0) atomicOr(&st->err, kErrCapacity);
     return;
   }
+  // the state of the last committed position: row n of the pass
+  if (h_last != nullptr)
+    for (int i = threadIdx.x; i < d; i += blockDim.x) h_last[i] = x_rows[(size_t)n * d + i];
+  if (threadIdx.x != 0) return;
   for (int i = 0; i <= n; ++i) hist[LT + 1 + i] = out[i];
   if (drafted_k > 0) st->LD = LT + (n + 1 < drafted_k ? n + 1 : drafted_k);
   st->LT = LT + n + 1;
@@ -171,18 +177,18 @@ __global__ void commit_kernel(DevState* st, int32_t* hist, int hist_cap, const i
 }
 
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                         const int32_t* n_acc, int drafted_k, int verified_k, hipStream_t s) {
+                         const int32_t* n_acc, int drafted_k, int verified_k, const float* x_rows,
+                         int d, float* h_last, hipStream_t s) {
   if (verified_k < 0 || verified_k >= kAcceptBins) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, st, hist, hist_cap, out, n_acc,
-                     drafted_k, verified_k);
+  if (h_last != nullptr && (x_rows == nullptr || d <= 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(256), 0, s, st, hist, hist_cap, out, n_acc,
+                     drafted_k, verified_k, x_rows, d, h_last);
   return hipGetLastError();
 }
 
-// ============================================================ read ceiling ==
-// Plain streaming read of a buffer (16-byte non-temporal loads, four in
-// flight per thread, grid-stride): the HBM read rate a kernel that does
+// Plain streaming read of a buffer: the HBM read rate a kernel that does
 // nothing else reaches, against which the verify pass's rate is read.
-// Streaming read: workgroup g reads the contiguous slice [n g / G, n (g+1) / G)
+// Workgroup g reads the contiguous slice [n g / G, n (g+1) / G)
 // of 16-byte words; its 512 lanes keep 8 non-temporal loads each in flight,
 // the waves interleaved over 8 KiB steps.
 constexpr int kReadThreads = 512;

@@ -115,9 +115,28 @@ struct NgramArgs {
 };
 hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s);
 
+// ------------------------------------------------- multi-token heads --
+struct HeadsArgs {
+  const float* h_last;      // [d] final residual of the last committed position
+  const uint16_t* g_final;  // [d] final RMSNorm gain (bf16)
+  int d;
+  float eps;
+  float* hn;                // [d] normed state h (fp32)
+  uint16_t* Ap;             // packed A operand (row 0: h; rows 0..K-1: z_k)
+  PassRows* rows;           // pass descriptor of the head GEMM, then of the LM head
+  const DevState* st;       // LT: position of the pending token
+  const float* y;           // [K][d] head products W_k h (heads_pack)
+  int K;                    // heads drafted, <= kMaxRows
+};
+hipError_t launch_heads_prep(const HeadsArgs& a, hipStream_t s);
+hipError_t launch_heads_pack(const HeadsArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- commit --
+// Also keeps the final residual row n_acc of the pass (x_rows, row stride d)
+// in h_last: the state the drafting heads start from.
 hipError_t launch_commit(DevState* st, int32_t* hist, int hist_cap, const int32_t* out,
-                         const int32_t* n_acc, int drafted_k, int verified_k, hipStream_t s);
+                         const int32_t* n_acc, int drafted_k, int verified_k, const float* x_rows,
+                         int d, float* h_last, hipStream_t s);
 // Streaming read of `bytes` (a multiple of 16): `grid` workgroups of 512 threads, each reading one
 // contiguous slice.
 hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,

@@ -88,6 +88,17 @@ struct spec_ctx {
   uint64_t* ar_ws = nullptr;
   PassRows* rows = nullptr;
   DevState* st = nullptr;
+  // multi-token-prediction heads (spec_heads_init): the stacked [n_heads*d][d]
+  // matrices packed like any weight, and the state they draft from: the
+  // target's final residual at the last committed position, kept by the
+  // prompt prefill and by every commit
+  Mat heads;
+  uint16_t* heads_arena = nullptr;
+  int n_heads = 0;
+  float* h_last = nullptr;   // [T.d]
+  float* hn = nullptr;       // [T.d] its normed form (heads pass)
+  float* head_y = nullptr;   // [n_heads][T.d] head products
+  bool h_valid = false;
   int32_t* hist = nullptr;
   int hist_cap = 0;
   int attn_max_chunks = 0;
@@ -466,6 +477,45 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
   return e;
 }
 
+// Drafting heads: normed state -> stacked head GEMM (one row, the first K
+// heads' columns) -> z_k rows -> LM head over K rows -> softmax into D ->
+// one sampler per draft (word 0 at the draft's position, as for the draft
+// model; argmax in greedy mode).
+hipError_t enqueue_heads_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32_t* d,
+                               float* Dp) {
+  const Model& m = c->T;
+  HeadsArgs h{};
+  h.h_last = c->h_last; h.g_final = m.final_norm(); h.d = m.d; h.eps = m.eps; h.hn = c->hn;
+  h.Ap = c->ap_x; h.rows = c->rows; h.st = c->st; h.y = c->head_y; h.K = K;
+  hipError_t e = launch_heads_prep(h, s);
+  if (e != hipSuccess) return e;
+  GemmArgs a = gemm_base(c, c->heads, c->ap_x);
+  const int blocks = K * m.d / 16, nb = c->heads.plan.shape.nb;
+  a.n_groups = (blocks + nb - 1) / nb;  // the first K heads' columns
+  a.out = c->head_y; a.ldo = c->heads.N;
+  e = launch_gemm(c->heads.plan.shape, EPI_STORE, a, s);
+  if (e == hipSuccess) e = launch_heads_pack(h, s);
+  if (e != hipSuccess) return e;
+  GemmArgs lm = gemm_base(c, m.lm, c->ap_x);  // no norm: z_k is scored as it is
+  lm.out = c->logits; lm.ldo = m.V; lm.lm_part = c->lm_part; lm.n_valid = m.V;
+  e = launch_gemm(m.lm.plan.shape, EPI_LOGITS, lm, s);
+  if (e != hipSuccess) return e;
+  SoftmaxArgs sm{};
+  sm.logits = c->logits; sm.part = c->lm_part; sm.G = m.lm.plan.n_groups; sm.V = m.V;
+  sm.rows = c->rows; sm.last_row_only = 0; sm.out = Dp; sm.chunk = c->sm_chunk;
+  e = launch_softmax(sm, c->sm_nchunks, K, s);
+  for (int k = 0; k < K && e == hipSuccess; ++k) {
+    ArArgs ar{};
+    ar.T = Dp + (size_t)k * m.V; ar.D = nullptr; ar.d = d; ar.B = 1; ar.K = 0; ar.V = m.V;
+    ar.seed = seed; ar.stream_id = c->p.stream_id; ar.pos = nullptr; ar.st = c->st;
+    ar.pos_offset = k + 1; ar.greedy = c->p.greedy; ar.word = 0;
+    ar.chunk = c->ar_chunk; ar.n_chunks = c->ar_nchunks;
+    ar.out = d + k; ar.n_acc = nullptr; ar.ws = c->ar_ws;
+    e = launch_accept_reject(ar, s);
+  }
+  return e;
+}
+
 // Runs `body` either through a cached graph captured on the capture stream,
 // or (no graphs) directly on the context stream.  With profiling on, the
 // pass's timestamp slots [slot0, slot0 + n_slots) are reset on the stream
@@ -529,8 +579,10 @@ void destroy_ctx(spec_ctx* c) {
   (void)hipFree(c->ts);
   free_model(c->D);
   free_model(c->T);
-  void* bufs[] = {c->x, c->qf, c->ssq_a, c->ssq_b, c->ap_x, c->ap_o, c->ap_a, c->logits, c->Tbuf,
-                  c->attn_wo, c->attn_ml, c->lm_part, c->ar_ws, c->rows, c->st, c->hist};
+  void* bufs[] = {c->x,      c->qf,      c->ssq_a,  c->ssq_b, c->ap_x,  c->ap_o,
+                  c->ap_a,   c->logits,  c->Tbuf,   c->attn_wo, c->attn_ml, c->lm_part,
+                  c->ar_ws,  c->rows,    c->st,     c->hist,  c->heads_arena, c->h_last,
+                  c->hn,     c->head_y};
   for (void* b : bufs) (void)hipFree(b);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
@@ -657,6 +709,8 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   TRYH(hipMemsetAsync(c->ap_x, 0, (size_t)32 * dmax, c->stream));
   TRYH(hipMemsetAsync(c->ap_o, 0, (size_t)32 * qmax, c->stream));
   TRYH(hipMemsetAsync(c->ap_a, 0, (size_t)32 * fmax, c->stream));
+  TRYH(dalloc(&c->h_last, (size_t)c->T.d));
+  TRYH(dalloc(&c->hn, (size_t)c->T.d));
   c->hist_cap = p->max_seq + 16;
   TRYH(dalloc(&c->hist, (size_t)c->hist_cap));
   TRYH(hipMemsetAsync(c->x, 0, (size_t)kMaxRows * dmax * 4, c->stream));
@@ -668,6 +722,13 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
 
   // prompt[0..n-2] into both caches; prompt[n-1] is the pending token
   TRY(prefill(c, c->T, 0, n_prompt - 1));
+  if (n_prompt >= 2) {
+    // the prefill's last row (position n_prompt - 2) sits at row (n_prompt - 2) % 8 of its chunk
+    const int r = (n_prompt - 2) % kMaxRows;
+    TRYH(hipMemcpyAsync(c->h_last, c->x + (size_t)r * c->T.d, (size_t)c->T.d * 4,
+                        hipMemcpyDeviceToDevice, c->stream));
+    c->h_valid = true;
+  }
   TRY(prefill(c, c->D, 0, n_prompt - 1));
   hs.LT = n_prompt - 1;
   hs.LD = n_prompt - 1;
@@ -732,6 +793,70 @@ int spec_draft_ngram(spec_ctx* c, int32_t K, int32_t n_max, int32_t* d_dev, floa
   return SPEC_OK;
 }
 
+int spec_heads_init(spec_ctx* c, const void* W_dev, int32_t n_heads) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_heads_init: null context");
+  if (!W_dev) return fail(c, SPEC_ERR_ARG, "spec_heads_init: null weights");
+  if (n_heads < 1 || n_heads > SPEC_K_MAX)
+    return fail(c, SPEC_ERR_ARG, fmt("n_heads=%d outside 1..%d", n_heads, SPEC_K_MAX));
+  if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_heads_init: a verify is pending");
+  HIPTRY(c, hipSetDevice(c->device));
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  // drop the previous heads and the graphs that captured them
+  for (auto it = c->graph_cache.begin(); it != c->graph_cache.end();) {
+    if (it->first[0] == 3) {
+      if (it->second.exec) (void)hipGraphExecDestroy(it->second.exec);
+      it = c->graph_cache.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  (void)hipFree(c->heads_arena);
+  (void)hipFree(c->head_y);
+  c->heads_arena = nullptr;
+  c->head_y = nullptr;
+  c->n_heads = 0;
+  int n_cu = 0;
+  HIPTRY(c, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
+  const int d = c->T.d;
+  Mat h;
+  h.N = n_heads * d;
+  h.K = d;
+  h.plan = plan_gemm(h.N, 1, d, n_cu);
+  HIPTRY(c, dalloc(&c->heads_arena, h.elems()));
+  h.p = c->heads_arena;
+  HIPTRY(c, dalloc(&c->head_y, (size_t)h.N));
+  const uint16_t* W = (const uint16_t*)W_dev;
+  std::vector<const uint16_t*> rows((size_t)h.plan.n_groups * h.plan.shape.nb * 16, nullptr);
+  for (int n = 0; n < h.N; ++n) rows[n] = W + (size_t)n * d;  // row n: head n / d, output n % d
+  if (int r = pack_rows(c, rows, h)) return r;
+  c->heads = h;
+  c->n_heads = n_heads;
+  return SPEC_OK;
+}
+
+int spec_draft_heads(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev) {
+  if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_draft_heads: null context");
+  if (c->n_heads < 1) return fail(c, SPEC_ERR_STATE, "spec_draft_heads: no heads (spec_heads_init)");
+  if (K < 1 || K > c->n_heads || K > c->p.k_max)
+    return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..min(n_heads, k_max)", K));
+  if (!d_dev || !D_dev) return fail(c, SPEC_ERR_ARG, "spec_draft_heads: null output");
+  if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_draft_heads: a verify is pending");
+  if (!c->h_valid)
+    return fail(c, SPEC_ERR_STATE, "spec_draft_heads: no processed position yet (one-token prompt)");
+  HIPTRY(c, hipSetDevice(c->device));
+  if (c->LT_ub + K > c->p.max_seq) {
+    DevState hs;
+    if (int r = sync_state(c, &hs)) return r;
+    c->LT_ub = hs.LT;
+    if (hs.LT + K > c->p.max_seq)
+      return fail(c, SPEC_ERR_CAPACITY, "draft positions would exceed max_seq");
+  }
+  std::vector<uint64_t> key = {3, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
+                               (uint64_t)(uintptr_t)D_dev, (uint64_t)(uintptr_t)c->heads_arena};
+  return run_pass(c, key, 0, 0,
+                  [&](hipStream_t s) { return enqueue_heads_draft(c, s, K, seed, d_dev, D_dev); });
+}
+
 int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
                 int32_t* out_dev, int32_t* n_acc_dev, float* T_dev, float* logits_dev) {
   if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_verify: null context");
@@ -774,7 +899,8 @@ int spec_commit(spec_ctx* c, const int32_t* out_dev, const int32_t* n_acc_dev) {
   if (!c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_commit: no verify pending");
   HIPTRY(c, hipSetDevice(c->device));
   HIPTRY(c, launch_commit(c->st, c->hist, c->hist_cap, out_dev, n_acc_dev, c->drafted_k, c->last_k,
-                         c->stream));
+                         c->x, c->T.d, c->h_last, c->stream));
+  c->h_valid = true;
   c->LT_ub += c->last_k + 1;
   c->lag_ub = c->drafted_k > 0 ? 1 : c->lag_ub + c->last_k + 1;
   c->drafted_k = 0;
