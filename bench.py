@@ -41,9 +41,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """(bytes per launch, note) from the committed counter summary, or
-    (None, reason) when there is none or the kernel sources changed since."""
+def measured_traffic(target_only: bool = False):
+    """(bytes per launch, note) from the committed counter summary -- the
+    1:2 target/draft launch mix of the draft-model rounds, or the target
+    launches alone -- or (None, reason) when there is none or the kernel
+    sources changed since."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as fh:
@@ -53,7 +55,8 @@ def measured_traffic():
                     kv[k.strip()] = v.strip()
         if kv.get("kernel_source_sha256") != kernel_source_digest():
             return None, "kernel sources changed since the counters were taken"
-        return int(kv["traffic_bytes_per_launch"]), os.path.relpath(TRAFFIC_FILE, ROOT)
+        key = "traffic_bytes_per_launch_target" if target_only else "traffic_bytes_per_launch"
+        return int(kv[key]), os.path.relpath(TRAFFIC_FILE, ROOT) + " (" + key + ")"
     except (OSError, KeyError, ValueError):
         return None, "no counter summary"
 
@@ -96,8 +99,9 @@ def main():
     ap.add_argument("--pair", default="8b", choices=["toy", "1.3b", "8b", "31b"])
     ap.add_argument("--prompt-len", type=int, default=None)
     ap.add_argument("--greedy", action="store_true")
-    ap.add_argument("--drafter", default="model", choices=["model", "ngram"],
-                    help="draft model (default) or the prompt-lookup drafter (spec_draft_ngram)")
+    ap.add_argument("--drafter", default="model", choices=["model", "ngram", "heads"],
+                    help="draft model (default), the prompt-lookup drafter (spec_draft_ngram) or "
+                         "K multi-token-prediction heads on the target (spec_draft_heads)")
     ap.add_argument("--ngram-n", type=int, default=3, help="longest key of the n-gram drafter")
     ap.add_argument("--gemm-sweep", action="store_true",
                     help="batched verify: time the weight-streaming GEMM (spec_mat_mul) on the "
@@ -162,6 +166,8 @@ def main():
     ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=args.greedy,
                        use_graphs=True, profile_kernels=False)
     log(f"spec_init (pack + prefill {plen} tokens) in {time.time() - t0:.1f}s")
+    if args.drafter == "heads":
+        sd.spec_heads_init(ctx, synth.heads_torch(tcfg, K), K)
 
     V = tcfg.vocab
     d = torch.zeros(K, dtype=torch.int32, device="cuda")
@@ -176,6 +182,8 @@ def main():
             ev[0].record(stream)
         if args.drafter == "ngram":
             sd.spec_draft_ngram(ctx, K, args.ngram_n, d, D)
+        elif args.drafter == "heads":
+            sd.spec_draft_heads(ctx, K, seed, d, D)
         else:
             sd.spec_draft(ctx, K, seed, d, D)
         if ev is not None:
@@ -217,9 +225,15 @@ def main():
     L_mid = plen + tokens // 2 + st0["target_len"] - plen
     vbytes = verify_pass_bytes(tcfg, K, L_mid)
     vgbs = vbytes / (np.median(verify_ms) / 1e3) / 1e9
-    # the prompt-lookup drafter reads the history and writes K one-hot rows
-    dbytes = (K * draft_step_bytes(dcfg, L_mid) if args.drafter == "model"
-              else K * V * 4 + (L_mid + 1) * 4)
+    # the prompt-lookup drafter reads the history and writes K one-hot rows;
+    # the heads stream their K [d][d] matrices and the LM head once and
+    # write K rows
+    if args.drafter == "model":
+        dbytes = K * draft_step_bytes(dcfg, L_mid)
+    elif args.drafter == "heads":
+        dbytes = K * tcfg.d_model ** 2 * 2 + V * tcfg.d_model * 2 + K * V * 4
+    else:
+        dbytes = K * V * 4 + (L_mid + 1) * 4
     dgbs = dbytes / (np.median(draft_ms) / 1e3) / 1e9
 
     # dominant kernel: the feed-forward gate/up GEMM.  A second timed region
@@ -246,7 +260,7 @@ def main():
         avg_bytes = (b_d + b_t) / n_l
         avg_ms = float((kt_d.sum() + kt_t.sum()) / n_l)
         ach = avg_bytes / (avg_ms / 1e3) / 1e9
-        traffic, traffic_note = measured_traffic()
+        traffic, traffic_note = measured_traffic(target_only=len(kt_d) == 0)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "traffic_note": traffic_note,
@@ -258,8 +272,9 @@ def main():
                 "avg_algorithmic_bytes": int(avg_bytes),
                 "target_launch_us": round(float(kt_t.mean()) * 1e3, 2),
                 "target_GBs": round(gateup_bytes(tcfg, K + 1) / (float(kt_t.mean()) / 1e3) / 1e9, 1),
-                "draft_launch_us": round(float(kt_d.mean()) * 1e3, 2),
-                "draft_GBs": round(gateup_bytes(dcfg, 1) / (float(kt_d.mean()) / 1e3) / 1e9, 1)}
+                "draft_launch_us": round(float(kt_d.mean()) * 1e3, 2) if len(kt_d) else None,
+                "draft_GBs": (round(gateup_bytes(dcfg, 1) / (float(kt_d.mean()) / 1e3) / 1e9, 1)
+                              if len(kt_d) else None)}
 
     # acceptance record of the timed rounds: the context counts every commit
     # by (K, n_acc); alpha_i = P(d_i accepted | d_1..d_{i-1} accepted)
@@ -327,8 +342,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{tcfg.name} target + "
-                        + (f"{dcfg.name} draft" if args.drafter == "model"
-                           else f"prompt-lookup drafter (keys up to {args.ngram_n} tokens)")
+                        + {"model": f"{dcfg.name} draft",
+                           "ngram": f"prompt-lookup drafter (keys up to {args.ngram_n} tokens)",
+                           "heads": f"{K} multi-token-prediction heads (random-init, "
+                                    f"z = h + silu(W h), target LM head)"}[args.drafter]
                         + f", batch 1, K={K}, prompt {plen}, "
                         f"{'greedy' if args.greedy else 'temperature-1 sampling'}, random-init bf16",
             "K": K, "batch": 1, "prompt_len": plen, "mode": "greedy" if args.greedy else "sampling",
