@@ -19,7 +19,7 @@ short text summaries:
       factor that makes the same counter read the known size of a plain copy
       kernel (N bytes read and N bytes written per launch).
 
-Usage:  python -m speculative_decoding_02_amd.profsum trace gpurun_out/prof_kt
+Usage:  python -m speculative_decoding_02_amd.profsum trace prof/kt
 """
 from __future__ import annotations
 
