@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 # HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, with the hash of the kernel sources
 # they were taken with; used only while the sources still hash the same.
@@ -252,10 +253,11 @@ def main():
     roof = None
     if not args.no_kernel_timing:
         sd.spec_set_profiling(ctx, True)
-        kts = []
+        kts, heads_ms = [], []
         for _ in range(args.kernel_rounds):
             one_round()
             kts.append(sd.spec_kernel_times(ctx))
+            heads_ms.append(sd.spec_head_time(ctx))
         sd.spec_set_profiling(ctx, False)
         n_draft = K * dcfg.n_layers if args.drafter == "model" else 0
         kt_d = np.concatenate([k[:n_draft] for k in kts])
@@ -281,6 +283,24 @@ def main():
                 "draft_launch_us": round(float(kt_d.mean()) * 1e3, 2) if len(kt_d) else None,
                 "draft_GBs": (round(gateup_bytes(dcfg, 1) / (float(kt_d.mean()) / 1e3) / 1e9, 1)
                               if len(kt_d) else None)}
+
+    # the verify pass's LM head: (K+1) rows x vocab x d, timed like the
+    # gate/up GEMM in the stamped rounds; matrix-core use against the dense
+    # bf16 peak, useful (K+1 rows) and issued (the 16-row MFMA tile)
+    lm_head = None
+    if roof is not None:
+        hm = [x for x in heads_ms if x > 0]
+        if hm:
+            t = float(np.mean(hm)) / 1e3
+            flop = 2 * (K + 1) * V * tcfg.d_model
+            lm_bytes = V * tcfg.d_model * 2 + (K + 1) * V * 4
+            lm_head = {"us": round(t * 1e6, 2), "launches": len(hm),
+                       "GB_s": round(lm_bytes / t / 1e9, 1),
+                       "useful_TFLOP_s": round(flop / t / 1e12, 2),
+                       "mfma_util": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 5),
+                       "mfma_util_issued": round(2 * 16 * V * tcfg.d_model / t / 1e12
+                                                 / PEAK_BF16_TFLOPS, 5),
+                       "peak_TFLOP_s": PEAK_BF16_TFLOPS}
 
     # acceptance record of the timed rounds: the context counts every commit
     # by (K, n_acc); alpha_i = P(d_i accepted | d_1..d_{i-1} accepted)
@@ -374,6 +394,7 @@ def main():
         "read_ceiling": ceiling,
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
+        "lm_head": lm_head,
         "cpu_baseline": None,
     }
     log(json.dumps({k: res[k] for k in ("value", "ms_per_step", "verify_pass", "draft_loop",

@@ -256,6 +256,13 @@ int spec_kernel_times(spec_ctx* ctx, float* ms_out, int32_t cap, int32_t* n_out)
  * Also set at creation by spec_init_params.profile_kernels. */
 int spec_set_profiling(spec_ctx* ctx, int32_t enable);
 
+/* Measurement helper: the duration in ms of the LM head of the last
+ * spec_verify run with profiling on, from the same per-workgroup end stamps
+ * (the latest LM-head workgroup end minus the latest end of the last layer's
+ * down projection, launch overhead included); -1 when that verify ran
+ * without profiling.  Synchronises.  Errors: SPEC_ERR_ARG, SPEC_ERR_HIP. */
+int spec_head_time(spec_ctx* ctx, float* ms_out);
+
 /* A packed weight matrix multiplied by a batch of activation rows: the
  * verify pass's weight-streaming GEMM for M = B * (K+1) rows of B sequences
  * ([en] Floor 6, "crowded tower days": with a large batch every weight read

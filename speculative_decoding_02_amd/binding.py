@@ -96,6 +96,7 @@ def lib():
         L.spec_get_history.argtypes = [_p, _p, _i32]
         L.spec_kernel_times.argtypes = [_p, _p, _i32, C.POINTER(_i32)]
         L.spec_set_profiling.argtypes = [_p, _i32]
+        L.spec_head_time.argtypes = [_p, C.POINTER(C.c_float)]
         L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
                                          _p, _p]
         L.spec_read_ceiling.argtypes = [_p, _u64, _i32, _p, C.POINTER(C.c_double)]
@@ -106,7 +107,7 @@ def lib():
 EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_heads_init", "spec_draft_heads",
             "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
-            "spec_kernel_times", "spec_set_profiling", "spec_accept_reject", "spec_expected_tokens",
+            "spec_kernel_times", "spec_set_profiling", "spec_head_time", "spec_accept_reject", "spec_expected_tokens",
             "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
             "spec_mat_destroy", "spec_read_ceiling")
 
@@ -281,6 +282,13 @@ def spec_kernel_times(ctx: Ctx, cap: int = 4096) -> np.ndarray:
     n = _i32()
     _check(lib().spec_kernel_times(ctx.handle, buf.ctypes.data, cap, C.byref(n)), ctx)
     return buf[: n.value].copy()
+
+
+def spec_head_time(ctx: Ctx) -> float:
+    """LM-head duration (ms) of the last profiled spec_verify, or -1."""
+    ms = C.c_float(-1.0)
+    _check(lib().spec_head_time(ctx.handle, C.byref(ms)), ctx)
+    return float(ms.value)
 
 
 def spec_set_profiling(ctx: Ctx, enable: bool) -> None:

@@ -125,6 +125,12 @@ struct spec_ctx {
   int ts_groups = 0;            // workgroups per stamp row (largest O / gate/up grid)
   int ts_next = 0;              // next slot while enqueueing a pass
   int prof_draft_n = 0, prof_verify_n = 0;  // slots written by the last calls
+  // the verify pass's LM head: end stamps of the last layer's down GEMM
+  // ([0][g]) and of the LM head ([1][g]); its duration is the latest LM-head
+  // end minus the latest down end (same convention as the gate/up slots)
+  unsigned long long* ts_head = nullptr;
+  int ts_head_groups = 0;
+  bool head_stamped = false;
   int wall_khz = 0;             // wall-clock counter rate
 };
 
@@ -351,7 +357,8 @@ GemmArgs gemm_base(spec_ctx* c, const Mat& w, const uint16_t* ap) {
 // -> gate/up (norm scale, SiLU*up) -> down (+residual).  The sums of squares
 // for each RMSNorm alternate between two buffers so a producer never writes
 // the partials its own consumer-to-be is still to read.
-hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows, bool profile) {
+hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows, bool profile,
+                          bool stamp_last_down = false) {
   hipError_t e = hipSuccess;
   int ssq_groups = m.d / 64;  // produced by the embedding
   float* ssq_in = c->ssq_a;
@@ -397,6 +404,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     GemmArgs dn = gemm_base(c, m.dn[l], c->ap_a);
     dn.resid = c->x; dn.ldr = m.d; dn.Ap_out = c->ap_x; dn.ssq_out = ssq_other;
     dn.gain_next = l + 1 < m.L ? m.attn_norm(l + 1) : m.final_norm();
+    if (stamp_last_down && l == m.L - 1) dn.ts_end = c->ts_head;
     e = launch_gemm(m.dn[l].plan.shape, EPI_RESID, dn, s);
     std::swap(ssq_in, ssq_other);
     ssq_groups = m.dn[l].plan.n_groups;
@@ -411,8 +419,9 @@ float* final_ssq(spec_ctx* c, const Model&) { return c->ssq_a; }
 
 // final norm + LM head (+ logits partials) + softmax into `dst`
 hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only, int n_rows,
-                        float* logits_dst, float* dst) {
+                        float* logits_dst, float* dst, bool stamp = false) {
   GemmArgs a = gemm_base(c, m.lm, c->ap_x);
+  if (stamp) a.ts_end = c->ts_head + c->ts_head_groups;
   a.ssq = final_ssq(c, m); a.ssq_groups = final_ssq_groups(m); a.eps = m.eps;
   a.last_row_only = last_row_only;
   a.out = logits_dst; a.ldo = m.V; a.lm_part = c->lm_part; a.n_valid = m.V;
@@ -463,8 +472,8 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
   float* Tb = Tdst ? Tdst : c->Tbuf;
   float* Lb = Ldst ? Ldst : c->logits;
   hipError_t e = enqueue_embed(c, m, s, EMB_VERIFY, K + 1, 0, 0, d);
-  if (e == hipSuccess) e = enqueue_layers(c, m, s, K + 1, c->profiling);
-  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, K + 1, Lb, Tb);
+  if (e == hipSuccess) e = enqueue_layers(c, m, s, K + 1, c->profiling, c->profiling);
+  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, K + 1, Lb, Tb, c->profiling);
   if (e == hipSuccess) {
     ArArgs ar{};
     ar.T = Tb; ar.D = Dp; ar.d = d; ar.B = 1; ar.K = K; ar.V = m.V;
@@ -582,7 +591,7 @@ void destroy_ctx(spec_ctx* c) {
   void* bufs[] = {c->x,      c->qf,      c->ssq_a,  c->ssq_b, c->ap_x,  c->ap_o,
                   c->ap_a,   c->logits,  c->Tbuf,   c->attn_wo, c->attn_ml, c->lm_part,
                   c->ar_ws,  c->rows,    c->st,     c->hist,  c->heads_arena, c->h_last,
-                  c->hn,     c->head_y};
+                  c->hn,     c->head_y,  c->ts_head};
   for (void* b : bufs) (void)hipFree(b);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
@@ -704,6 +713,8 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
     for (int l = 0; l < m->L; ++l)
       c->ts_groups = std::max({c->ts_groups, m->o[l].plan.n_groups, m->gu[l].plan.n_groups});
   TRYH(dalloc(&c->ts, (size_t)c->ts_cap * 2 * c->ts_groups));
+  c->ts_head_groups = std::max(c->T.lm.plan.n_groups, c->T.dn[c->T.L - 1].plan.n_groups);
+  TRYH(dalloc(&c->ts_head, (size_t)2 * c->ts_head_groups));
   TRYH(hipDeviceGetAttribute(&c->wall_khz, hipDeviceAttributeWallClockRate, c->device));
   if (c->wall_khz <= 0) return bail(fail(c, SPEC_ERR_HIP, "device reports no wall-clock rate"));
   TRYH(hipMemsetAsync(c->ap_x, 0, (size_t)32 * dmax, c->stream));
@@ -883,6 +894,10 @@ int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, con
                                (uint64_t)(uintptr_t)T_dev,
                                (uint64_t)(uintptr_t)logits_dev};
   const int vslot0 = c->p.k_max * c->D.L;
+  if (c->profiling)
+    HIPTRY(c, hipMemsetAsync(c->ts_head, 0, (size_t)2 * c->ts_head_groups * sizeof(unsigned long long),
+                             c->stream));
+  c->head_stamped = c->profiling;
   int r = run_pass(c, key, vslot0, c->T.L, [&](hipStream_t s) {
     return enqueue_verify(c, s, K, seed, d_dev, D_dev, out_dev, n_acc_dev, T_dev, logits_dev);
   });
@@ -975,6 +990,27 @@ int spec_kernel_times(spec_ctx* c, float* ms_out, int32_t cap, int32_t* n_out) {
   take(0, c->prof_draft_n, c->D, 0);
   take(c->p.k_max * c->D.L, c->prof_verify_n, c->T, 0);
   *n_out = std::min(n, cap);
+  return SPEC_OK;
+}
+
+int spec_head_time(spec_ctx* c, float* ms_out) {
+  if (!c || !ms_out) return fail(c, SPEC_ERR_ARG, "spec_head_time: null argument");
+  *ms_out = -1.0f;
+  if (!c->head_stamped) return SPEC_OK;
+  HIPTRY(c, hipStreamSynchronize(c->stream));
+  std::vector<unsigned long long> h((size_t)2 * c->ts_head_groups);
+  HIPTRY(c, hipMemcpy(h.data(), c->ts_head, h.size() * sizeof(unsigned long long),
+                      hipMemcpyDeviceToHost));
+  const Model& m = c->T;
+  unsigned long long d_end = 0, l_end = 0;
+  bool ok = true;
+  for (int w = 0; w < m.dn[m.L - 1].plan.n_groups; ++w) { ok = ok && h[w] != 0; d_end = std::max(d_end, h[w]); }
+  for (int w = 0; w < m.lm.plan.n_groups; ++w) {
+    const unsigned long long t = h[(size_t)c->ts_head_groups + w];
+    ok = ok && t != 0;
+    l_end = std::max(l_end, t);
+  }
+  if (ok && l_end > d_end) *ms_out = (float)((double)(l_end - d_end) / c->wall_khz);
   return SPEC_OK;
 }
 

@@ -100,9 +100,10 @@ def test_graph_and_eager_agree_and_repeat(toy):
 
 
 def test_profiling_rounds_match_and_time(toy):
-    """With profiling on, the graphs carry the gate/up GEMM's timestamp slots:
-    tokens and rows are the same as without, and every draft and verify
-    gate/up launch reports a positive duration, in launch order."""
+    """With profiling on, the graphs carry the gate/up GEMM's timestamp slots
+    and the verify pass's LM-head stamps: tokens and rows are the same as
+    without, every draft and verify gate/up launch and the LM head report a
+    positive duration (and the LM head none without profiling)."""
     import speculative_decoding_02_amd as sd
     tw, dw = toy
     prompt = synth.prompt(synth.TOY.vocab, 20, seed=6)
@@ -116,10 +117,14 @@ def test_profiling_rounds_match_and_time(toy):
         rounds = []
         for _ in range(4):
             rounds.append(gpu_round(sd, ctx, K, 31, b))
+            h = sd.spec_head_time(ctx)
             if prof:
                 t = sd.spec_kernel_times(ctx)
                 assert len(t) == K * synth.TOY_DRAFT.n_layers + synth.TOY.n_layers
                 assert np.all(t > 0) and np.all(t < 50.0), t
+                assert 0 < h < 50.0, h
+            else:
+                assert h == -1.0
         runs.append(rounds)
         sd.spec_destroy(ctx)
     for a, c in zip(runs[0], runs[1]):
