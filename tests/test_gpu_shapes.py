@@ -2,7 +2,8 @@
 configurations bench.py uses (same GEMM plans, attention tiles, vocabulary
 sizes), with fewer layers so the fp64 oracle finishes in seconds:
 
-  * 8B-shaped target slice (d 4096, 32/8 heads x 128, FFN 14336, vocab
+  * the full 8B-shaped pair (32 + 16 layers) with a short prompt, and an
+    8B-shaped target slice (d 4096, 32/8 heads x 128, FFN 14336, vocab
     128256) with a 1B-shaped draft slice (d 2048, 32/8 x 64, tied head);
   * 31B-shaped slice (d 5376, 32/16 heads x 168, FFN 21504, vocab 262144)
     with a 4B-shaped draft slice (20/4 heads x 128: five query heads per KV
@@ -49,6 +50,14 @@ def run_case(tcfg, dcfg, prompt_len, K, rounds, greedy, share=(), seed=1003, max
     print(f"{tcfg.name}: logit err {sh.max_logit_err:.2e}, prob err {sh.max_prob_err:.2e}, "
           f"draft prob err {sh.max_draft_prob_err:.2e}, near-ties {sh.near_ties}")
     sd.spec_destroy(ctx)
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_8b_full_depth(greedy):
+    """The whole 8B-shaped target (32 layers) and 1B-shaped draft (16 layers),
+    K = 4, exactly as bench.py builds them, with a short prompt so the fp64
+    oracle keeps up: two teacher-forced rounds."""
+    run_case(synth.L8B, synth.L8B_DRAFT, prompt_len=16, K=4, rounds=2, greedy=greedy, max_extra=16)
 
 
 @pytest.mark.parametrize("greedy", [False, True])
