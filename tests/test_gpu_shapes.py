@@ -2,7 +2,8 @@
 configurations bench.py uses (same GEMM plans, attention tiles, vocabulary
 sizes), with fewer layers so the fp64 oracle finishes in seconds:
 
-  * the full 8B-shaped pair (32 + 16 layers) with a short prompt, and an
+  * the full 8B-shaped pair (32 + 16 layers) and the full 31B-shaped pair
+    (60 + 34 layers) with short prompts, and an
     8B-shaped target slice (d 4096, 32/8 heads x 128, FFN 14336, vocab
     128256) with a 1B-shaped draft slice (d 2048, 32/8 x 64, tied head);
   * 31B-shaped slice (d 5376, 32/16 heads x 168, FFN 21504, vocab 262144)
@@ -58,6 +59,12 @@ def test_8b_full_depth(greedy):
     K = 4, exactly as bench.py builds them, with a short prompt so the fp64
     oracle keeps up: two teacher-forced rounds."""
     run_case(synth.L8B, synth.L8B_DRAFT, prompt_len=16, K=4, rounds=2, greedy=greedy, max_extra=16)
+
+
+def test_31b_full_depth():
+    """The whole 31B-shaped target (60 layers, ~55 GB of bf16 weights) and
+    4B-shaped draft (34 layers), K = 5, one teacher-forced round."""
+    run_case(synth.G31B, synth.G31B_DRAFT, prompt_len=8, K=5, rounds=1, greedy=False, max_extra=16)
 
 
 @pytest.mark.parametrize("greedy", [False, True])
