@@ -161,7 +161,10 @@ int spec_heads_init(spec_ctx* ctx, const void* W_dev, int32_t n_heads);
  * with Philox word w0 at that position (seed, stream_id), or its top token in
  * greedy mode -- the same draw spec_draft makes.  Each D row depends on the
  * committed prefix only, not on the earlier drafts of the round; spec_verify
- * takes the pair unchanged.  Asynchronous on the context stream.
+ * takes the pair unchanged.  Called after spec_draft in the same round, its
+ * drafts replace the draft model's and the draft cache's committed length
+ * stays where it was (the next spec_draft catches up over the committed
+ * text).  Asynchronous on the context stream.
  *   d_dev: int32 [K]; D_dev: fp32 [K][vocab].
  * Errors: SPEC_ERR_ARG (K outside 1..min(n_heads, k_max), null pointers),
  * SPEC_ERR_STATE (no heads; a verify is pending; a one-token prompt and no

@@ -63,6 +63,9 @@ struct Model {
   const uint16_t* final_norm() const { return norms + (size_t)2 * L * d; }
 };
 
+// First element of a graph-cache key: the kind of pass captured.
+constexpr uint64_t kPassDraft = 1, kPassVerify = 2, kPassNgram = 3, kPassHeads = 4;
+
 struct GraphEntry {
   hipGraphExec_t exec = nullptr;
 };
@@ -773,7 +776,7 @@ int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_d
     }
     c->lag_ub = hs.LT - hs.LD;
   }
-  std::vector<uint64_t> key = {1, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
+  std::vector<uint64_t> key = {kPassDraft, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev};
   int r = run_pass(c, key, 0, K * c->D.L,
                    [&](hipStream_t s) { return enqueue_draft(c, s, K, seed, d_dev, D_dev); });
@@ -790,7 +793,7 @@ int spec_draft_ngram(spec_ctx* c, int32_t K, int32_t n_max, int32_t* d_dev, floa
     return fail(c, SPEC_ERR_ARG, fmt("n_max=%d outside 1..%d", n_max, kNgramMaxN));
   if (!d_dev || (!D_dev && !c->p.greedy)) return fail(c, SPEC_ERR_ARG, "spec_draft_ngram: null output");
   HIPTRY(c, hipSetDevice(c->device));
-  std::vector<uint64_t> key = {3, (uint64_t)K, (uint64_t)n_max, (uint64_t)(uintptr_t)d_dev,
+  std::vector<uint64_t> key = {kPassNgram, (uint64_t)K, (uint64_t)n_max, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev};
   int r = run_pass(c, key, 0, 0, [&](hipStream_t s) {
     NgramArgs a{};
@@ -814,7 +817,7 @@ int spec_heads_init(spec_ctx* c, const void* W_dev, int32_t n_heads) {
   HIPTRY(c, hipStreamSynchronize(c->stream));
   // drop the previous heads and the graphs that captured them
   for (auto it = c->graph_cache.begin(); it != c->graph_cache.end();) {
-    if (it->first[0] == 3) {
+    if (it->first[0] == kPassHeads) {
       if (it->second.exec) (void)hipGraphExecDestroy(it->second.exec);
       it = c->graph_cache.erase(it);
     } else {
@@ -862,10 +865,14 @@ int spec_draft_heads(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, floa
     if (hs.LT + K > c->p.max_seq)
       return fail(c, SPEC_ERR_CAPACITY, "draft positions would exceed max_seq");
   }
-  std::vector<uint64_t> key = {3, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
+  std::vector<uint64_t> key = {kPassHeads, (uint64_t)K, seed, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev, (uint64_t)(uintptr_t)c->heads_arena};
-  return run_pass(c, key, 0, 0,
-                  [&](hipStream_t s) { return enqueue_heads_draft(c, s, K, seed, d_dev, D_dev); });
+  int r = run_pass(c, key, 0, 0,
+                   [&](hipStream_t s) { return enqueue_heads_draft(c, s, K, seed, d_dev, D_dev); });
+  if (r) return r;
+  c->drafted_k = 0;  // the draft model computed none of these rows: its cache keeps its length
+  c->prof_draft_n = 0;
+  return SPEC_OK;
 }
 
 int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, const float* D_dev,
@@ -884,7 +891,7 @@ int spec_verify(spec_ctx* c, int32_t K, uint64_t seed, const int32_t* d_dev, con
     if (hs.LT + K + 1 > c->p.max_seq)
       return fail(c, SPEC_ERR_CAPACITY, "verify positions would exceed max_seq");
   }
-  std::vector<uint64_t> key = {2,
+  std::vector<uint64_t> key = {kPassVerify,
                                (uint64_t)K,
                                seed,
                                (uint64_t)(uintptr_t)d_dev,

@@ -176,6 +176,36 @@ def test_heads_and_draft_model_take_turns(toy):
     np.testing.assert_array_equal(gen, ref)
 
 
+def test_heads_override_a_draft_model_pass(toy):
+    """A draft-model pass whose drafts are then replaced by the heads' leaves
+    the draft cache's committed length where it was (the draft model computed
+    no row of what gets committed), so the next draft-model rounds catch up
+    over the committed text and match the oracle."""
+    import speculative_decoding_02_amd as sd
+    from gpu_util import Shadow, gpu_round
+    tw, dw, W = toy
+    prompt = synth.prompt(synth.TOY.vocab, 20, seed=9)
+    K, seed = 3, synth.SEED_PHILOX
+    ctx, keep = toy_ctx(sd, tw, dw, prompt, K, False)
+    sd.spec_heads_init(ctx, heads_dev(W), N_HEADS)
+    sh = Shadow(synth.TOY, tw, synth.TOY_DRAFT, dw, prompt, 160, K, seed, False)
+    b = Buffers(K, synth.TOY.vocab)
+    for r in range(6):
+        if r % 3 == 1:
+            sd.spec_draft(ctx, K, seed, b.d, b.D)
+            g = heads_round(sd, ctx, K, seed, b)
+            n, LT = g["nacc"], sh.LT
+            oracle.forward(sh.T, sh.kvT, [sh.hist[LT]] + [int(x) for x in g["d"]], LT,
+                           want_logits=False)
+            sh.hist += [int(x) for x in g["out"][: n + 1]]
+            sh.LT = LT + n + 1
+        else:
+            sh.check_round(gpu_round(sd, ctx, K, seed, b))
+        st = sd.spec_get_state(ctx)
+        assert st["device_error"] == 0
+        assert (st["target_len"], st["draft_len"]) == (sh.LT, sh.LD), r
+
+
 def test_zero_heads_reproduce_the_verified_row(toy):
     """With zero head matrices every head is the target's own LM head on the
     kept state, i.e. row n_acc of the last verify's T (to the pass's
