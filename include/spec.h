@@ -286,6 +286,85 @@ int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out);
 int spec_mat_mul(spec_mat* m, const float* X_dev, int32_t M, float* Y_dev, void* hip_stream);
 int spec_mat_destroy(spec_mat* m);
 
+/* Batched verification: B sequences decoded together against one target
+ * ([en] Floor 6, "crowded tower days"; [zh] Level 6: with many requests at
+ * once every weight read serves B (K+1) rows, and the pass moves from memory
+ * bound toward compute bound).  Each sequence keeps its own history,
+ * positions and paged KV cache, and gets its own accept/reject decision;
+ * sequence b draws its Philox words with sequence index s = b (counter
+ * (p, b, stream_id, 0), the same words spec_verify uses for s = 0), so
+ * sequence b's results are exactly those of a single-sequence verify of its
+ * rows with that index.  Drafts come from the caller (any drafter) or from
+ * spec_batch_draft_ngram.
+ * Limits: 1 <= n_seq <= SPEC_BATCH_MAX_SEQ, 1 <= k_max <= SPEC_K_MAX,
+ * n_seq * (k_max + 1) <= 128 activation rows; every prompt has n_prompt
+ * tokens; the target follows spec_model_desc's shape rules. */
+#define SPEC_BATCH_MAX_SEQ 32
+
+typedef struct spec_batch_params {
+  spec_model_desc target;
+  int32_t n_seq;             /* B */
+  int32_t k_max;             /* largest K later calls may use */
+  int32_t max_seq;           /* token capacity of each sequence's cache (>= n_prompt + k_max + 1) */
+  int32_t greedy;            /* 1: greedy checking; 0: sampling at T = 1 */
+  int32_t use_graphs;        /* 1: replay the verify pass from captured hipGraphs */
+  uint64_t stream_id;        /* Philox counter word c */
+  void* hip_stream;          /* hipStream_t to enqueue on; NULL: the context creates one */
+} spec_batch_params;
+
+typedef struct spec_batch spec_batch;
+
+/* Creates a batch context: packs the target weights (its own copy), allocates
+ * B paged caches and the workspaces, and prefills prompts_host[b][0..n-2] of
+ * every sequence; prompts_host[b][n-1] is sequence b's pending token.
+ *   prompts_host: int32 [n_seq][n_prompt] (host).
+ * Synchronises.  Errors: SPEC_ERR_ARG (shapes, limits, n_prompt < 1, token
+ * ids), SPEC_ERR_CAPACITY, SPEC_ERR_OOM, SPEC_ERR_HIP.  On error *out is NULL. */
+int spec_batch_init(const spec_batch_params* p, const int32_t* prompts_host, int32_t n_prompt,
+                    spec_batch** out);
+
+/* Prompt-lookup drafts for every sequence (the drafter of spec_draft_ngram,
+ * applied to each sequence's own history).
+ *   d_dev: int32 [n_seq][K]; D_dev: fp32 [n_seq][K][vocab] one-hot rows (may
+ *   be NULL in greedy mode).
+ * Errors: SPEC_ERR_ARG (K outside 1..k_max, n_max outside 1..8, null). */
+int spec_batch_draft_ngram(spec_batch* bc, int32_t K, int32_t n_max, int32_t* d_dev, float* D_dev);
+
+/* One target pass over the B (K+1) rows [pending_b, d_b1..d_bK] of every
+ * sequence (weights streamed once for the whole batch), the row softmax, and
+ * the rule per sequence, as spec_verify does for one sequence.
+ *   d_dev: int32 [n_seq][K]; D_dev: fp32 [n_seq][K][vocab] (unused in greedy
+ *   mode, may be NULL there); out_dev: int32 [n_seq][K+1]; n_acc_dev: int32
+ *   [n_seq]; T_dev / logits_dev: optional fp32 [n_seq][K+1][vocab] copies of
+ *   the target rows / logits (NULL: internal buffers).
+ * Errors: SPEC_ERR_ARG (K outside 1..k_max, null pointers), SPEC_ERR_STATE (a
+ * verify is pending), SPEC_ERR_CAPACITY (a sequence's positions would pass
+ * max_seq). */
+int spec_batch_verify(spec_batch* bc, int32_t K, uint64_t seed, const int32_t* d_dev,
+                      const float* D_dev, int32_t* out_dev, int32_t* n_acc_dev, float* T_dev,
+                      float* logits_dev);
+
+/* Commits the last verify of every sequence from its outputs (same pointers
+ * or copies): hist_b gets out[b][0..n_acc[b]], length L_b += n_acc[b] + 1;
+ * the cache slots of rejected drafts are overwritten by the next pass.
+ * Errors: SPEC_ERR_ARG (null), SPEC_ERR_STATE (no verify pending). */
+int spec_batch_commit(spec_batch* bc, const int32_t* out_dev, const int32_t* n_acc_dev);
+
+/* Waits for the context's stream. */
+int spec_batch_sync(spec_batch* bc);
+/* Synchronises, then copies every sequence's committed length L_b (the
+ * pending token sits at hist_b[L_b]) and its sticky device error bits (1: a
+ * token id out of range, 4: a position past max_seq); err_host may be NULL.
+ *   len_host, err_host: int32 [n_seq]. */
+int spec_batch_get_state(spec_batch* bc, int32_t* len_host, int32_t* err_host);
+/* Synchronises, then copies hist_b[0..n) of sequence b into host_out. */
+int spec_batch_get_history(spec_batch* bc, int32_t b, int32_t* host_out, int32_t n);
+/* Last error message of the context (or of the thread's last failed call
+ * when bc is NULL). */
+const char* spec_batch_last_error(const spec_batch* bc);
+/* Synchronises and frees everything the context owns; NULL accepted. */
+int spec_batch_destroy(spec_batch* bc);
+
 /* Choosing K from the measured acceptance rate (host-side helpers; no
  * context, no device work).
  * spec_expected_tokens: mean tokens one round yields when each of its K

@@ -8,4 +8,7 @@ from .binding import (  # noqa: F401
     spec_stream, spec_get_state, spec_get_history, spec_kernel_times, spec_set_profiling, spec_head_time,
     spec_accept_reject, spec_expected_tokens, spec_alpha_from_tokens, spec_choose_k,
     spec_mat_create, spec_mat_mul, spec_mat_destroy, spec_read_ceiling,
+    Batch, SPEC_BATCH_MAX_SEQ, spec_batch_init, spec_batch_draft_ngram, spec_batch_verify,
+    spec_batch_commit, spec_batch_sync, spec_batch_get_state, spec_batch_get_history,
+    spec_batch_last_error, spec_batch_destroy,
 )

@@ -53,6 +53,15 @@ class SpecInitParams(C.Structure):
     ]
 
 
+class SpecBatchParams(C.Structure):
+    _fields_ = [
+        ("target", SpecModelDesc), ("n_seq", _i32), ("k_max", _i32), ("max_seq", _i32),
+        ("greedy", _i32), ("use_graphs", _i32), ("stream_id", _u64), ("hip_stream", _p),
+    ]
+
+
+SPEC_BATCH_MAX_SEQ = 32
+
 K_BINS = 8  # SPEC_K_MAX + 1
 
 
@@ -100,6 +109,16 @@ def lib():
         L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
                                          _p, _p]
         L.spec_read_ceiling.argtypes = [_p, _u64, _i32, _p, C.POINTER(C.c_double)]
+        L.spec_batch_init.argtypes = [C.POINTER(SpecBatchParams), _p, _i32, C.POINTER(_p)]
+        L.spec_batch_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
+        L.spec_batch_verify.argtypes = [_p, _i32, _u64, _p, _p, _p, _p, _p, _p]
+        L.spec_batch_commit.argtypes = [_p, _p, _p]
+        L.spec_batch_sync.argtypes = [_p]
+        L.spec_batch_get_state.argtypes = [_p, _p, _p]
+        L.spec_batch_get_history.argtypes = [_p, _i32, _p, _i32]
+        L.spec_batch_last_error.argtypes = [_p]
+        L.spec_batch_last_error.restype = C.c_char_p
+        L.spec_batch_destroy.argtypes = [_p]
         _lib = L
     return _lib
 
@@ -109,7 +128,9 @@ EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_heads_init", "s
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
             "spec_kernel_times", "spec_set_profiling", "spec_head_time", "spec_accept_reject", "spec_expected_tokens",
             "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
-            "spec_mat_destroy", "spec_read_ceiling")
+            "spec_mat_destroy", "spec_read_ceiling", "spec_batch_init", "spec_batch_draft_ngram",
+            "spec_batch_verify", "spec_batch_commit", "spec_batch_sync", "spec_batch_get_state",
+            "spec_batch_get_history", "spec_batch_last_error", "spec_batch_destroy")
 
 
 def _check(rc: int, ctx=None):
@@ -312,3 +333,79 @@ def spec_accept_reject(T, D, d, seed: int, pos, stream_id: int, greedy: bool, ou
     _check(lib().spec_accept_reject(_ptr(T), _ptr(D), _ptr(d), B, K1 - 1, V, seed, _ptr(pos),
                                     stream_id, int(bool(greedy)), _ptr(out), _ptr(n_acc),
                                     stream or None))
+
+
+# ------------------------------------------------------- batched verify --
+class Batch:
+    """Owns a spec_batch* handle (B sequences verified together)."""
+
+    def __init__(self, handle: int, n_seq: int):
+        self.handle = handle
+        self.n_seq = n_seq
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib().spec_batch_destroy(self.handle)
+            self.handle = None
+
+
+def _bcheck(rc: int, bc: Optional[Batch] = None):
+    if rc != SPEC_OK:
+        h = bc.handle if isinstance(bc, Batch) else None
+        raise SpecError(rc, lib().spec_batch_last_error(h).decode(errors="replace"))
+
+
+def spec_batch_init(target_cfg, target_w, prompts, *, k_max: int, max_seq: int, greedy: bool,
+                    use_graphs: bool = True, stream_id: int = 0, stream: int = 0) -> Batch:
+    """prompts: int [n_seq][n_prompt] (one row per sequence)."""
+    pr = np.ascontiguousarray(prompts, dtype=np.int32)
+    if pr.ndim != 2:
+        raise ValueError("prompts must be [n_seq][n_prompt]")
+    p = SpecBatchParams()
+    p.target = model_desc(target_cfg, target_w)
+    p.n_seq = pr.shape[0]; p.k_max = k_max; p.max_seq = max_seq; p.greedy = int(bool(greedy))
+    p.use_graphs = int(bool(use_graphs)); p.stream_id = stream_id; p.hip_stream = stream or None
+    h = _p()
+    _bcheck(lib().spec_batch_init(C.byref(p), pr.ctypes.data, pr.shape[1], C.byref(h)))
+    return Batch(h.value, pr.shape[0])
+
+
+def spec_batch_draft_ngram(bc: Batch, K: int, n_max: int, d, D=None) -> None:
+    _bcheck(lib().spec_batch_draft_ngram(bc.handle, K, n_max, _ptr(d), _ptr(D)), bc)
+
+
+def spec_batch_verify(bc: Batch, K: int, seed: int, d, D, out, n_acc, T=None, logits=None) -> None:
+    _bcheck(lib().spec_batch_verify(bc.handle, K, seed, _ptr(d), _ptr(D), _ptr(out), _ptr(n_acc),
+                                    _ptr(T), _ptr(logits)), bc)
+
+
+def spec_batch_commit(bc: Batch, out, n_acc) -> None:
+    _bcheck(lib().spec_batch_commit(bc.handle, _ptr(out), _ptr(n_acc)), bc)
+
+
+def spec_batch_sync(bc: Batch) -> None:
+    _bcheck(lib().spec_batch_sync(bc.handle), bc)
+
+
+def spec_batch_get_state(bc: Batch) -> dict:
+    ln = np.zeros(bc.n_seq, np.int32)
+    err = np.zeros(bc.n_seq, np.int32)
+    _bcheck(lib().spec_batch_get_state(bc.handle, ln.ctypes.data, err.ctypes.data), bc)
+    return {"len": ln, "device_error": err}
+
+
+def spec_batch_get_history(bc: Batch, b: int, n: int) -> np.ndarray:
+    out = np.zeros(n, np.int32)
+    _bcheck(lib().spec_batch_get_history(bc.handle, b, out.ctypes.data, n), bc)
+    return out
+
+
+def spec_batch_last_error(bc: Optional[Batch] = None) -> str:
+    h = bc.handle if isinstance(bc, Batch) else None
+    return lib().spec_batch_last_error(h).decode(errors="replace")
+
+
+def spec_batch_destroy(bc: Batch) -> None:
+    if bc.handle:
+        lib().spec_batch_destroy(bc.handle)
+        bc.handle = None

@@ -11,7 +11,7 @@ OBJ = os.path.join(ROOT, "_build", "libspec")
 LIB = os.path.join(HERE, "libspec.so")
 RUNNER = os.path.join(HERE, "spec_run")   # native driver of the C ABI (no Python in the process)
 SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_accept.hip", "k_ngram.hip", "k_gemm_rows.hip",
-           "k_heads.hip", "spec_api.cpp"]
+           "k_heads.hip", "k_batch.hip", "spec_api.cpp", "spec_batch.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SPEC_ARCH", "gfx950")

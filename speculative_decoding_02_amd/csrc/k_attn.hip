@@ -28,6 +28,9 @@
 //      partials are loaded at once and combined with running-max rescaling,
 //      per thread and then across threads in a fixed order (deterministic);
 //      it writes the packed A operand of the O projection.
+// A batch of sequences runs in the same two launches: the sequence index
+// extends grid.z of the partial kernel and grid.y of the merge, and selects
+// the sequence's pass descriptor, block table, query fragments and workspace.
 #include "kernels.h"
 
 namespace spec {
@@ -70,18 +73,21 @@ template <int NES>
 __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   constexpr int NET = 2 * NES;            // e-tiles of 16 covering 32*NES dims
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
-  const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z;
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
   const int n_qt_max = (G + 1) / 2;
+  const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z % n_qt_max;
+  const int seq = blockIdx.z / n_qt_max;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
   const int key0 = c * kAttnChunk;
+  const int32_t* table = a.block_table + (size_t)seq * a.n_blocks;
+  const PassRows* rows = a.rows + seq;
 
   // Buffer loads: an offset at or past the resource's size reads as zero,
   // which masks padded dims and absent tiles without branches, so every load
   // of the wave is in flight at once.
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.kv_layer_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.kv_layer_bytes);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf, a.qf_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf + (size_t)seq * (a.qf_bytes / 2), a.qf_bytes);
   // Query fragments of this wave's tile.  Columns beyond this pass's query
   // vectors hold finite values from earlier passes; their scores are masked
   // below.  Issued before the pass descriptor is read, with the chunk's two
@@ -97,18 +103,19 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
       qf[es][p] = load16(rq, ok ? off : kOOB);
     }
   }
-  const int blk0 = a.block_table[2 * c];
-  const int blk1_any = a.block_table[min(2 * c + 1, a.n_blocks - 1)];
+  const int blk0 = table[2 * c];
+  const int blk1_any = table[min(2 * c + 1, a.n_blocks - 1)];
 
-  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int n_rows = rows->n_rows, pos0 = rows->pos0;
   const int n_keys = pos0 + n_rows;
   if (n_rows <= 0 || key0 >= n_keys) return;
   const int QG = G * n_rows, n_qt = (QG + 15) / 16;
   if (qt >= n_qt) return;
   const int blk1 = key0 + kBlock < n_keys ? blk1_any : blk0;
   const float scale = 1.0f / sqrtf((float)hd);
-  float* wso = a.ws_o + ((size_t)h * a.max_chunks + c) * a.qg_max * E16;
-  float2* wsml = a.ws_ml + ((size_t)h * a.max_chunks + c) * a.qg_max;
+  const size_t hs = (size_t)seq * n_kv + h;  // (sequence, kv head) slice of the workspace
+  float* wso = a.ws_o + (hs * a.max_chunks + c) * a.qg_max * E16;
+  float2* wsml = a.ws_ml + (hs * a.max_chunks + c) * a.qg_max;
 
   uint4 kf[2][NES][2];
 #pragma unroll
@@ -221,15 +228,16 @@ SPEC_DEVICE void merge_in(MergeState& st, float m, float l, const float* o) {
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __shared__ float s_o[256 * 9];
   __shared__ float s_m[4];
-  const int qi = blockIdx.x, h = blockIdx.y;
+  const int qi = blockIdx.x, h = blockIdx.y % a.n_kv, seq = blockIdx.y / a.n_kv;
+  const size_t hs = (size_t)seq * a.n_kv + h;  // (sequence, kv head) slice of the workspace
   const int hd = a.hd, G = a.n_q / a.n_kv;
   const int E16 = (hd + 15) / 16 * 16;
   const int n8 = hd / 8, ncg = 256 / n8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid / n8, d8 = tid % n8;
   const size_t cs_ml = (size_t)a.qg_max, cs_o = (size_t)a.qg_max * E16;
-  const float2* ml = a.ws_ml + (size_t)h * a.max_chunks * a.qg_max + qi;
-  const float* wo = a.ws_o + ((size_t)h * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
+  const float2* ml = a.ws_ml + hs * a.max_chunks * a.qg_max + qi;
+  const float* wo = a.ws_o + (hs * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
   const bool worker = cg < ncg;
 
   float4 v0[kMergeBatch], v1[kMergeBatch];
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   // the first batch is issued before the pass descriptor is read
   load(worker ? cg : 0);
 
-  const int n_rows = a.rows->n_rows, pos0 = a.rows->pos0;
+  const int n_rows = a.rows[seq].n_rows, pos0 = a.rows[seq].pos0;
   const int QG = G * n_rows;
   if (n_rows <= 0 || qi >= QG) return;
   const int n_keys = pos0 + n_rows;
@@ -295,33 +303,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = acc[1 + e] * inv;
     const int r = qi / G, gi = qi % G;
-    apack_store8(a.Ap_out, r, (h * G + gi) * hd + tid * 8, out);
+    apack_store8_rt(a.Ap_out, seq * a.seq_rows + r, (h * G + gi) * hd + tid * 8, out,
+                    a.a_tiles > 1 ? a.a_tiles : 1);
   }
 }
 
 template <int NES>
-static void launch_partial(const AttnArgs& a, hipStream_t s) {
+static void launch_partial(const AttnArgs& a, int n_seq, hipStream_t s) {
   const int n_qt_max = (a.n_q / a.n_kv + 1) / 2;  // 16-query tiles of kMaxRows rows
-  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv, n_qt_max), dim3(64), 0,
-                     s, a);
+  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv, n_qt_max * n_seq),
+                     dim3(64), 0, s, a);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {
   if (n_rows < 1 || n_rows > kMaxRows) return hipErrorInvalidValue;
+  const int n_seq = a.n_seq > 1 ? a.n_seq : 1;
+  if (n_seq > 1 && (a.seq_rows < n_rows || n_seq * a.seq_rows > 8 * a.a_tiles))
+    return hipErrorInvalidValue;
   switch ((a.hd + 31) / 32) {
-    case 1: launch_partial<1>(a, s); break;
-    case 2: launch_partial<2>(a, s); break;
-    case 3: launch_partial<3>(a, s); break;
-    case 4: launch_partial<4>(a, s); break;
-    case 5: launch_partial<5>(a, s); break;
-    case 6: launch_partial<6>(a, s); break;
-    case 7: launch_partial<7>(a, s); break;
-    case 8: launch_partial<8>(a, s); break;
+    case 1: launch_partial<1>(a, n_seq, s); break;
+    case 2: launch_partial<2>(a, n_seq, s); break;
+    case 3: launch_partial<3>(a, n_seq, s); break;
+    case 4: launch_partial<4>(a, n_seq, s); break;
+    case 5: launch_partial<5>(a, n_seq, s); break;
+    case 6: launch_partial<6>(a, n_seq, s); break;
+    case 7: launch_partial<7>(a, n_seq, s); break;
+    case 8: launch_partial<8>(a, n_seq, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_q / a.n_kv) * n_rows, a.n_kv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_q / a.n_kv) * n_rows, a.n_kv * n_seq), dim3(256),
+                     0, s, a);
   return hipGetLastError();
 }
 

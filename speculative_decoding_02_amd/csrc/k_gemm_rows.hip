@@ -13,7 +13,9 @@
 //    v_mfma_f32_16x16x32_bf16, [Kb][RT][64 lanes][8 bf16]: tile t carries the
 //    bf16 high parts of rows 8t..8t+7 in its rows 0-7 and their low parts
 //    (x - hi) in rows 8-15, the same ~16-bit activation precision as the
-//    verify pass.  Rows past M are zero.
+//    verify pass.  Rows past M are zero.  A batched verify's producers
+//    (norm, SiLU, attention merge) write this layout themselves, and the
+//    residual updates accumulate into Y.
 //  * A workgroup owns NB 16-column blocks for the whole of K; its W waves
 //    split K; for every k-block a wave multiplies its NB weight fragments by
 //    all RT row tiles, so each weight byte is read once whatever M is.  The
@@ -54,7 +56,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const float* X, int M, i
 
 template <int NB, int W, int RT>
 __global__ __launch_bounds__(W * 64) void gemm_rows_kernel(const uint16_t* Wp, const uint16_t* A,
-                                                           int Kb, float* Y, int M, int ldy) {
+                                                           int Kb, float* Y, int M, int ldy,
+                                                           int accumulate) {
   constexpr int YW = NB * 16;
   constexpr int U = RT <= 2 ? 8 : (RT <= 4 ? 4 : 2);  // k-blocks per batch of loads
   __shared__ float s_red[W * NB * 256];
@@ -117,7 +120,10 @@ __global__ __launch_bounds__(W * 64) void gemm_rows_kernel(const uint16_t* Wp, c
       for (int w = 0; w < W; ++w)
         v += s_red[((w * NB + j) * 64 + ln) * 4 + r] + s_red[((w * NB + j) * 64 + ln + 32) * 4 + r];
       const int m = 8 * t + 4 * (ln >> 4) + r;
-      if (m < M) Y[(size_t)m * ldy + col0 + j * 16 + (ln & 15)] = v;
+      if (m < M) {
+        float* y = Y + (size_t)m * ldy + col0 + j * 16 + (ln & 15);
+        *y = accumulate ? *y + v : v;
+      }
     }
     __syncthreads();
   }
@@ -125,34 +131,37 @@ __global__ __launch_bounds__(W * 64) void gemm_rows_kernel(const uint16_t* Wp, c
 
 template <int NB>
 static hipError_t launch_rt(int RT, const uint16_t* Wp, const uint16_t* A, int Kb, int n_groups,
-                            float* Y, int M, int ldy, hipStream_t s) {
+                            float* Y, int M, int ldy, int acc, hipStream_t s) {
   const dim3 grid(n_groups), block(4 * 64);
   switch (RT) {
-    case 1: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 1>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy); break;
-    case 2: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 2>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy); break;
-    case 4: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 4>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy); break;
-    case 8: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 8>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy); break;
-    case 16: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 16>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy); break;
+    case 1: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 1>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy, acc); break;
+    case 2: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 2>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy, acc); break;
+    case 4: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 4>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy, acc); break;
+    case 8: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 8>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy, acc); break;
+    case 16: hipLaunchKernelGGL((gemm_rows_kernel<NB, 4, 16>), grid, block, 0, s, Wp, A, Kb, Y, M, ldy, acc); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s) {
-  if (a.M < 1 || a.M > kRowsMaxM || a.K % 32 || a.N % (16 * a.nb)) return hipErrorInvalidValue;
-  int RT = 1;
-  while (8 * RT < a.M) RT *= 2;
+  if (a.M < 1 || a.M > kRowsMaxM || a.K % 32 || (a.nb != 1 && a.nb != 2) || a.N % (16 * a.nb))
+    return hipErrorInvalidValue;
+  const int ldy = a.ldy > 0 ? a.ldy : a.N;
+  if (ldy < a.N) return hipErrorInvalidValue;
+  const int RT = rows_tiles(a.M);
   const int Kb = a.K / 32, n_groups = a.N / (16 * a.nb);
-  const size_t total = (size_t)Kb * RT * 64;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.X, a.M, a.K, RT,
-                     a.A);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.nb == 1) return launch_rt<1>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, a.N, s);
-  if (a.nb == 2) return launch_rt<2>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, a.N, s);
-  return hipErrorInvalidValue;
+  if (a.X != nullptr) {
+    const size_t total = (size_t)Kb * RT * 64;
+    size_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.X, a.M, a.K,
+                       RT, a.A);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.nb == 1) return launch_rt<1>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, ldy, a.accumulate, s);
+  return launch_rt<2>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, ldy, a.accumulate, s);
 }
 
 }  // namespace spec

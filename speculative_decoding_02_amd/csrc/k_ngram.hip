@@ -14,7 +14,8 @@
 //
 // Every workgroup runs the (cheap) search itself, so no workgroup waits for
 // another: each then writes its share of the one-hot rows, and workgroup 0
-// the tokens.
+// the tokens.  A batch of sequences runs in one launch, grid.y indexing the
+// sequence.
 #include "kernels.h"
 
 namespace spec {
@@ -28,6 +29,13 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_draft_kernel(NgramArgs a)
   __shared__ unsigned long long s_best[kNgramThreads / 64];
   __shared__ int32_t s_d[kNgramMaxK];
   const int tid = threadIdx.x;
+  {  // this workgroup's sequence
+    const int b = blockIdx.y;
+    a.st += b;
+    a.hist += (size_t)b * a.hist_cap;
+    a.d += (size_t)b * a.K;
+    if (a.D != nullptr) a.D += (size_t)b * a.K * a.V;
+  }
   int L = a.st->LT;
   if (L < 0 || L >= a.hist_cap) L = 0;  // a corrupt state is flagged elsewhere; stay in bounds
   const int nmax = min(a.n_max, L);
@@ -90,7 +98,9 @@ hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s) {
   const size_t n4 = (size_t)a.K * a.V / 4;
   size_t blocks = (n4 + kNgramThreads * 4 - 1) / (kNgramThreads * 4);
   blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-  hipLaunchKernelGGL(ngram_draft_kernel, dim3((unsigned)blocks), dim3(kNgramThreads), 0, s, a);
+  const int B = a.B > 1 ? a.B : 1;
+  hipLaunchKernelGGL(ngram_draft_kernel, dim3((unsigned)blocks, (unsigned)B), dim3(kNgramThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 

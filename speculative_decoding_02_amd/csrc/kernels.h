@@ -27,6 +27,13 @@ struct AttnArgs {
   float2* ws_ml;             // [n_kv][max_chunks][qg_max] (max score, sum of exp)
   int qg_max;                // (n_q/n_kv) * kMaxRows
   uint16_t* Ap_out;          // packed attention output rows (K = n_q*hd) for the O projection
+  // A batch of sequences in one launch (0 or 1: a single pass).  Sequence b
+  // reads rows[b], block_table + b * n_blocks, the query fragments
+  // qf + b * qf_bytes / 2 (qf_bytes is then one sequence's share), its own
+  // workspace slice, and writes its rows as rows b * seq_rows + r of the
+  // packed output, laid out in a_tiles row tiles (rows GEMM layout; 0 or 1:
+  // the single pass's 16-row tile).
+  int n_seq, seq_rows, a_tiles;
 };
 constexpr int kAttnChunk = 32;  // keys per partial (one wave), two cache blocks
 // n_rows: rows the pass can have (bounds the merge grid); rows beyond
@@ -92,13 +99,45 @@ hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s);
 
 // --------------------------------------------- GEMM for a batch of rows --
 constexpr int kRowsMaxM = 128;  // 16 row tiles of 8 activation rows (hi/lo)
+// Row tiles of the packed A operand for M rows: the smallest power of two
+// RT with 8 RT >= M.
+inline int rows_tiles(int M) {
+  int RT = 1;
+  while (8 * RT < M) RT *= 2;
+  return RT;
+}
+// Packed A of the rows GEMM, [K/32][RT][64 lanes][8 bf16]: tile t holds the
+// bf16 high parts of rows 8t..8t+7 in its MFMA rows 0-7 and their low parts
+// in rows 8-15.  With RT = 1 it is the single pass's layout (apack_index).
+SPEC_DEVICE size_t apack_index_rt(int m, int part, int k, int RT) {
+  const int kk = k & 31;
+  const int lane = (m & 7) + 8 * part + 16 * (kk >> 3);
+  return (((size_t)(k >> 5) * RT + (m >> 3)) * 64 + lane) * 8 + (kk & 7);
+}
+SPEC_DEVICE void apack_store8_rt(uint16_t* Ap, int m, int k0, const float* v, int RT) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16_rne(v[e]);
+    l[e] = f32_to_bf16_rne(v[e] - bf16_to_f32(h[e]));
+  }
+  *(uint4*)(Ap + apack_index_rt(m, 0, k0, RT)) =
+      make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                 pack_bf16x2(h[6], h[7]));
+  *(uint4*)(Ap + apack_index_rt(m, 1, k0, RT)) =
+      make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
+                 pack_bf16x2(l[6], l[7]));
+}
 struct RowsGemmArgs {
   const uint16_t* Wp;     // packed weights (launch_pack layout, NB = nb)
   int N, K, nb;
-  const float* X;         // [M][K] fp32 activations
+  const float* X;         // [M][K] fp32 activations, packed into A by the launch; or null:
+                          // A already holds them (rows_tiles(M) tiles)
   int M;
-  uint16_t* A;            // workspace: [K/32][ceil(M/8) rounded to a power of 2][64][8] bf16
-  float* Y;               // [M][N] fp32
+  uint16_t* A;            // [K/32][rows_tiles(M)][64][8] bf16
+  float* Y;               // [M][ldy] fp32 (ldy 0: N)
+  int ldy;
+  int accumulate;         // 1: Y += X W^T (a residual update); 0: Y = X W^T
 };
 hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s);
 
@@ -112,6 +151,8 @@ struct NgramArgs {
   int K, n_max, V;
   int32_t* d;             // [K] draft tokens
   float* D;               // [K][V] one-hot draft rows, or null
+  int B;                  // sequences (0 or 1: one); sequence b uses st + b,
+                          // hist + b * hist_cap, d + b * K, D + b * K * V
 };
 hipError_t launch_ngram_draft(const NgramArgs& a, hipStream_t s);
 
@@ -130,6 +171,87 @@ struct HeadsArgs {
 };
 hipError_t launch_heads_prep(const HeadsArgs& a, hipStream_t s);
 hipError_t launch_heads_pack(const HeadsArgs& a, hipStream_t s);
+
+// ------------------------------------------------ batches of sequences --
+// A batched pass carries R rows per sequence for B sequences: row m = b R + r
+// of the activations is row r of sequence b, at position rows[b].pos0 + r.
+enum BatchEmbedMode : int {
+  BEMB_VERIFY = 0,   // rows [hist_b[LT_b], d_b0..d_b,R-2] at LT_b..
+  BEMB_PREFILL = 1,  // rows hist_b[pos0 + r] at pos0..
+};
+struct BatchEmbedArgs {
+  const uint16_t* E;      // [vocab][d]
+  int d, vocab, max_seq;
+  DevState* st;           // [B]
+  const int32_t* hist;    // [B][hist_cap]
+  int hist_cap;
+  const int32_t* dtok;    // [B][R-1] drafts (verify)
+  int mode, B, R, pos0;
+  PassRows* rows;         // [B] written
+  uint64_t* pos_rule;     // [B] written: position of row 1 (the first draft)
+  float* x;               // [B R][d] written
+};
+hipError_t launch_batch_embed(const BatchEmbedArgs& a, hipStream_t s);
+
+// h = x / sqrt(mean(x^2) + eps) * gain for rows m < M, packed (rows GEMM
+// layout, RT tiles); rows M..8 RT-1 are written as zeros.
+struct NormPackArgs {
+  const float* x;         // [M][d]
+  int M, d, RT;
+  const uint16_t* gain;   // [d] bf16
+  float eps;
+  uint16_t* Ap;
+};
+hipError_t launch_norm_pack(const NormPackArgs& a, hipStream_t s);
+
+// QKV product rows [M][q_dim + 2 kv_dim] (q, k, v in natural order) -> RoPE
+// on q and k at each row's position; q into the sequence's query fragments,
+// k and v (high and low planes) into the paged cache through its block table.
+struct QkvPostArgs {
+  const float* y;
+  int M, R, q_dim, kv_dim, hd, n_kv, max_seq;
+  const PassRows* rows;        // [B]
+  const float2* rope;          // [max_seq][hd/2] (cos, sin)
+  uint16_t* qf;                // [B][qf_seq] fragments
+  size_t qf_seq;
+  uint16_t* k_cache;           // one layer of the pool
+  uint16_t* v_cache;
+  const int32_t* block_table;  // [B][n_blocks]
+  int n_blocks;
+};
+hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s);
+
+// y [M][2F] (gate columns 0..F-1, up columns F..2F-1) -> silu(gate) * up,
+// packed (RT tiles, K = F); rows M..8 RT-1 zero.
+struct SiluPackArgs {
+  const float* y;
+  int M, F, RT;
+  uint16_t* Ap;
+};
+hipError_t launch_silu_pack(const SiluPackArgs& a, hipStream_t s);
+
+// Row softmax of logits [M][V] into out (max-subtracted, fp32), in two
+// launches: per (chunk, row) (max, sum of exp) partials, then the
+// normalisation, each block folding its row's partials in chunk order.
+struct RowSoftmaxArgs {
+  const float* logits;
+  int M, V, chunk, n_chunks;   // n_chunks * chunk >= V, n_chunks <= 256
+  float2* part;                // [M][n_chunks]
+  float* out;
+};
+hipError_t launch_row_softmax(const RowSoftmaxArgs& a, hipStream_t s);
+
+// Commit of a batched verify: per sequence b, hist_b[LT_b+1..LT_b+1+n] =
+// out[b][0..n] with n = n_acc[b], then LT_b += n + 1.
+struct BatchCommitArgs {
+  DevState* st;
+  int32_t* hist;
+  int hist_cap;
+  const int32_t* out;     // [B][K+1]
+  const int32_t* n_acc;   // [B]
+  int B, K;
+};
+hipError_t launch_batch_commit(const BatchCommitArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- commit --
 // Also keeps the final residual row n_acc of the pass (x_rows, row stride d)

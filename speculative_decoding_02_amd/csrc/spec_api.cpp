@@ -18,14 +18,17 @@
 #include <string>
 #include <vector>
 
+#include "host_util.h"
 #include "kernels.h"
 #include "spec.h"
 
 using namespace spec;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
+
+namespace spec_host {
 
 std::string fmt(const char* f, ...) {
   char buf[512];
@@ -35,6 +38,53 @@ std::string fmt(const char* f, ...) {
   va_end(ap);
   return buf;
 }
+
+void set_last_error(const std::string& msg) { g_err = msg; }
+
+bool valid_model(const spec_model_desc& m, std::string* why) {
+  if (m.n_layers < 1 || m.d_model < 64 || m.n_heads < 1 || m.n_kv_heads < 1 || m.head_dim < 2 ||
+      m.d_ffn < 32 || m.vocab < 16) {
+    *why = "non-positive or too small dimension";
+    return false;
+  }
+  if (m.d_model % 64 || m.d_ffn % 32 || m.vocab % 16 || m.head_dim % 2) {
+    *why = "need d_model % 64 == 0, d_ffn % 32 == 0, vocab % 16 == 0, even head_dim";
+    return false;
+  }
+  if (m.n_heads % m.n_kv_heads) {
+    *why = "n_heads must be a multiple of n_kv_heads";
+    return false;
+  }
+  if ((m.n_heads * m.head_dim / 2) % 8 || (m.n_kv_heads * m.head_dim / 2) % 8) {
+    *why = "n_heads*head_dim/2 and n_kv_heads*head_dim/2 must be multiples of 8";
+    return false;
+  }
+  if (m.head_dim > 256 || (m.n_heads / m.n_kv_heads) * kMaxRows > 64 || m.head_dim % 8) {
+    *why = "head_dim must be a multiple of 8 and <= 256; n_heads/n_kv_heads <= 8";
+    return false;
+  }
+  if ((m.n_heads * m.head_dim) % 32) {
+    *why = "n_heads*head_dim must be a multiple of 32";
+    return false;
+  }
+  if (!m.embed || !m.attn_norm || !m.wq || !m.wk || !m.wv || !m.wo || !m.ffn_norm || !m.wg ||
+      !m.wu || !m.wd || !m.final_norm || !m.lm_head) {
+    *why = "null weight pointer";
+    return false;
+  }
+  if (!(m.rms_eps >= 0.0f) || !(m.rope_theta > 0.0f)) {
+    *why = "rms_eps must be >= 0 and rope_theta > 0";
+    return false;
+  }
+  return true;
+}
+
+}  // namespace spec_host
+
+namespace {
+
+using spec_host::fmt;
+using spec_host::valid_model;
 
 struct Mat {
   uint16_t* p = nullptr;  // packed (inside the model arena)
@@ -156,44 +206,6 @@ int fail(spec_ctx* c, int code, const std::string& msg) {
 template <typename T>
 hipError_t dalloc(T** p, size_t n) {
   return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
-}
-
-bool valid_model(const spec_model_desc& m, std::string* why) {
-  if (m.n_layers < 1 || m.d_model < 64 || m.n_heads < 1 || m.n_kv_heads < 1 || m.head_dim < 2 ||
-      m.d_ffn < 32 || m.vocab < 16) {
-    *why = "non-positive or too small dimension";
-    return false;
-  }
-  if (m.d_model % 64 || m.d_ffn % 32 || m.vocab % 16 || m.head_dim % 2) {
-    *why = "need d_model % 64 == 0, d_ffn % 32 == 0, vocab % 16 == 0, even head_dim";
-    return false;
-  }
-  if (m.n_heads % m.n_kv_heads) {
-    *why = "n_heads must be a multiple of n_kv_heads";
-    return false;
-  }
-  if ((m.n_heads * m.head_dim / 2) % 8 || (m.n_kv_heads * m.head_dim / 2) % 8) {
-    *why = "n_heads*head_dim/2 and n_kv_heads*head_dim/2 must be multiples of 8";
-    return false;
-  }
-  if (m.head_dim > 256 || (m.n_heads / m.n_kv_heads) * kMaxRows > 64 || m.head_dim % 8) {
-    *why = "head_dim must be a multiple of 8 and <= 256; n_heads/n_kv_heads <= 8";
-    return false;
-  }
-  if ((m.n_heads * m.head_dim) % 32) {
-    *why = "n_heads*head_dim must be a multiple of 32";
-    return false;
-  }
-  if (!m.embed || !m.attn_norm || !m.wq || !m.wk || !m.wv || !m.wo || !m.ffn_norm || !m.wg ||
-      !m.wu || !m.wd || !m.final_norm || !m.lm_head) {
-    *why = "null weight pointer";
-    return false;
-  }
-  if (!(m.rms_eps >= 0.0f) || !(m.rope_theta > 0.0f)) {
-    *why = "rms_eps must be >= 0 and rope_theta > 0";
-    return false;
-  }
-  return true;
 }
 
 // Packs one matrix from row pointers (host list) into dst.

@@ -58,4 +58,9 @@ def test_argument_errors_need_no_device(lib):
     lib.spec_init.restype = ctypes.c_int
     assert lib.spec_init(None, None, 0, ctypes.byref(out)) == sd.SPEC_ERR_ARG
     assert out.value is None
+    lib.spec_batch_init.restype = ctypes.c_int
+    assert lib.spec_batch_init(None, None, 0, ctypes.byref(out)) == sd.SPEC_ERR_ARG
+    assert out.value is None
+    lib.spec_batch_last_error.restype = ctypes.c_char_p
+    assert b"null" in lib.spec_batch_last_error(None)
     lib.spec_destroy(None)  # NULL is accepted
