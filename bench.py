@@ -72,15 +72,15 @@ def log(*a):
 KV_ELEM_BYTES = 2
 
 
-def verify_pass_bytes(cfg, K: int, L: int) -> int:
-    """Algorithmic bytes of one verify pass: every weight once, K+1 embedding
-    rows, keys/values of L+K+1 positions read and K+1 written (bf16), T rows
-    written."""
+def verify_pass_bytes(cfg, K: int, L: int, B: int = 1) -> int:
+    """Algorithmic bytes of one verify pass over B sequences: every weight
+    once, K+1 embedding rows per sequence, keys/values of L+K+1 positions read
+    and K+1 written (bf16) per sequence, T rows written."""
     w = cfg.weight_bytes()
-    emb = (K + 1) * cfg.d_model * 2
+    emb = B * (K + 1) * cfg.d_model * 2
     kv_tok = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * KV_ELEM_BYTES
-    kv = (L + K + 1) * kv_tok + (K + 1) * kv_tok
-    t_rows = (K + 1) * cfg.vocab * 4
+    kv = B * ((L + K + 1) * kv_tok + (K + 1) * kv_tok)
+    t_rows = B * (K + 1) * cfg.vocab * 4
     return w + emb + kv + t_rows
 
 
@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--gemm-sweep", action="store_true",
                     help="batched verify: time the weight-streaming GEMM (spec_mat_mul) on the "
                          "8B-shaped matrices for M = B(K+1) = 1..128 rows")
+    ap.add_argument("--batch-sweep", default=None, metavar="B1,B2,...",
+                    help="batched verify (spec_batch_*): B sequences of the target verified in "
+                         "one pass, n-gram drafts; prints one JSON line with a row per B")
     ap.add_argument("--adaptive-k", action="store_true",
                     help="choose K every few rounds from the measured acceptance rate "
                          "(spec_alpha_from_tokens + spec_choose_k) instead of a fixed K")
@@ -141,6 +144,9 @@ def main():
 
     if args.gemm_sweep:
         print(json.dumps(gemm_sweep(sd, torch, np)), flush=True)
+        return
+    if args.batch_sweep:
+        print(json.dumps(batch_sweep(sd, torch, np, synth, args)), flush=True)
         return
 
     tcfg, dcfg = synth.PAIRS[args.pair]
@@ -454,6 +460,89 @@ def gemm_sweep(sd, torch, np):
             "peak_hbm_GB_s": PEAK_HBM_GBS, "peak_bf16_dense_TFLOP_s": 2500.0,
             "config": {"workload": "8B-shaped weight matrices, M activation rows, weights cold"},
             "sweep": res}
+
+
+def batch_sweep(sd, torch, np, synth, args):
+    """Batched verify: for each B, a context with B sequences (prompt plen
+    each, different texts) drafts with the batched prompt-lookup drafter and
+    verifies all B (K+1) rows in one pass per round.  Reported per B: the
+    verify pass (median of the timed rounds, events on the context's stream),
+    its algorithmic GB/s (weights once, every sequence's cache and rows) and
+    useful TFLOP/s (2 per weight per row), the round time, and the accepted
+    tokens/s of the whole batch."""
+    tcfg = synth.PAIRS[args.pair][0]
+    K = args.k
+    plen = args.prompt_len or {"toy": 32, "1.3b": 512, "8b": 1024, "31b": 2048}[args.pair]
+    Bs = [int(x) for x in args.batch_sweep.split(",")]
+    torch.cuda.set_device(0)
+    tw = synth.weights_torch(tcfg, device="cuda")
+    torch.cuda.synchronize()
+    V = tcfg.vocab
+    stream = torch.cuda.Stream()
+    rows = []
+    for B in Bs:
+        prompts = np.stack([synth.prompt(V, plen, seed=100 + b) for b in range(B)])
+        max_seq = plen + (K + 1) * (args.steps + args.warmup) + 16
+        t0 = time.time()
+        bc = sd.spec_batch_init(tcfg, tw, prompts, k_max=K, max_seq=max_seq, greedy=args.greedy,
+                                stream=stream.cuda_stream)
+        log(f"batch B={B}: spec_batch_init (pack + prefill {B} x {plen}) in {time.time() - t0:.1f}s")
+        d = torch.zeros(B, K, dtype=torch.int32, device="cuda")
+        D = torch.zeros(B, K, V, dtype=torch.float32, device="cuda")
+        out = torch.zeros(B, K + 1, dtype=torch.int32, device="cuda")
+        nacc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+        def rnd(ev=None):
+            sd.spec_batch_draft_ngram(bc, K, args.ngram_n, d, D)
+            if ev is not None:
+                ev[0].record(stream)
+            sd.spec_batch_verify(bc, K, synth.SEED_PHILOX, d, D, out, nacc)
+            if ev is not None:
+                ev[1].record(stream)
+            sd.spec_batch_commit(bc, out, nacc)
+
+        for _ in range(args.warmup):
+            rnd()
+        len0 = sd.spec_batch_get_state(bc)["len"].astype(np.int64)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            rnd(evs[i])
+        e1.record(stream)
+        sd.spec_batch_sync(bc)
+        st = sd.spec_batch_get_state(bc)
+        assert np.all(st["device_error"] == 0), st
+        tokens = int((st["len"].astype(np.int64) - len0).sum())
+        ms = e0.elapsed_time(e1)
+        vms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        L_mid = plen + int((st["len"].astype(np.int64) - len0).mean()) // 2
+        M = B * (K + 1)
+        vbytes = verify_pass_bytes(tcfg, K, L_mid, B)
+        flops = 2 * M * tcfg.weight_bytes() // 2
+        rows.append({"B": B, "M": M, "verify_ms": round(vms, 3),
+                     "verify_GB_s": round(vbytes / (vms / 1e3) / 1e9, 1),
+                     "useful_TFLOP_s": round(flops / (vms / 1e3) / 1e12, 2),
+                     "round_ms": round(ms / args.steps, 3),
+                     "tokens_per_round": round(tokens / args.steps, 3),
+                     "tokens_per_s": round(tokens / (ms / 1e3), 1)})
+        log(f"batch B={B} (M={M}): verify {vms:.3f} ms, {rows[-1]['verify_GB_s']} GB/s, "
+            f"{rows[-1]['tokens_per_s']} tokens/s")
+        sd.spec_batch_destroy(bc)
+        del d, D, out, nacc
+        torch.cuda.empty_cache()
+    base = rows[0]["verify_ms"]
+    for r in rows:
+        r["verify_vs_first"] = round(r["verify_ms"] / base, 3)
+    return {"metric": "batched verify: pass time and accepted tokens/s vs sequences B",
+            "unit": "ms / tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "dtype": "bf16", "data": "synthetic",
+            "peak_hbm_GB_s": PEAK_HBM_GBS, "peak_bf16_dense_TFLOP_s": PEAK_BF16_TFLOPS,
+            "config": {"workload": f"{tcfg.name} target, K = {K}, prompt {plen} per sequence, "
+                                   f"prompt-lookup drafts (n <= {args.ngram_n}), "
+                                   f"{'greedy' if args.greedy else 'sampling at T = 1'}"},
+            "sweep": rows}
 
 
 def adaptive_k_run(sd, torch, ctx, stream, d, D, out, nacc, seed, args, tcfg, dcfg, plen):
