@@ -138,7 +138,31 @@ struct RowsGemmArgs {
   float* Y;               // [M][ldy] fp32 (ldy 0: N)
   int ldy;
   int accumulate;         // 1: Y += X W^T (a residual update); 0: Y = X W^T
+  float* P;               // split-K partials of the wide kernel (may be null: no split)
+  size_t P_elems;         // capacity of P in floats
 };
+// More than 8 rows take the wide kernel when N is a multiple of
+// kRowsWideCols: its waves split a workgroup's columns and share the
+// activation tiles through LDS.  Narrow matrices split K over up to
+// kRowsMaxSplit workgroups (partials summed by a second launch).
+constexpr int kRowsWideCols = 128;
+constexpr int kRowsMaxSplit = 8;
+// K slices the wide kernel uses for an N x K matrix (1: no split): enough
+// workgroups for about one per CU.  (Two per CU measured slower: the extra
+// partial traffic and reduce launch cost more than the overlap gains.)
+inline int rows_wide_split(int N, int K) {
+  const int groups = N / kRowsWideCols, Kb = K / 32;
+  if (groups >= 192) return 1;
+  int S = 256 / (groups > 0 ? groups : 1);
+  S = S < 1 ? 1 : (S > kRowsMaxSplit ? kRowsMaxSplit : S);
+  while (S > 1 && Kb / S < 4) --S;  // at least four k-blocks per slice
+  return S;
+}
+// Partial floats the wide kernel needs for M rows of an N x K matrix.
+inline size_t rows_partials(int M, int N, int K) {
+  const int S = rows_wide_split(N, K);
+  return S > 1 ? (size_t)S * M * N : 0;
+}
 hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ n-gram drafter --

@@ -1046,6 +1046,8 @@ struct spec_mat {
   int N = 0, K = 0, nb = 1;
   uint16_t* Wp = nullptr;
   uint16_t* A = nullptr;  // activation workspace for up to kRowsMaxM rows
+  float* P = nullptr;     // split-K partials for up to kRowsMaxM rows
+  size_t P_elems = 0;
 };
 
 int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
@@ -1064,6 +1066,8 @@ int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
   const uint16_t** drows = nullptr;
   if (e == hipSuccess) e = dalloc(&m->Wp, (size_t)N * K);
   if (e == hipSuccess) e = dalloc(&m->A, (size_t)(K / 32) * (kRowsMaxM / 8) * 64 * 8);
+  m->P_elems = rows_partials(kRowsMaxM, N, K);
+  if (e == hipSuccess) e = dalloc(&m->P, m->P_elems);
   if (e == hipSuccess) e = dalloc(&drows, (size_t)N);
   if (e == hipSuccess)
     e = hipMemcpy(drows, rows.data(), (size_t)N * sizeof(void*), hipMemcpyHostToDevice);
@@ -1073,6 +1077,7 @@ int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
   if (e != hipSuccess) {
     (void)hipFree(m->Wp);
     (void)hipFree(m->A);
+    (void)hipFree(m->P);
     delete m;
     return fail(nullptr, e == hipErrorOutOfMemory ? SPEC_ERR_OOM : SPEC_ERR_HIP,
                 fmt("spec_mat_create: %s", hipGetErrorString(e)));
@@ -1087,7 +1092,7 @@ int spec_mat_mul(spec_mat* m, const float* X_dev, int32_t M, float* Y_dev, void*
     return fail(nullptr, SPEC_ERR_ARG, fmt("spec_mat_mul: M=%d outside 1..%d", M, kRowsMaxM));
   RowsGemmArgs a{};
   a.Wp = m->Wp; a.N = m->N; a.K = m->K; a.nb = m->nb;
-  a.X = X_dev; a.M = M; a.A = m->A; a.Y = Y_dev;
+  a.X = X_dev; a.M = M; a.A = m->A; a.Y = Y_dev; a.P = m->P; a.P_elems = m->P_elems;
   HIPTRY(nullptr, hipSetDevice(m->device));
   HIPTRY(nullptr, launch_gemm_rows(a, (hipStream_t)hip_stream));
   return SPEC_OK;
@@ -1099,6 +1104,7 @@ int spec_mat_destroy(spec_mat* m) {
   (void)hipDeviceSynchronize();
   (void)hipFree(m->Wp);
   (void)hipFree(m->A);
+  (void)hipFree(m->P);
   delete m;
   return SPEC_OK;
 }

@@ -71,6 +71,8 @@ struct spec_batch {
   float2* attn_ml = nullptr;
   float2* sm_part = nullptr;
   int sm_chunk = 0, sm_nchunks = 0;
+  float* gemm_part = nullptr;  // split-K partials of the rows GEMM
+  size_t gemm_part_elems = 0;
   uint64_t* ar_ws = nullptr;
   int ar_chunk = 0, ar_nchunks = 0;
   PassRows* rows = nullptr;
@@ -199,6 +201,7 @@ hipError_t gemm(spec_batch* c, const RMat& w, int M, float* Y, int ldy, int accu
   RowsGemmArgs a{};
   a.Wp = w.p; a.N = w.N; a.K = w.K; a.nb = w.nb;
   a.X = nullptr; a.M = M; a.A = c->ap; a.Y = Y; a.ldy = ldy; a.accumulate = accumulate;
+  a.P = c->gemm_part; a.P_elems = c->gemm_part_elems;
   return launch_gemm_rows(a, s);
 }
 
@@ -296,7 +299,7 @@ void destroy(spec_batch* c) {
   c->graph_cache.clear();
   void* bufs[] = {c->T.arena, c->T.embed, c->T.norms, c->kcache, c->vcache, c->block_table,
                   c->rope, c->x, c->y, c->logits, c->Tbuf, c->ap, c->qf, c->attn_wo, c->attn_ml,
-                  c->sm_part, c->ar_ws, c->rows, c->pos_rule, c->st, c->hist};
+                  c->sm_part, c->gemm_part, c->ar_ws, c->rows, c->pos_rule, c->st, c->hist};
   for (void* b : bufs) (void)hipFree(b);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
@@ -344,6 +347,11 @@ int init(spec_batch* c, const int32_t* prompts, int n_prompt) {
   // finite from the start: padding rows no producer writes are multiplied too
   // (their output rows are discarded)
   BTRY(c, hipMemsetAsync(c->ap, 0, (size_t)(kmax / 32) * (Mmax / 8) * 64 * 8 * 2, c->stream));
+  size_t part = 0;
+  for (const RMat* r : {&m.qkv[0], &m.o[0], &m.gu[0], &m.dn[0], &m.lm})
+    part = std::max(part, rows_partials(Mmax, r->N, r->K));
+  c->gemm_part_elems = part;
+  BTRY(c, dalloc(&c->gemm_part, part));
   const size_t rows_out = (size_t)B * (p.k_max + 1) * m.V;
   BTRY(c, dalloc(&c->logits, rows_out));
   BTRY(c, dalloc(&c->Tbuf, rows_out));

@@ -161,6 +161,22 @@ def test_toy_largest_batch(toy_w):
     assert acc > 0
 
 
+# every matrix a multiple of 128 columns: passes over more than 8 rows take
+# the wide GEMM (LDS-shared activation tiles, split K for the narrow ones)
+MID = synth.ModelConfig("mid-2L-d256", 2, 256, 4, 2, 64, 512, 1024)
+
+
+@pytest.mark.parametrize("B,K", [(5, 4), (16, 7)])
+def test_mid_batch_wide_gemm_rounds_match_oracle(B, K):
+    """25 and 128 rows through the wide GEMM (QKV 512, O 256, gate/up 1024,
+    down 256, LM head 1024 columns: every matrix with K split two to four
+    ways)."""
+    import speculative_decoding_02_amd as sd
+    w = synth.weights_np(MID)
+    acc = run_teacher_forced(sd, MID, w, B, K, False, rounds=3, prompt_len=14)
+    assert acc > 0
+
+
 def test_greedy_streams_equal_plain_greedy_with_ngram_drafts(toy_w):
     """Greedy speculative output is the target's own greedy text whatever the
     drafts; here the batched prompt-lookup drafter, on prompts that repeat so
