@@ -298,7 +298,8 @@ int spec_mat_destroy(spec_mat* m);
  * spec_batch_draft_ngram.
  * Limits: 1 <= n_seq <= SPEC_BATCH_MAX_SEQ, 1 <= k_max <= SPEC_K_MAX,
  * n_seq * (k_max + 1) <= 128 activation rows; every prompt has n_prompt
- * tokens; the target follows spec_model_desc's shape rules. */
+ * tokens; the target follows spec_model_desc's shape rules with
+ * d_model <= 8192. */
 #define SPEC_BATCH_MAX_SEQ 32
 
 typedef struct spec_batch_params {

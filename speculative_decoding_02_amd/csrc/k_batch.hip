@@ -70,6 +70,10 @@ hipError_t launch_batch_embed(const BatchEmbedArgs& a, hipStream_t s) {
 }
 
 // ----------------------------------------------------------- norm_pack --
+// One workgroup per row; thread t owns the 8-element chunks t, t + 256, ...
+// of its row in both passes (values kept in registers).
+constexpr int kNormChunks = kNormPackMaxD / (kBatchThreads * 8);
+
 __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a) {
   __shared__ float s_red[16];
   const int m = blockIdx.x, tid = threadIdx.x, d = a.d;
@@ -78,22 +82,51 @@ __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a
     for (int k0 = tid * 8; k0 < d; k0 += kBatchThreads * 8) apack_store8_rt(a.Ap, m, k0, z, a.RT);
     return;
   }
-  const float* x = a.x + (size_t)m * d;
+  float* x = a.x + (size_t)m * d;
+  float v[kNormChunks][8];
   float ss = 0.0f;
-  for (int i = tid; i < d; i += kBatchThreads) ss += x[i] * x[i];
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int k0 = (c * kBatchThreads + tid) * 8;
+    if (k0 < d) {
+      const float4 x0 = *(const float4*)(x + k0), x1 = *(const float4*)(x + k0 + 4);
+      float r[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      if (a.S > 0) {
+        for (int sl = 0; sl < a.S; ++sl) {
+          const float* p = a.P + ((size_t)sl * a.M + m) * d + k0;
+          const float4 p0 = *(const float4*)p, p1 = *(const float4*)(p + 4);
+          r[0] += p0.x; r[1] += p0.y; r[2] += p0.z; r[3] += p0.w;
+          r[4] += p1.x; r[5] += p1.y; r[6] += p1.z; r[7] += p1.w;
+        }
+        *(float4*)(x + k0) = make_float4(r[0], r[1], r[2], r[3]);
+        *(float4*)(x + k0 + 4) = make_float4(r[4], r[5], r[6], r[7]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[c][e] = r[e];
+        ss += r[e] * r[e];
+      }
+    }
+  }
   ss = block_reduce(ss, s_red, [](float p, float q) { return p + q; });
   const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
-  for (int k0 = tid * 8; k0 < d; k0 += kBatchThreads * 8) {
-    float g[8], v[8];
-    load_gain8(a.gain, k0, g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = x[k0 + e] * inv * g[e];
-    apack_store8_rt(a.Ap, m, k0, v, a.RT);
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int k0 = (c * kBatchThreads + tid) * 8;
+    if (k0 < d) {
+      float g[8], h[8];
+      load_gain8(a.gain, k0, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = v[c][e] * inv * g[e];
+      apack_store8_rt(a.Ap, m, k0, h, a.RT);
+    }
   }
 }
 
 hipError_t launch_norm_pack(const NormPackArgs& a, hipStream_t s) {
-  if (a.M < 1 || a.M > 8 * a.RT || a.RT > kRowsMaxM / 8 || a.d % 32) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 8 * a.RT || a.RT > kRowsMaxM / 8 || a.d % 32 || a.d > kNormPackMaxD ||
+      a.S < 0 || (a.S > 0 && a.P == nullptr))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(norm_pack_kernel, dim3(8 * a.RT), dim3(kBatchThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -106,13 +139,19 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
   const int ldy = a.q_dim + 2 * a.kv_dim;
   const int G = a.q_dim / a.kv_dim, n_es = (a.hd + 31) / 32;
   const size_t total = (size_t)a.M * per_row;
+  // column c of row m: the product, or the sum of its split partials
+  auto yv = [&](int m, int c) -> float {
+    if (a.S == 0) return a.y[(size_t)m * ldy + c];
+    float v = 0.0f;
+    for (int sl = 0; sl < a.S; ++sl) v += a.P[((size_t)sl * a.M + m) * ldy + c];
+    return v;
+  };
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int m = (int)(idx / per_row), i = (int)(idx % per_row);
     const int b = m / a.R, r = m % a.R;
     const int pos = a.rows[b].pos0 + r;
     if (pos < 0 || pos >= a.max_seq) continue;  // flagged by the embedding
-    const float* y = a.y + (size_t)m * ldy;
     const int blk = a.block_table[(size_t)b * a.n_blocks + pos / kBlock];
     if (i < n_pairs) {
       // rotate-half RoPE on the pair (j, j + hd/2) of one head
@@ -120,7 +159,7 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
       const int pl = is_q ? i : i - a.q_dim / 2;
       const int head = pl / half, j = pl % half;
       const int c1 = (is_q ? 0 : a.q_dim) + head * a.hd + j;
-      const float x1 = y[c1], x2 = y[c1 + half];
+      const float x1 = yv(m, c1), x2 = yv(m, c1 + half);
       const float2 cs = a.rope[(size_t)pos * half + j];
       const float v[2] = {x1 * cs.x - x2 * cs.y, x2 * cs.x + x1 * cs.y};
 #pragma unroll
@@ -140,7 +179,7 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
       }
     } else {
       const int f = i - n_pairs, head = f / a.hd, dim = f % a.hd;
-      const float v = y[a.q_dim + a.kv_dim + f];
+      const float v = yv(m, a.q_dim + a.kv_dim + f);
       const uint16_t hb = f32_to_bf16_rne(v);
       a.v_cache[vt_index(blk, a.n_kv, head, 0, a.hd, dim, pos % kBlock)] = hb;
       a.v_cache[vt_index(blk, a.n_kv, head, 1, a.hd, dim, pos % kBlock)] =
@@ -151,7 +190,7 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
 
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
   if (a.M < 1 || a.R < 1 || a.R > kMaxRows || a.M % a.R || a.hd % 2 || a.kv_dim <= 0 ||
-      a.q_dim % a.kv_dim)
+      a.q_dim % a.kv_dim || a.S < 0 || (a.S > 0 ? a.P == nullptr : a.y == nullptr))
     return hipErrorInvalidValue;
   const size_t total = (size_t)a.M * (a.q_dim / 2 + a.kv_dim / 2 + a.kv_dim);
   size_t blocks = (total + kBatchThreads - 1) / kBatchThreads;

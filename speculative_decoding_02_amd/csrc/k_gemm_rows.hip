@@ -303,7 +303,8 @@ static hipError_t launch_wide(const RowsGemmArgs& a, int RT, int ldy, hipStream_
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
+  if (a.split_out) *a.split_out = S > 1 && a.defer_sum ? S : 0;
+  if (e != hipSuccess || S == 1 || a.defer_sum) return e;
   const size_t total = (size_t)a.M * a.N;
   size_t blocks = (total + 255) / 256;
   blocks = blocks > 2048 ? 2048 : blocks;
@@ -343,6 +344,7 @@ hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.split_out) *a.split_out = 0;
   if (RT > 1 && a.N % kRowsWideCols == 0) return launch_wide(a, RT, ldy, s);
   if (a.nb == 1) return launch_rt<1>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, ldy, a.accumulate, s);
   return launch_rt<2>(RT, a.Wp, a.A, Kb, n_groups, a.Y, a.M, ldy, a.accumulate, s);

@@ -140,6 +140,8 @@ struct RowsGemmArgs {
   int accumulate;         // 1: Y += X W^T (a residual update); 0: Y = X W^T
   float* P;               // split-K partials of the wide kernel (may be null: no split)
   size_t P_elems;         // capacity of P in floats
+  int defer_sum;          // 1: leave split partials in P for the next kernel to sum
+  int* split_out;         // host, may be null: slices left in P (0: Y holds the result)
 };
 // More than 8 rows take the wide kernel when N is a multiple of
 // kRowsWideCols: its waves split a workgroup's columns and share the
@@ -218,13 +220,18 @@ struct BatchEmbedArgs {
 hipError_t launch_batch_embed(const BatchEmbedArgs& a, hipStream_t s);
 
 // h = x / sqrt(mean(x^2) + eps) * gain for rows m < M, packed (rows GEMM
-// layout, RT tiles); rows M..8 RT-1 are written as zeros.
+// layout, RT tiles); rows M..8 RT-1 are written as zeros.  With S > 0 split
+// partials P[s][m][:] of a residual GEMM are first added to x (in slice
+// order) and x is written back.  d <= kNormPackMaxD.
+constexpr int kNormPackMaxD = 8192;
 struct NormPackArgs {
-  const float* x;         // [M][d]
+  float* x;               // [M][d]
   int M, d, RT;
   const uint16_t* gain;   // [d] bf16
   float eps;
   uint16_t* Ap;
+  const float* P;         // [S][M][d] or null
+  int S;
 };
 hipError_t launch_norm_pack(const NormPackArgs& a, hipStream_t s);
 
@@ -232,7 +239,9 @@ hipError_t launch_norm_pack(const NormPackArgs& a, hipStream_t s);
 // on q and k at each row's position; q into the sequence's query fragments,
 // k and v (high and low planes) into the paged cache through its block table.
 struct QkvPostArgs {
-  const float* y;
+  const float* y;              // [M][q_dim + 2 kv_dim], or with S > 0:
+  const float* P;              // [S][M][q_dim + 2 kv_dim] split partials, summed in slice order
+  int S;
   int M, R, q_dim, kv_dim, hd, n_kv, max_seq;
   const PassRows* rows;        // [B]
   const float2* rope;          // [max_seq][hd/2] (cos, sin)

@@ -7,7 +7,8 @@
 // append) -> batched attention -> O GEMM (+= residual) -> norm_pack ->
 // gate/up GEMM -> silu_pack -> down GEMM (+= residual); then the final
 // norm, the LM head, the row softmax and the rule for all B sequences in one
-// launch pair.  The verify pass is captured as a hipGraph per (K, seed,
+// launch pair.  GEMMs that split K leave their slices for the next kernel
+// (norm_pack adds the residual GEMMs' slices to x, qkv_post sums QKV's).  The verify pass is captured as a hipGraph per (K, seed,
 // pointers), as for a single sequence.
 #include <hip/hip_runtime.h>
 
@@ -196,19 +197,24 @@ int build_target(spec_batch* c, const spec_model_desc& md) {
   return SPEC_OK;
 }
 
+// With split != nullptr a split-K GEMM leaves its slices in gemm_part and
+// *split says how many (0: Y holds the result); the next kernel sums them.
 hipError_t gemm(spec_batch* c, const RMat& w, int M, float* Y, int ldy, int accumulate,
-                hipStream_t s) {
+                hipStream_t s, int* split = nullptr) {
   RowsGemmArgs a{};
   a.Wp = w.p; a.N = w.N; a.K = w.K; a.nb = w.nb;
   a.X = nullptr; a.M = M; a.A = c->ap; a.Y = Y; a.ldy = ldy; a.accumulate = accumulate;
   a.P = c->gemm_part; a.P_elems = c->gemm_part_elems;
+  a.defer_sum = split != nullptr; a.split_out = split;
   return launch_gemm_rows(a, s);
 }
 
-hipError_t norm_pack(spec_batch* c, int M, const uint16_t* gain, hipStream_t s) {
+// RMSNorm of the residual rows into the packed operand; `split` slices of
+// the residual GEMM before it are added to x first.
+hipError_t norm_pack(spec_batch* c, int M, const uint16_t* gain, int split, hipStream_t s) {
   NormPackArgs a{};
   a.x = c->x; a.M = M; a.d = c->T.d; a.RT = rows_tiles(M); a.gain = gain; a.eps = c->T.eps;
-  a.Ap = c->ap;
+  a.Ap = c->ap; a.P = c->gemm_part; a.S = split;
   return launch_norm_pack(a, s);
 }
 
@@ -236,14 +242,17 @@ hipError_t enqueue_pass(spec_batch* c, hipStream_t s, int mode, int R, int pos0,
   em.rows = c->rows; em.pos_rule = c->pos_rule; em.x = c->x;
   hipError_t e = launch_batch_embed(em, s);
   const int n_qkv = m.qd + 2 * m.kvd;
+  int split = 0;  // slices of the last residual GEMM still to be added to x
   for (int l = 0; l < m.L && e == hipSuccess; ++l) {
     uint16_t* kc = c->kcache + (size_t)l * c->kv_layer;
     uint16_t* vc = c->vcache + (size_t)l * c->kv_layer;
-    e = norm_pack(c, M, m.attn_norm(l), s);
-    if (e == hipSuccess) e = gemm(c, m.qkv[l], M, c->y, n_qkv, 0, s);
+    e = norm_pack(c, M, m.attn_norm(l), split, s);
+    int qkv_split = 0;
+    if (e == hipSuccess) e = gemm(c, m.qkv[l], M, c->y, n_qkv, 0, s, &qkv_split);
     if (e == hipSuccess) {
       QkvPostArgs q{};
-      q.y = c->y; q.M = M; q.R = R; q.q_dim = m.qd; q.kv_dim = m.kvd; q.hd = m.hd; q.n_kv = m.nkv;
+      q.y = c->y; q.P = c->gemm_part; q.S = qkv_split;
+      q.M = M; q.R = R; q.q_dim = m.qd; q.kv_dim = m.kvd; q.hd = m.hd; q.n_kv = m.nkv;
       q.max_seq = c->p.max_seq; q.rows = c->rows; q.rope = c->rope; q.qf = c->qf;
       q.qf_seq = c->qf_seq; q.k_cache = kc; q.v_cache = vc; q.block_table = c->block_table;
       q.n_blocks = c->n_blocks;
@@ -260,18 +269,19 @@ hipError_t enqueue_pass(spec_batch* c, hipStream_t s, int mode, int R, int pos0,
       at.n_seq = B; at.seq_rows = R; at.a_tiles = RT;
       e = launch_attn(at, R, s);
     }
-    if (e == hipSuccess) e = gemm(c, m.o[l], M, c->x, m.d, 1, s);
-    if (e == hipSuccess) e = norm_pack(c, M, m.ffn_norm(l), s);
+    if (e == hipSuccess) e = gemm(c, m.o[l], M, c->x, m.d, 1, s, &split);
+    if (e == hipSuccess) e = norm_pack(c, M, m.ffn_norm(l), split, s);
     if (e == hipSuccess) e = gemm(c, m.gu[l], M, c->y, 2 * m.F, 0, s);
     if (e == hipSuccess) {
       SiluPackArgs sp{};
       sp.y = c->y; sp.M = M; sp.F = m.F; sp.RT = RT; sp.Ap = c->ap;
       e = launch_silu_pack(sp, s);
     }
-    if (e == hipSuccess) e = gemm(c, m.dn[l], M, c->x, m.d, 1, s);
+    if (e == hipSuccess) e = gemm(c, m.dn[l], M, c->x, m.d, 1, s, &split);
   }
+  // a prefill pass ends with the caches written (its residual is not needed)
   if (e != hipSuccess || mode != BEMB_VERIFY) return e;
-  e = norm_pack(c, M, m.final_norm(), s);
+  e = norm_pack(c, M, m.final_norm(), split, s);
   if (e == hipSuccess) e = gemm(c, m.lm, M, io.Lb, m.V, 0, s);
   if (e == hipSuccess) {
     RowSoftmaxArgs sm{};
@@ -420,6 +430,8 @@ int spec_batch_init(const spec_batch_params* p, const int32_t* prompts_host, int
   std::string why;
   if (!spec_host::valid_model(p->target, &why))
     return fail(nullptr, SPEC_ERR_ARG, "spec_batch_init: target: " + why);
+  if (p->target.d_model > kNormPackMaxD)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("spec_batch_init: d_model above %d", kNormPackMaxD));
   const int B = p->n_seq;
   if (B < 1 || B > SPEC_BATCH_MAX_SEQ)
     return fail(nullptr, SPEC_ERR_ARG, fmt("spec_batch_init: n_seq=%d outside 1..%d", B, SPEC_BATCH_MAX_SEQ));
