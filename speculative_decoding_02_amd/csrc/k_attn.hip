@@ -69,14 +69,18 @@ SPEC_DEVICE uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // key 16 (j / 4) + 4 grp + (j % 4) -- exactly the keys lane l holds in the C
 // layouts of tiles kt = 0, 1; the V^T operand uses the same slot order (two
 // 4-key runs of the transposed value cache).
-template <int NES>
+// QTW query tiles per wave: with QTW = 2 one wave scores both tiles of a
+// chunk from one load of its keys and values (the batched pass); with 1 the
+// tiles run as separate waves.
+template <int NES, int QTW>
 __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   constexpr int NET = 2 * NES;            // e-tiles of 16 covering 32*NES dims
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
   const int n_qt_max = (G + 1) / 2;
-  const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z % n_qt_max;
-  const int seq = blockIdx.z / n_qt_max;
+  const int n_qw = (n_qt_max + QTW - 1) / QTW;  // waves per (chunk, kv head, sequence)
+  const int c = blockIdx.x, h = blockIdx.y, qw = blockIdx.z % n_qw;
+  const int seq = blockIdx.z / n_qw;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
   const int key0 = c * kAttnChunk;
   const int32_t* table = a.block_table + (size_t)seq * a.n_blocks;
@@ -92,15 +96,19 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   // vectors hold finite values from earlier passes; their scores are masked
   // below.  Issued before the pass descriptor is read, with the chunk's two
   // cache blocks (the second clamped to the table).
-  uint4 qf[NES][2];
+  uint4 qf[QTW][NES][2];
 #pragma unroll
-  for (int es = 0; es < NES; ++es) {
-    const bool ok = qt < n_qt_max && 32 * es + 8 * grp < hd;
+  for (int q = 0; q < QTW; ++q) {
+    const int qt = qw * QTW + q;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t off =
-          (uint32_t)((((((size_t)h * n_qt_max + qt) * n_es + es) * 2 + p) * 64 + lane) * 16);
-      qf[es][p] = load16(rq, ok ? off : kOOB);
+    for (int es = 0; es < NES; ++es) {
+      const bool ok = qt < n_qt_max && 32 * es + 8 * grp < hd;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t off =
+            (uint32_t)((((((size_t)h * n_qt_max + qt) * n_es + es) * 2 + p) * 64 + lane) * 16);
+        qf[q][es][p] = load16(rq, ok ? off : kOOB);
+      }
     }
   }
   const int blk0 = table[2 * c];
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   const int n_keys = pos0 + n_rows;
   if (n_rows <= 0 || key0 >= n_keys) return;
   const int QG = G * n_rows, n_qt = (QG + 15) / 16;
-  if (qt >= n_qt) return;
+  if (qw * QTW >= n_qt) return;
   const int blk1 = key0 + kBlock < n_keys ? blk1_any : blk0;
   const float scale = 1.0f / sqrtf((float)hd);
   const size_t hs = (size_t)seq * n_kv + h;  // (sequence, kv head) slice of the workspace
@@ -146,6 +154,10 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     }
   }
 
+#pragma unroll
+  for (int q = 0; q < QTW; ++q) {
+  const int qt = qw * QTW + q;
+  if (qt >= n_qt) break;  // wave-uniform
   // ---- scores S^T = K Q^T for the 32 keys -----------------------------
   floatx4 s[2];
 #pragma unroll
@@ -153,9 +165,9 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int es = 0; es < NES; ++es) {
-      s[kt] = mfma16(kf[kt][es][0], qf[es][0], s[kt]);
-      s[kt] = mfma16(kf[kt][es][0], qf[es][1], s[kt]);
-      s[kt] = mfma16(kf[kt][es][1], qf[es][0], s[kt]);
+      s[kt] = mfma16(kf[kt][es][0], qf[q][es][0], s[kt]);
+      s[kt] = mfma16(kf[kt][es][0], qf[q][es][1], s[kt]);
+      s[kt] = mfma16(kf[kt][es][1], qf[q][es][0], s[kt]);
     }
   }
   const int qi = 16 * qt + l16;
@@ -201,6 +213,7 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
       *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = make_float4(o[0], o[1], o[2], o[3]);
   }
   if (grp == 0 && qi < QG) wsml[qi] = make_float2(mx, lsum);
+  }  // query tiles
 }
 
 // Merge of the chunk partials of query vector qi of kv head h.  Thread
@@ -311,8 +324,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int NES>
 static void launch_partial(const AttnArgs& a, int n_seq, hipStream_t s) {
   const int n_qt_max = (a.n_q / a.n_kv + 1) / 2;  // 16-query tiles of kMaxRows rows
-  hipLaunchKernelGGL(attn_partial_kernel<NES>, dim3(a.max_chunks, a.n_kv, n_qt_max * n_seq),
-                     dim3(64), 0, s, a);
+  if (a.qt_per_wave == 2 && n_qt_max > 1) {
+    hipLaunchKernelGGL((attn_partial_kernel<NES, 2>),
+                       dim3(a.max_chunks, a.n_kv, (n_qt_max + 1) / 2 * n_seq), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_partial_kernel<NES, 1>), dim3(a.max_chunks, a.n_kv, n_qt_max * n_seq),
+                       dim3(64), 0, s, a);
+  }
 }
 
 hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {

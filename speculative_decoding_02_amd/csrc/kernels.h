@@ -34,6 +34,7 @@ struct AttnArgs {
   // packed output, laid out in a_tiles row tiles (rows GEMM layout; 0 or 1:
   // the single pass's 16-row tile).
   int n_seq, seq_rows, a_tiles;
+  int qt_per_wave;           // 2: one wave scores both 16-query tiles of a chunk (0 or 1: one)
 };
 constexpr int kAttnChunk = 32;  // keys per partial (one wave), two cache blocks
 // n_rows: rows the pass can have (bounds the merge grid); rows beyond

@@ -266,7 +266,10 @@ hipError_t enqueue_pass(spec_batch* c, hipStream_t s, int mode, int R, int pos0,
       at.max_chunks = c->max_chunks; at.n_blocks = c->n_blocks;
       at.ws_o = c->attn_wo; at.ws_ml = c->attn_ml;
       at.qg_max = (m.nq / m.nkv) * kMaxRows; at.Ap_out = c->ap;
-      at.n_seq = B; at.seq_rows = R; at.a_tiles = RT;
+      // one wave per chunk for both query tiles once the batch fills the chip
+      // (measured: 11.55 -> 11.29 ms at B = 25; at B = 1 the halved wave count
+      // is slower)
+      at.n_seq = B; at.seq_rows = R; at.a_tiles = RT; at.qt_per_wave = B >= 4 ? 2 : 1;
       e = launch_attn(at, R, s);
     }
     if (e == hipSuccess) e = gemm(c, m.o[l], M, c->x, m.d, 1, s, &split);
