@@ -259,6 +259,31 @@ def test_8b_shaped_slice_batch(greedy):
     sd.spec_batch_destroy(bc)
 
 
+def test_graph_replays_equal_eager_launches():
+    """The captured verify pass, replayed round after round (with host work
+    and synchronisation between replays), gives bit-identical rows, logits
+    and decisions to the same pass launched without a graph."""
+    import speculative_decoding_02_amd as sd
+    w = synth.weights_np(MID)
+    tdev, = dev_weights(w)
+    B, K, V = 5, 3, MID.vocab
+    prompts = batch_prompts(V, B, 10)
+    ctxs = [sd.spec_batch_init(MID, tdev, prompts, k_max=K, max_seq=40, greedy=False,
+                               use_graphs=g) for g in (True, False)]
+    bufs = [BatchBuffers(B, K, V) for _ in ctxs]
+    rng = np.random.default_rng(3)
+    for r in range(5):
+        D_np = rng.dirichlet(np.full(V, 0.3), size=(B, K)).astype(np.float32)
+        d_np = D_np.argmax(axis=-1).astype(np.int32)
+        got = [gpu_batch_round(sd, bc, K, 11, buf, d_np, D_np) for bc, buf in zip(ctxs, bufs)]
+        for key in ("T", "logits", "out", "nacc"):
+            assert np.array_equal(got[0][key], got[1][key]), (r, key)
+    lens = [sd.spec_batch_get_state(bc)["len"] for bc in ctxs]
+    assert np.array_equal(lens[0], lens[1])
+    for bc in ctxs:
+        sd.spec_batch_destroy(bc)
+
+
 def test_batch_errors(toy_w):
     import speculative_decoding_02_amd as sd
     tdev, = dev_weights(toy_w)
