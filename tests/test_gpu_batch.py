@@ -154,10 +154,12 @@ def test_toy_batch_rounds_match_oracle(toy_w, B, K, greedy):
     run_teacher_forced(sd, synth.TOY, toy_w, B, K, greedy, rounds=5, prompt_len=20)
 
 
-def test_toy_largest_batch(toy_w):
-    """16 sequences x (7 + 1) rows = 128 activation rows, the rows GEMM's limit."""
+@pytest.mark.parametrize("B,K", [(16, 7), (32, 3)])
+def test_toy_largest_batch(toy_w, B, K):
+    """128 activation rows (the rows GEMM's limit): 16 sequences x 8 rows, and
+    the most sequences a context takes, 32 x 4 rows."""
     import speculative_decoding_02_amd as sd
-    acc = run_teacher_forced(sd, synth.TOY, toy_w, 16, 7, False, rounds=3, prompt_len=12)
+    acc = run_teacher_forced(sd, synth.TOY, toy_w, B, K, False, rounds=3, prompt_len=12)
     assert acc > 0
 
 
