@@ -11,7 +11,8 @@ sizes), with fewer layers so the fp64 oracle finishes in seconds:
     head), K = 5;
   * 1.3B-shaped slice (MHA 16 x 128, vocab 32000) with a draft sharing the
     target's embedding and LM head;
-  * a long context: 1500-token prompt through 32/8 x 128 attention.
+  * a long context: 1500-token prompt through 32/8 x 128 attention;
+  * the benchmark's own workload at full size (sampled outputs, below).
 
 Every round is teacher-forced: draft rows (1e-4) and samples (bit-exact),
 target logits (2e-2) and rows (1e-4), accept/reject on the GPU's own rows
@@ -20,6 +21,7 @@ near-ties, and the committed state."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from gpu_util import Buffers, Shadow
 
@@ -90,3 +92,50 @@ def test_long_context_attention():
     t = synth.ModelConfig("long-ctx-1L", 1, 256, 32, 8, 128, 512, 1024)
     d = t.replace(name="long-ctx-draft")
     run_case(t, d, prompt_len=1500, K=4, rounds=3, greedy=False)
+
+
+def test_8b_bench_workload_sampled():
+    """The benchmark's workload at full size: the 8B-shaped target and
+    1B-shaped draft at full depth, bench.py's 1024-token prompt, K = 4,
+    sampling, in its launch plans.  The fp64 oracle cannot run this forward
+    in test time, so what is checked is what it computes output by output:
+    every draft token is the oracle sampler's draw from the GPU's own draft
+    row (word 0 at its position), every decision is the oracle rule on the
+    GPU's own target and draft rows (bit-exact), every row is a probability
+    distribution, the state advances by n_acc + 1; and row 0 of the first
+    five-row verify equals, bit for bit, a one-row verify (K = 0) of the same
+    context in a second context (the launch plans depend on the shapes only,
+    and no row's arithmetic depends on the other rows)."""
+    import speculative_decoding_02_amd as sd
+    from gpu_util import gpu_round
+    tcfg, dcfg = synth.L8B, synth.L8B_DRAFT
+    tw = synth.weights_torch(tcfg, device="cuda")
+    dw = synth.weights_torch(dcfg, seed=synth.SEED_WEIGHTS + 1, device="cuda")
+    torch.cuda.synchronize()
+    plen, K, seed, rounds = 1024, 4, synth.SEED_PHILOX, 4
+    prompt = synth.prompt(tcfg.vocab, plen)
+    max_seq = plen + rounds * (K + 1) + 24
+    ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=False)
+    ref = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=max_seq, greedy=False)
+    b, b1 = Buffers(K, tcfg.vocab), Buffers(K, tcfg.vocab)
+    LT = plen - 1
+    for r in range(rounds):
+        g = gpu_round(sd, ctx, K, seed, b)
+        for i in range(K):
+            assert oracle.draft_sample(g["D"][i], seed, LT + 1 + i, 0, 0, False) == int(g["d"][i])
+        for rows in (g["D"], g["T"]):
+            assert np.all(rows >= 0.0) and np.abs(rows.sum(axis=-1) - 1.0).max() < 1e-4
+        rc, n, out = oracle.verify_sample(g["T"], g["D"], g["d"], seed, 0, 0, LT + 1)
+        assert rc == 0 and n == g["nacc"] and list(out[: n + 1]) == list(g["out"][: n + 1])
+        if r == 0:
+            sd.spec_verify(ref, 0, seed, None, None, b1.out, b1.nacc, b1.T, b1.logits)
+            sd.spec_sync(ref)
+            lerr = float(np.abs(b1.logits.cpu().numpy()[0] - g["logits"][0]).max())
+            perr = float(np.abs(b1.T.cpu().numpy()[0] - g["T"][0]).max())
+            print(f"row 0, five-row vs one-row pass: logits {lerr:.2e}, probabilities {perr:.2e}")
+            assert lerr == 0.0 and perr == 0.0  # same plans and per-row arithmetic
+            sd.spec_destroy(ref)
+        LT += n + 1
+        st = sd.spec_get_state(ctx)
+        assert st["device_error"] == 0 and st["target_len"] == LT
+    sd.spec_destroy(ctx)
