@@ -286,6 +286,47 @@ def test_graph_replays_equal_eager_launches():
         sd.spec_batch_destroy(bc)
 
 
+def test_8b_full_size_batch_sampled():
+    """The batched verify at the benchmark's size: the full 8B-shaped target
+    (32 layers), 1024-token prompts, K = 4.  What the oracle computes output
+    by output: each sequence's decision on the GPU's own rows (bit-exact,
+    sequence index b), every row a distribution.  And batch invariance: a
+    3-sequence batch and a 4-sequence batch holding the same three (both
+    through the wide GEMM) give those three bit-identical rows, logits and
+    decisions -- no row's arithmetic depends on the other sequences."""
+    import speculative_decoding_02_amd as sd
+    tcfg = synth.L8B
+    tw = synth.weights_torch(tcfg, device="cuda")
+    torch.cuda.synchronize()
+    K, seed, rounds, plen = 4, 1003, 2, 1024
+    V = tcfg.vocab
+    prompts = batch_prompts(V, 4, plen)
+    max_seq = plen + rounds * (K + 1) + 8
+    big = sd.spec_batch_init(tcfg, tw, prompts, k_max=K, max_seq=max_seq, greedy=False)
+    small = sd.spec_batch_init(tcfg, tw, prompts[:3], k_max=K, max_seq=max_seq, greedy=False)
+    bb, bs = BatchBuffers(4, K, V), BatchBuffers(3, K, V)
+    rng = np.random.default_rng(5)
+    LT = np.full(4, plen - 1)
+    for _ in range(rounds):
+        D_np = rng.dirichlet(np.full(V, 0.05), size=(4, K)).astype(np.float32)
+        D_np /= D_np.sum(axis=-1, keepdims=True)
+        d_np = np.stack([[oracle.draft_sample(D_np[b, i], seed, int(LT[b]) + 1 + i, b, 0, False)
+                          for i in range(K)] for b in range(4)]).astype(np.int32)
+        g = gpu_batch_round(sd, big, K, seed, bb, d_np, D_np)
+        h = gpu_batch_round(sd, small, K, seed, bs, d_np[:3], D_np[:3])
+        for key in ("T", "logits", "out", "nacc"):
+            assert np.array_equal(g[key][:3], h[key]), key
+        for b in range(4):
+            rows = g["T"][b]
+            assert np.all(rows >= 0.0) and np.abs(rows.sum(axis=-1) - 1.0).max() < 1e-4
+            rc, n, out = oracle.verify_sample(rows, D_np[b], d_np[b], seed, b, 0, int(LT[b]) + 1)
+            assert rc == 0 and n == g["nacc"][b] and list(out[: n + 1]) == list(g["out"][b][: n + 1])
+            LT[b] += n + 1
+        assert list(sd.spec_batch_get_state(big)["len"]) == list(LT)
+    sd.spec_batch_destroy(big)
+    sd.spec_batch_destroy(small)
+
+
 def test_batch_errors(toy_w):
     import speculative_decoding_02_amd as sd
     tdev, = dev_weights(toy_w)
