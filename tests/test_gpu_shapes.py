@@ -139,3 +139,55 @@ def test_8b_bench_workload_sampled():
         st = sd.spec_get_state(ctx)
         assert st["device_error"] == 0 and st["target_len"] == LT
     sd.spec_destroy(ctx)
+
+
+def test_8b_bench_workload_other_drafters_sampled():
+    """The drafters without a draft model at the benchmark's size (full
+    8B-shaped target, 1024-token prompt, K = 4, sampling), alternating:
+    multi-token heads (four random 4096 x 4096 heads) -- every draft the
+    oracle sampler's draw from the GPU's own head row, word 0 at its
+    position -- and prompt lookup -- drafts equal to the oracle's search over
+    the GPU's history, one-hot rows exact; the rule bit-exact on the GPU's
+    rows after either, and the committed state."""
+    import speculative_decoding_02_amd as sd
+    from gpu_util import Buffers
+    tcfg, dcfg = synth.L8B, synth.L8B_DRAFT
+    tw = synth.weights_torch(tcfg, device="cuda")
+    dw = synth.weights_torch(dcfg, seed=synth.SEED_WEIGHTS + 1, device="cuda")
+    W = synth.heads_torch(tcfg, 4)
+    torch.cuda.synchronize()
+    plen, K, seed, rounds = 1024, 4, synth.SEED_PHILOX, 4
+    prompt = synth.prompt(tcfg.vocab, plen)
+    ctx = sd.spec_init(tcfg, tw, dcfg, dw, prompt, k_max=K, max_seq=plen + rounds * (K + 1) + 24,
+                       greedy=False)
+    sd.spec_heads_init(ctx, W, 4)
+    b = Buffers(K, tcfg.vocab)
+    LT = plen - 1
+    for r in range(rounds):
+        heads = r % 2 == 0
+        if heads:
+            sd.spec_draft_heads(ctx, K, seed, b.d, b.D)
+        else:
+            sd.spec_draft_ngram(ctx, K, 3, b.d, b.D)
+        sd.spec_verify(ctx, K, seed, b.d, b.D, b.out, b.nacc, b.T, b.logits)
+        sd.spec_commit(ctx, b.out, b.nacc)
+        sd.spec_sync(ctx)
+        d, D, T = b.d.cpu().numpy(), b.D.cpu().numpy(), b.T.cpu().numpy()
+        out, n_acc = b.out.cpu().numpy(), int(b.nacc.cpu().numpy()[0])
+        if heads:
+            assert np.all(D >= 0.0) and np.abs(D.sum(axis=-1) - 1.0).max() < 1e-4
+            for i in range(K):
+                assert oracle.draft_sample(D[i], seed, LT + 1 + i, 0, 0, False) == int(d[i])
+        else:
+            hist = sd.spec_get_history(ctx, LT + 1)
+            ref, _ = oracle.ngram_draft(hist, LT, K, 3)
+            assert list(d) == list(ref)
+            onehot = np.zeros_like(D)
+            onehot[np.arange(K), ref] = 1.0
+            assert np.array_equal(D, onehot)
+        rc, n, o = oracle.verify_sample(T, D, d, seed, 0, 0, LT + 1)
+        assert rc == 0 and n == n_acc and list(o[: n + 1]) == list(out[: n + 1])
+        LT += n + 1
+        st = sd.spec_get_state(ctx)
+        assert st["device_error"] == 0 and st["target_len"] == LT
+    sd.spec_destroy(ctx)
