@@ -118,7 +118,8 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
  * stream_id), or the top token in greedy mode.
  *   d_dev: int32 [K];  D_dev: fp32 [K][vocab].
  * Errors: SPEC_ERR_ARG (K outside 1..k_max, null pointers), SPEC_ERR_CAPACITY,
- * SPEC_ERR_STATE (the draft cache lags by more than 7 tokens). */
+ * SPEC_ERR_STATE (a verify is pending: drafting now would re-draft positions
+ * whose decision awaits its commit and corrupt the draft cache). */
 int spec_draft(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D_dev);
 
 /* Prompt-lookup drafter ([en] Floor 6, [zh] Level 6: n-gram approaches such
@@ -134,7 +135,7 @@ int spec_draft(spec_ctx* ctx, int32_t K, uint64_t seed, int32_t* d_dev, float* D
  * left as it is (a later spec_draft catches it up).
  *   d_dev: int32 [K]; D_dev: fp32 [K][vocab] (may be NULL in greedy mode).
  * Errors: SPEC_ERR_ARG (K outside 1..k_max, n_max outside 1..8, null
- * pointers). */
+ * pointers), SPEC_ERR_STATE (a verify is pending). */
 int spec_draft_ngram(spec_ctx* ctx, int32_t K, int32_t n_max, int32_t* d_dev, float* D_dev);
 
 /* Multi-token-prediction heads as the drafter ("Speculative decoding

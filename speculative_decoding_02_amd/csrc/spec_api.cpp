@@ -772,6 +772,7 @@ int spec_draft(spec_ctx* c, int32_t K, uint64_t seed, int32_t* d_dev, float* D_d
   if (!c) return fail(nullptr, SPEC_ERR_ARG, "spec_draft: null context");
   if (K < 1 || K > c->p.k_max) return fail(c, SPEC_ERR_ARG, fmt("K=%d outside 1..k_max", K));
   if (!d_dev || !D_dev) return fail(c, SPEC_ERR_ARG, "spec_draft: null output");
+  if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_draft: a verify is pending");
   HIPTRY(c, hipSetDevice(c->device));
   if (c->lag_ub > kMaxRows - 1 || c->LT_ub + K > c->p.max_seq) {
     DevState hs;
@@ -804,6 +805,7 @@ int spec_draft_ngram(spec_ctx* c, int32_t K, int32_t n_max, int32_t* d_dev, floa
   if (n_max < 1 || n_max > kNgramMaxN)
     return fail(c, SPEC_ERR_ARG, fmt("n_max=%d outside 1..%d", n_max, kNgramMaxN));
   if (!d_dev || (!D_dev && !c->p.greedy)) return fail(c, SPEC_ERR_ARG, "spec_draft_ngram: null output");
+  if (c->verify_pending) return fail(c, SPEC_ERR_STATE, "spec_draft_ngram: a verify is pending");
   HIPTRY(c, hipSetDevice(c->device));
   std::vector<uint64_t> key = {kPassNgram, (uint64_t)K, (uint64_t)n_max, (uint64_t)(uintptr_t)d_dev,
                                (uint64_t)(uintptr_t)D_dev};

@@ -114,3 +114,44 @@ def test_repeatable():
         b = run_gpu(T, D, d, 1, pos, 0, False)
         np.testing.assert_array_equal(a[0], b[0])
         np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_greedy_ties_lowest_index():
+    """Greedy mode with several equal maxima in a row ([zh] Level 4, greedy
+    checking; ties go to the lowest index): a draft at a later tied index is
+    rejected and replaced by the lowest one, a draft at the lowest passes;
+    ties span vocabulary chunks; a row of signed zeros (-0.0 and +0.0 only)
+    has its maximum 0 at index 0.  Bit-exact against the oracle and against
+    the expected tokens written out."""
+    B, K, V = 4, 3, 5000
+    rng = np.random.default_rng(21)
+    T = (rng.random((B, K + 1, V)) * 1e-4).astype(np.float32)
+    tie = np.float32(0.0625)
+    for b in range(B):
+        for i in range(K + 1):
+            T[b, i, [1500 + 7 * i, 3000, 4999]] = tie   # tied maxima in chunks 1, 2 and 4
+    # sequence 0: drafts at the lowest tied index -> all pass, bonus = lowest of row K
+    # sequence 1: draft 1 at a later tied index -> rejected at position 1
+    # sequence 2: row 0 is all signed zeros (max 0 at index 0); draft 0 = 0 passes,
+    #             draft 1 at a later tied index is rejected
+    # sequence 3: draft 0 at the last tied index -> rejected at once
+    T[2, 0, :] = np.where(np.arange(V) % 2 == 0, np.float32(-0.0), np.float32(0.0))
+    T[2, 0, 0] = np.float32(-0.0)
+    low = [1500 + 7 * i for i in range(K + 1)]
+    d = np.array([[low[0], low[1], low[2]],
+                  [low[0], 3000, low[2]],
+                  [0, 4999, low[2]],
+                  [4999, low[1], low[2]]], np.int32)
+    D = np.zeros((B, K, V), np.float32)  # not read in greedy mode
+    pos = np.arange(B, dtype=np.uint64) * 10
+    og, ng = run_gpu(T, D, d, 3, pos, 0, True)
+    oo, no = oracle.accept_reject_batch(T, D, d, 3, pos, 0, True)
+    np.testing.assert_array_equal(ng, no)
+    np.testing.assert_array_equal(og, oo)
+    want_n = [3, 1, 1, 0]
+    want_out = [[low[0], low[1], low[2], low[3]],
+                [low[0], low[1], -1, -1],
+                [0, low[1], -1, -1],
+                [low[0], -1, -1, -1]]
+    assert ng.tolist() == want_n
+    assert og.tolist() == want_out

@@ -160,6 +160,13 @@ def test_external_drafts_and_state_errors(toy):
         with pytest.raises(sd.SpecError) as e:
             sd.spec_verify(ctx, K, 9, b.d, b.D, b.out, b.nacc)
         assert e.value.code == sd.SPEC_ERR_STATE
+        # drafting between a verify and its commit is refused too (it would
+        # re-draft the positions awaiting their decision), by every drafter
+        for draft in (lambda: sd.spec_draft(ctx, K, 9, b.d, b.D),
+                      lambda: sd.spec_draft_ngram(ctx, K, 3, b.d, b.D)):
+            with pytest.raises(sd.SpecError) as e:
+                draft()
+            assert e.value.code == sd.SPEC_ERR_STATE
         sd.spec_commit(ctx, b.out, b.nacc)
         sd.spec_sync(ctx)
         T = b.T.cpu().numpy(); out = b.out.cpu().numpy(); n = int(b.nacc.cpu().numpy()[0])

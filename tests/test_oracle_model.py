@@ -37,6 +37,43 @@ def test_rope_is_rotation_and_composes():
                                    atol=1e-9)
 
 
+def test_rope_angle_schedule_closed_form():
+    """The frequencies themselves.  hd = 4, theta = 1e4: pair j = 0 holds dims
+    (0, 2) and turns by pos * 1e4^0 = pos rad, pair j = 1 holds dims (1, 3)
+    and turns by pos * 1e4^(-2/4) = pos / 100 rad.  A basis vector e_j goes
+    to cos(a) e_j + sin(a) e_{j+2} (rotate-half: x_j' = x_j cos - x_{j+2} sin,
+    x_{j+2}' = x_{j+2} cos + x_j sin).  A wrong exponent (theta^(-j/hd),
+    theta^(-2j/(hd-2))) or a wrong pairing (j with j+1) moves these values."""
+    for pos in (1, 7):
+        for j, ang in ((0, float(pos)), (1, pos / 100.0)):
+            e = np.zeros(4)
+            e[j] = 1.0
+            want = np.zeros(4)
+            want[j], want[j + 2] = np.cos(ang), np.sin(ang)
+            np.testing.assert_allclose(oracle.rope(e, pos, 1e4), want, atol=1e-15)
+            e2 = np.zeros(4)
+            e2[j + 2] = 1.0
+            want2 = np.zeros(4)
+            want2[j], want2[j + 2] = -np.sin(ang), np.cos(ang)
+            np.testing.assert_allclose(oracle.rope(e2, pos, 1e4), want2, atol=1e-15)
+
+
+def test_rope_angle_schedule_8b_head():
+    """One 8B-shaped head (hd = 128, theta = 5e5) at position 1000 on a random
+    vector, against math.cos / math.sin of pos * theta^(-2j/hd) written out
+    per pair (j, j + 64)."""
+    import math
+    hd, theta, pos = 128, 5e5, 1000
+    v = np.random.default_rng(4).standard_normal(hd)
+    got = oracle.rope(v, pos, theta)
+    h = hd // 2
+    for j in range(h):
+        a = pos * theta ** (-2.0 * j / hd)
+        c, s = math.cos(a), math.sin(a)
+        assert abs(got[j] - (v[j] * c - v[j + h] * s)) < 1e-12
+        assert abs(got[j + h] - (v[j + h] * c + v[j] * s)) < 1e-12
+
+
 def test_rope_scores_depend_on_relative_position():
     rng = np.random.default_rng(2)
     q, k = rng.standard_normal(64), rng.standard_normal(64)
