@@ -412,6 +412,26 @@ int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_
                        uint64_t stream_id, int32_t greedy, int32_t* out_dev, int32_t* n_acc_dev,
                        void* hip_stream);
 
+/* spec_accept_reject for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and results, but the chunk
+ * partials live in a fixed device array of SPEC_AR_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends.
+ * No call allocates or frees device memory.  Every call on one device shares
+ * that device's array and leaves its contents behind; calls that overlap on
+ * one device (different streams, or with no ordering between them) race and
+ * must be serialised by the caller.
+ * Errors: those of spec_accept_reject, and SPEC_ERR_CAPACITY when B, K and V
+ * need more scratch than the fixed size (B * chunks(B, V) * max(K + 2, 4)
+ * 8-byte words, chunks(B, V) = min(ceil(512 / B), ceil(V / 1024), 512)
+ * rounded up to whole 256-entry chunks; e.g. B = 64, K = 8, V = 32000 needs
+ * 40 KiB). */
+#define SPEC_AR_NOALLOC_SCRATCH_BYTES (2u << 20)
+int spec_accept_reject_noalloc(const float* T_dev, const float* D_dev, const int32_t* d_dev,
+                               int32_t B, int32_t K, int32_t V, uint64_t seed,
+                               const uint64_t* pos_dev, uint64_t stream_id, int32_t greedy,
+                               int32_t* out_dev, int32_t* n_acc_dev, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

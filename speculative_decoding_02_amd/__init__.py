@@ -6,7 +6,8 @@ from .binding import (  # noqa: F401
     SPEC_ERR_HIP, SPEC_K_MAX, SPEC_AR_K_MAX, EXPORTED, LIBPATH,
     spec_init, spec_draft, spec_draft_ngram, spec_heads_init, spec_draft_heads, spec_verify, spec_commit, spec_destroy, spec_last_error, spec_sync,
     spec_stream, spec_get_state, spec_get_history, spec_kernel_times, spec_set_profiling, spec_head_time,
-    spec_accept_reject, spec_expected_tokens, spec_alpha_from_tokens, spec_choose_k,
+    spec_accept_reject, spec_accept_reject_noalloc, spec_expected_tokens, spec_alpha_from_tokens,
+    spec_choose_k,
     spec_mat_create, spec_mat_mul, spec_mat_destroy, spec_read_ceiling,
     Batch, SPEC_BATCH_MAX_SEQ, spec_batch_init, spec_batch_draft_ngram, spec_batch_verify,
     spec_batch_commit, spec_batch_sync, spec_batch_get_state, spec_batch_get_history,

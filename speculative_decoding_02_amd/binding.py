@@ -108,6 +108,8 @@ def lib():
         L.spec_head_time.argtypes = [_p, C.POINTER(C.c_float)]
         L.spec_accept_reject.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32, _p,
                                          _p, _p]
+        L.spec_accept_reject_noalloc.argtypes = [_p, _p, _p, _i32, _i32, _i32, _u64, _p, _u64, _i32,
+                                                 _p, _p, _p]
         L.spec_read_ceiling.argtypes = [_p, _u64, _i32, _p, C.POINTER(C.c_double)]
         L.spec_batch_init.argtypes = [C.POINTER(SpecBatchParams), _p, _i32, C.POINTER(_p)]
         L.spec_batch_draft_ngram.argtypes = [_p, _i32, _i32, _p, _p]
@@ -126,7 +128,8 @@ def lib():
 EXPORTED = ("spec_init", "spec_draft", "spec_draft_ngram", "spec_heads_init", "spec_draft_heads",
             "spec_verify", "spec_commit", "spec_destroy",
             "spec_last_error", "spec_sync", "spec_stream", "spec_get_state", "spec_get_history",
-            "spec_kernel_times", "spec_set_profiling", "spec_head_time", "spec_accept_reject", "spec_expected_tokens",
+            "spec_kernel_times", "spec_set_profiling", "spec_head_time", "spec_accept_reject",
+            "spec_accept_reject_noalloc", "spec_expected_tokens",
             "spec_alpha_from_tokens", "spec_choose_k", "spec_mat_create", "spec_mat_mul",
             "spec_mat_destroy", "spec_read_ceiling", "spec_batch_init", "spec_batch_draft_ngram",
             "spec_batch_verify", "spec_batch_commit", "spec_batch_sync", "spec_batch_get_state",
@@ -334,6 +337,16 @@ def spec_accept_reject(T, D, d, seed: int, pos, stream_id: int, greedy: bool, ou
                                     stream_id, int(bool(greedy)), _ptr(out), _ptr(n_acc),
                                     stream or None))
 
+
+
+def spec_accept_reject_noalloc(T, D, d, seed: int, pos, stream_id: int, greedy: bool, out, n_acc,
+                               stream: int = 0) -> None:
+    """spec_accept_reject with the library's fixed scratch array instead of an
+    allocated workspace (same arguments and results)."""
+    B, K1, V = T.shape
+    _check(lib().spec_accept_reject_noalloc(_ptr(T), _ptr(D), _ptr(d), B, K1 - 1, V, seed,
+                                            _ptr(pos), stream_id, int(bool(greedy)), _ptr(out),
+                                            _ptr(n_acc), stream or None))
 
 # ------------------------------------------------------- batched verify --
 class Batch:

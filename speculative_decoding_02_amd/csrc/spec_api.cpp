@@ -1158,25 +1158,44 @@ struct ArWorkspace {
 };
 std::mutex g_ar_mu;
 std::map<int, ArWorkspace> g_ar;
+
+// Argument checks and the launch plan shared by both stateless entry points.
+// Returns SPEC_OK and fills a (all but ws) and *words, or an error code.
+int ar_prepare(const char* who, const float* T_dev, const float* D_dev, const int32_t* d_dev,
+               int32_t B, int32_t K, int32_t V, uint64_t seed, const uint64_t* pos_dev,
+               uint64_t stream_id, int32_t greedy, int32_t* out_dev, int32_t* n_acc_dev,
+               ArArgs* a, size_t* words) {
+  if (B < 0 || K < 1 || K > SPEC_AR_K_MAX || V < 1)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("%s: bad B, K or V", who));
+  if (B > 0 && (!T_dev || !d_dev || !pos_dev || !out_dev || !n_acc_dev || (!greedy && !D_dev)))
+    return fail(nullptr, SPEC_ERR_ARG, fmt("%s: null pointer", who));
+  int chunk = 0, nch = 0;
+  ar_choose_chunks(B, V, &chunk, &nch);
+  if ((long long)B * nch > 0x7fffffffLL)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("%s: batch too large for one launch", who));
+  *a = ArArgs{};
+  a->T = T_dev; a->D = D_dev; a->d = d_dev; a->B = B; a->K = K; a->V = V;
+  a->seed = seed; a->stream_id = stream_id; a->pos = pos_dev; a->st = nullptr; a->pos_offset = 0;
+  a->greedy = greedy; a->word = 2; a->chunk = chunk; a->n_chunks = nch;
+  a->out = out_dev; a->n_acc = n_acc_dev;
+  *words = (size_t)B * nch * ar_ws_words(K);
+  return SPEC_OK;
+}
 }  // namespace
 
 int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_dev, int32_t B,
                        int32_t K, int32_t V, uint64_t seed, const uint64_t* pos_dev,
                        uint64_t stream_id, int32_t greedy, int32_t* out_dev, int32_t* n_acc_dev,
                        void* hip_stream) {
-  if (B < 0 || K < 1 || K > SPEC_AR_K_MAX || V < 1)
-    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: bad B, K or V");
+  ArArgs a;
+  size_t words = 0;
+  if (int r = ar_prepare("spec_accept_reject", T_dev, D_dev, d_dev, B, K, V, seed, pos_dev,
+                         stream_id, greedy, out_dev, n_acc_dev, &a, &words))
+    return r;
   if (B == 0) return SPEC_OK;
-  if (!T_dev || !d_dev || !pos_dev || !out_dev || !n_acc_dev || (!greedy && !D_dev))
-    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: null pointer");
   hipStream_t s = (hipStream_t)hip_stream;
   int dev = 0;
   HIPTRY(nullptr, hipGetDevice(&dev));
-  int chunk, nch;
-  ar_choose_chunks(B, V, &chunk, &nch);
-  if ((long long)B * nch > 0x7fffffffLL)
-    return fail(nullptr, SPEC_ERR_ARG, "spec_accept_reject: batch too large for one launch");
-  const size_t words = (size_t)B * nch * ar_ws_words(K);
   std::lock_guard<std::mutex> lk(g_ar_mu);
   ArWorkspace& w = g_ar[dev];
   if (w.ws_words < words) {
@@ -1188,12 +1207,64 @@ int spec_accept_reject(const float* T_dev, const float* D_dev, const int32_t* d_
     HIPTRY(nullptr, dalloc(&w.ws, words));
     w.ws_words = words;
   }
-  ArArgs a{};
-  a.T = T_dev; a.D = D_dev; a.d = d_dev; a.B = B; a.K = K; a.V = V;
-  a.seed = seed; a.stream_id = stream_id; a.pos = pos_dev; a.st = nullptr; a.pos_offset = 0;
-  a.greedy = greedy; a.word = 2; a.chunk = chunk; a.n_chunks = nch;
-  a.out = out_dev; a.n_acc = n_acc_dev; a.ws = w.ws;
+  a.ws = w.ws;
   HIPTRY(nullptr, launch_accept_reject(a, s));
+  return SPEC_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------- accept/reject without allocating --
+// The chunk partials of spec_accept_reject_noalloc live in this file-scope
+// device array: every device the library runs on holds one copy, from module
+// load until the process ends.  In host code the name `scratch` is only a
+// host-side stand-in for the symbol; its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is ever handed to a kernel.  Every word a finishing block reads is
+// written by the partial kernel of the same call first, so nothing needs
+// clearing between calls.
+namespace {
+constexpr size_t kNoAllocScratchWords = SPEC_AR_NOALLOC_SCRATCH_BYTES / sizeof(uint64_t);
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint64_t scratch[kNoAllocScratchWords];
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kNoAllocMaxDevices] = {};
+}  // namespace
+
+extern "C" {
+
+int spec_accept_reject_noalloc(const float* T_dev, const float* D_dev, const int32_t* d_dev,
+                               int32_t B, int32_t K, int32_t V, uint64_t seed,
+                               const uint64_t* pos_dev, uint64_t stream_id, int32_t greedy,
+                               int32_t* out_dev, int32_t* n_acc_dev, void* hip_stream) {
+  ArArgs a;
+  size_t words = 0;
+  if (int r = ar_prepare("spec_accept_reject_noalloc", T_dev, D_dev, d_dev, B, K, V, seed, pos_dev,
+                         stream_id, greedy, out_dev, n_acc_dev, &a, &words))
+    return r;
+  if (words > kNoAllocScratchWords)
+    return fail(nullptr, SPEC_ERR_CAPACITY,
+                fmt("spec_accept_reject_noalloc: B=%d, K=%d, V=%d needs %zu bytes of scratch, "
+                    "more than the fixed %d",
+                    B, K, V, words * sizeof(uint64_t), (int)SPEC_AR_NOALLOC_SCRATCH_BYTES));
+  if (B == 0) return SPEC_OK;
+  int dev = 0;
+  HIPTRY(nullptr, hipGetDevice(&dev));
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(nullptr, SPEC_ERR_ARG, fmt("spec_accept_reject_noalloc: device %d unsupported", dev));
+  uint64_t* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      HIPTRY(nullptr, hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return fail(nullptr, SPEC_ERR_HIP, "spec_accept_reject_noalloc: no scratch address");
+      g_scratch_ptr[dev] = (uint64_t*)p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  a.ws = ws;
+  HIPTRY(nullptr, launch_accept_reject(a, (hipStream_t)hip_stream));
   return SPEC_OK;
 }
 

@@ -64,3 +64,19 @@ def test_argument_errors_need_no_device(lib):
     lib.spec_batch_last_error.restype = ctypes.c_char_p
     assert b"null" in lib.spec_batch_last_error(None)
     lib.spec_destroy(None)  # NULL is accepted
+
+
+def test_noalloc_size_limit_needs_no_device(lib):
+    """The allocation-free rule refuses, on the host, a batch whose chunk
+    partials would not fit its fixed scratch (65536 x 1 chunk x 65 words)."""
+    import speculative_decoding_02_amd as sd
+    f = lib.spec_accept_reject_noalloc
+    f.restype = ctypes.c_int
+    fake = ctypes.c_void_p(256)  # never dereferenced: the size check comes first
+    rc = f(fake, fake, fake, 1 << 16, 63, 1024, ctypes.c_uint64(0), fake, ctypes.c_uint64(0), 0,
+           fake, fake, None)
+    assert rc == sd.SPEC_ERR_CAPACITY
+    lib.spec_last_error.restype = ctypes.c_char_p
+    assert b"scratch" in lib.spec_last_error(None)
+    assert f(None, None, None, 0, 0, 10, ctypes.c_uint64(0), None, ctypes.c_uint64(0), 0, None,
+             None, None) == sd.SPEC_ERR_ARG
