@@ -14,7 +14,8 @@ from typing import Mapping, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIBPATH = os.path.join(_HERE, "liboracle.so")
+# SPEC_ORACLE_LIB: another build of the same source (the sanitizer build)
+_LIBPATH = os.environ.get("SPEC_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 OK, EARG, EBADPROB, ENOMEM, ECAPACITY = 0, -1, -2, -3, -4
 

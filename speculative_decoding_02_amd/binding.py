@@ -13,7 +13,8 @@ from typing import Mapping, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIBPATH = os.path.join(_HERE, "libspec.so")
+# SPEC_LIBSPEC: another build of the same sources (the host-sanitizer build)
+LIBPATH = os.environ.get("SPEC_LIBSPEC") or os.path.join(_HERE, "libspec.so")
 
 SPEC_OK = 0
 SPEC_ERR_ARG = -1

@@ -40,6 +40,40 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# Host code built with AddressSanitizer + UndefinedBehaviorSanitizer (device
+# code unchanged), loaded instead of LIB when SPEC_LIBSPEC points at it
+# (tests/run_sanitizers.sh).
+SAN_OBJ = os.path.join(ROOT, "_build", "sanitize", "libspec")
+SAN_LIB = os.path.join(ROOT, "_build", "sanitize", "libspec.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(SAN_OBJ, exist_ok=True)
+    host = [s for s in SOURCES if s.endswith(".cpp")]
+
+    def comp(src):
+        obj = os.path.join(SAN_OBJ, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(comp, host))
+    kern = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, *objs, *kern,
+           "-o", SAN_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
@@ -62,4 +96,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_sanitized(verbose=True) if "--sanitize" in sys.argv else build(verbose=True))

@@ -221,6 +221,17 @@ def logit_pair(B: int, K: int, V: int, sigma: float, seed: int = SEED_LOGITS,
     return _softmax64(zt).astype(np.float32), _softmax64(zd).astype(np.float32)
 
 
+def drafts_from_rows(D: np.ndarray, seed: int = SEED_LOGITS) -> np.ndarray:
+    """Draft tokens for the isolated rule's inputs: one categorical draw per
+    row of D [B][K][V] with numpy's generator (an input recipe only; the
+    library's own drafters draw differently)."""
+    rng = np.random.default_rng([seed, *D.shape])
+    c = np.cumsum(D.astype(np.float64), axis=-1)
+    u = rng.random(D.shape[:-1]) * c[..., -1]
+    idx = (c < u[..., None]).sum(axis=-1)
+    return np.minimum(idx, D.shape[-1] - 1).astype(np.int32)
+
+
 def dirichlet_pair(V: int, seed: int = SEED_DIRICHLET) -> Tuple[np.ndarray, np.ndarray]:
     """T, D ~ Dirichlet(1) over V entries (normalized Exp(1)), fp32."""
     rng = np.random.default_rng([seed, V])

@@ -9,7 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec.h")
-LIB = os.path.join(ROOT, "speculative_decoding_02_amd", "libspec.so")
+# SPEC_LIBSPEC: another build of the same sources (tests/run_sanitizers.sh)
+LIB = os.environ.get("SPEC_LIBSPEC") or os.path.join(ROOT, "speculative_decoding_02_amd", "libspec.so")
 
 
 def declared():
