@@ -437,8 +437,10 @@ def ar_bench(sd, torch, np, synth, args):
     """The isolated accept/reject rule: B = 64 sequences, K = 8, V = 32000;
     T and D are fp32 softmaxes of N(0, 2) logits, draft logits = target +
     N(0, sigma).  Five input sets per sigma (T + D = 139 MB each) are
-    rotated so no call finds its rows in the 256 MB MALL.  Each call is
-    timed with hipEvents on its stream over 200 back-to-back calls."""
+    rotated so no call finds its rows in the 256 MB MALL.  200 back-to-back
+    calls are captured in a graph whose replays on the same stream are timed
+    with hipEvents (us_per_call); the same calls made eagerly from Python
+    are reported beside it (us_per_call_eager)."""
     B, K, V, n_sets, reps = 64, 8, 32000, 5, 200
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -462,17 +464,37 @@ def ar_bench(sd, torch, np, synth, args):
                 fn(T, D, d, synth.SEED_PHILOX, pos, 0, False, out, nacc, stream=stream.cuda_stream)
                 stream.synchronize()
                 nbytes.append(ar_call_bytes(nacc.cpu().numpy(), K, V))
+            # the calls as a captured graph, replayed on the same stream (as
+            # inside the decoding loop), so the host's per-call cost and eager
+            # launches do not pace the device
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(reps):
+                    T, D, d, pos = sets[r % n_sets]
+                    fn(T, D, d, synth.SEED_PHILOX, pos, 0, False, out, nacc,
+                       stream=stream.cuda_stream)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                g.replay()
+                e0.record(stream)
+                for _ in range(3):
+                    g.replay()
+                e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (3 * reps)
+            # the same calls made eagerly from Python (ctypes, two plain launches each)
             e0.record(stream)
             for r in range(reps):
                 T, D, d, pos = sets[r % n_sets]
                 fn(T, D, d, synth.SEED_PHILOX, pos, 0, False, out, nacc, stream=stream.cuda_stream)
             e1.record(stream)
             e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            us_eager = e0.elapsed_time(e1) * 1e3 / reps
+            del g
             b = float(np.mean([nbytes[r % n_sets] for r in range(reps)]))
             res[name] = {"us_per_call": round(us, 2), "algorithmic_MB": round(b / 1e6, 3),
-                         "GB_s": round(b / (us * 1e-6) / 1e9, 1)}
+                         "GB_s": round(b / (us * 1e-6) / 1e9, 1),
+                         "us_per_call_eager": round(us_eager, 2)}
         res["mean_accepted_per_sequence"] = round(float(nacc.float().mean().item()), 3)
         rows.append(res)
         log(f"accept/reject sigma={sigma}: " + json.dumps(res))

@@ -9,8 +9,10 @@
 //     sample from: the residual fix(T_j) - fix(D_j) (saturating, 2^-40 grid)
 //     on a reject, else the bonus row fix(T_K).  The fallbacks (sum of
 //     fix(T_j), argmax of the row) are gathered in the same pass.
-//  2. finish kernel, one block per sequence: repeat the accept tests, fold
-//     the chunk partials, find the chunk holding the inverse-CDF needle
+//  2. finish kernel, one block per sequence: take the decision (and the
+//     final sample's uniform, drawn with the accept tests) that the partial
+//     blocks recorded beside their sums, fold the chunk partials, find the
+//     chunk holding the inverse-CDF needle
 //     floor(u24 * Z / 2^24) (u24 = Philox w2 at the decided position) with a
 //     block prefix sum, rescan that chunk and write the emitted tokens.
 // Every sum is over 64-bit integers, so the result does not depend on the
@@ -24,34 +26,48 @@ constexpr int kArThreads = 256;
 constexpr int kArMaxChunks = 2 * kArThreads;  // the finish kernel scans 2 chunks per thread
 
 // Accept tests and draft validation (wave 0).  Writes j (first reject, K if
-// none; K in greedy mode) and whether the inputs read so far are invalid.
-SPEC_DEVICE void decide_first_reject(const ArArgs& a, int b, uint64_t P, int* s_j, int* s_err) {
+// none; K in greedy mode), whether the inputs read so far are invalid, and
+// (sampling mode) the uniform of the final sample at position P + j.  Lane
+// i <= K evaluates Philox once at P + i: word 1 is its accept test, word
+// a.word the final sample's draw should the decision land on i.
+SPEC_DEVICE void decide_first_reject(const ArArgs& a, int b, uint64_t P, int* s_j, int* s_err,
+                                     uint32_t* s_u) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
     const int K = a.K, V = a.V;
+    const bool sample = !a.greedy;
     const float* Tb = a.T + (size_t)b * (K + 1) * V;
     const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
     const int32_t* db = a.d + (size_t)b * K;
-    bool bad_d = false, stop = false, invalid = false;
-    if (lane < K) {
-      const int di = db[lane];
-      bad_d = di < 0 || di >= V;
-      if (!a.greedy && !bad_d) {
-        const float t = Tb[(size_t)lane * V + di];
-        const float q = Db[(size_t)lane * V + di];
-        invalid = !prob_valid(t) || !prob_valid(q);
-        const uint32_t u = uniform_u24(a.seed, P + lane, b, a.stream_id, 1);
-        const float rr = (float)u * 0x1p-24f;
-        stop = invalid || !((double)rr * (double)q < (double)t);
-      }
+    // draft ids, then the gathered T_i(d_i), D_i(d_i) (issued before the
+    // Philox rounds so their latency overlaps them)
+    const int di = lane < K ? db[lane] : 0;
+    const bool bad_d = lane < K && (di < 0 || di >= V);
+    const bool gather = sample && lane < K && !bad_d;
+    const float t = gather ? Tb[(size_t)lane * V + di] : 0.0f;
+    const float q = gather ? Db[(size_t)lane * V + di] : 0.0f;
+    // one Philox evaluation per lane 0..K, all lanes in step
+    uint32_t u_acc = 0, u_fin = 0;
+    if (sample && lane <= K) {
+      const U64x4 w = philox4x64_10(P + lane, b, a.stream_id, 0, a.seed, 0);
+      u_acc = (uint32_t)(w.w[1] >> 40);
+      u_fin = (uint32_t)(w.w[a.word] >> 40);
+    }
+    bool stop = false, invalid = false;
+    if (gather) {
+      invalid = !prob_valid(t) || !prob_valid(q);
+      const float rr = (float)u_acc * 0x1p-24f;
+      stop = invalid || !((double)rr * (double)q < (double)t);
     }
     const uint64_t bd = __ballot(bad_d);
     const uint64_t st = __ballot(stop || bad_d);
     const int j = st ? __ffsll((long long)st) - 1 : K;
     const uint64_t inv = __ballot(invalid);
+    const uint32_t u_j = (uint32_t)__shfl((int)u_fin, j);
     if (lane == 0) {
       *s_j = a.greedy ? K : j;
       *s_err = (bd != 0) || (!a.greedy && j < K && ((inv >> j) & 1));
+      *s_u = u_j;
     }
   }
   __syncthreads();
@@ -70,6 +86,39 @@ SPEC_DEVICE uint64_t block_sum_u64(uint64_t v, uint64_t* lds) {
   return r;
 }
 
+SPEC_DEVICE uint64_t wave_or_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v |= shfl_xor_u64(v, m);
+  return v;
+}
+
+// Four reductions in one exchange: sums of a and b, maximum of c, OR of d.
+SPEC_DEVICE void block_sum2_max_or(uint64_t& a, uint64_t& b, uint64_t& c, uint64_t& d, uint64_t* lds) {
+  a = wave_sum_u64(a);
+  b = wave_sum_u64(b);
+  c = wave_max_u64(c);
+  d = wave_or_u64(d);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    lds[4 * w] = a; lds[4 * w + 1] = b; lds[4 * w + 2] = c; lds[4 * w + 3] = d;
+  }
+  __syncthreads();
+  a = lds[0] + lds[4] + lds[8] + lds[12];
+  b = lds[1] + lds[5] + lds[9] + lds[13];
+  c = max(max(lds[2], lds[6]), max(lds[10], lds[14]));
+  d = lds[3] | lds[7] | lds[11] | lds[15];
+  __syncthreads();
+}
+
+// The decision word each partial block stores with its sums: bit 0 an
+// invalid value in its scanned rows, bit 1 an invalid draft or gathered
+// probability, bits 8..15 the first reject j, bits 32..55 (sampling mode)
+// the uniform u24 of the final sample.  Every block computes the same word
+// apart from bit 0, so the OR of all chunks' words holds them all.
+SPEC_DEVICE uint64_t decision_word(uint64_t bad, int err, int j, uint32_t u24) {
+  return (bad ? 1ull : 0ull) | (err ? 2ull : 0ull) | ((uint64_t)j << 8) | ((uint64_t)u24 << 32);
+}
+
 SPEC_DEVICE uint64_t block_max_u64(uint64_t v, uint64_t* lds) {
   v = wave_max_u64(v);
   if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
@@ -79,17 +128,33 @@ SPEC_DEVICE uint64_t block_max_u64(uint64_t v, uint64_t* lds) {
   return r;
 }
 
-// weight of token v in the row being sampled: residual, or the row itself
-SPEC_DEVICE uint64_t row_weight(const float* Tr, const float* Dr, int v) {
-  const uint64_t ft = fix40(Tr[v]);
-  if (!Dr) return ft;
-  const uint64_t fd = fix40(Dr[v]);
+// weight of a token in the row being sampled: residual fix(T) - fix(D)
+// (saturating), or the row itself
+SPEC_DEVICE uint64_t token_weight(float tv, float dv, bool residual) {
+  const uint64_t ft = fix40(tv);
+  if (!residual) return ft;
+  const uint64_t fd = fix40(dv);
   return ft > fd ? ft - fd : 0;
+}
+
+// Rows are read in passes of kArPass elements: every thread issues all
+// kArSeg loads of a pass before using any, through a buffer resource over
+// the row (V floats), so an element past the chunk reads as 0 with no
+// fetch.  Any row alignment works (dword loads).
+constexpr int kArSeg = 16;
+constexpr int kArPass = kArThreads * kArSeg;
+constexpr uint32_t kArOOB = 0x80000000u;
+SPEC_DEVICE __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int V) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, V * 4, 0x00020000);
+}
+SPEC_DEVICE float row_at(__amdgpu_buffer_rsrc_t r, int v, bool in) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)(in ? (uint32_t)v * 4 : kArOOB), 0, 0));
 }
 
 __global__ __launch_bounds__(kArThreads) void ar_partial_kernel(ArArgs a) {
   __shared__ int32_t s_j, s_err;
-  __shared__ uint64_t s_red[4];
+  __shared__ uint32_t s_u;
+  __shared__ uint64_t s_red[16];
   const int tid = threadIdx.x;
   // one block per (chunk, sequence), flattened in x (grid.y is too narrow
   // for large batches)
@@ -100,78 +165,104 @@ __global__ __launch_bounds__(kArThreads) void ar_partial_kernel(ArArgs a) {
   const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
   const int W = ar_ws_words(K);
   uint64_t* p = a.ws + ((size_t)b * a.n_chunks + c) * W;
-  decide_first_reject(a, b, P, &s_j, &s_err);
-  const int j = s_j;
+  decide_first_reject(a, b, P, &s_j, &s_err, &s_u);
+  // uniform across the block: in scalar registers, so the row's buffer
+  // descriptor is too (a descriptor the compiler cannot prove uniform costs
+  // a serial loop around every load)
+  const int j = __builtin_amdgcn_readfirstlane(s_j);
   const int lo = c * a.chunk, hi = min(V, lo + a.chunk);
 
   if (!a.greedy) {
+    // the chunk of the row to sample from: T_j and D_j after a reject at j,
+    // else the bonus row T_K; integer sums and maxima, so the element order
+    // (strided over threads, pass by pass) changes nothing
     uint64_t zr = 0, zt = 0, am = 0, bad = 0;
     if (!s_err) {
-      const float* Tr = Tb + (size_t)j * V;
-      const float* Dr = j < K ? Db + (size_t)j * V : nullptr;
-      for (int v = lo + tid; v < hi; v += kArThreads) {
-        const float tv = Tr[v];
-        if (!prob_valid(tv)) { bad = 1; continue; }
-        const uint64_t ft = fix40(tv);
-        am = max(am, argmax_key(tv, (uint32_t)v));
-        if (Dr) {
-          const float dv = Dr[v];
-          if (!prob_valid(dv)) { bad = 1; continue; }
-          const uint64_t fd = fix40(dv);
-          zr += ft > fd ? ft - fd : 0;
+      const bool res = j < K;
+      const __amdgpu_buffer_rsrc_t rT = row_rsrc(Tb + (size_t)j * V, V);
+      const __amdgpu_buffer_rsrc_t rD = res ? row_rsrc(Db + (size_t)j * V, V) : rT;
+      for (int base = lo; base < hi; base += kArPass) {
+        float tv[kArSeg], dv[kArSeg];
+#pragma unroll
+        for (int q = 0; q < kArSeg; ++q) {
+          const int v = base + tid + q * kArThreads;
+          tv[q] = row_at(rT, v, v < hi);
+          dv[q] = res ? row_at(rD, v, v < hi) : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kArSeg; ++q) {
+          const int v = base + tid + q * kArThreads;
+          if (v >= hi) continue;
+          if (!prob_valid(tv[q]) || (res && !prob_valid(dv[q]))) {
+            bad = 1;
+            continue;
+          }
+          const uint64_t ft = fix40(tv[q]);
+          am = max(am, argmax_key(tv[q], (uint32_t)v));
           zt += ft;
-        } else {
-          zr += ft;
+          if (res) {
+            const uint64_t fd = fix40(dv[q]);
+            zr += ft > fd ? ft - fd : 0;
+          }
         }
       }
+      if (!res) zr = zt;  // the bonus row samples from T_K itself
     }
-    zr = block_sum_u64(zr, s_red);
-    zt = block_sum_u64(zt, s_red);
-    am = block_max_u64(am, s_red);
-    bad = block_max_u64(bad, s_red);
+    block_sum2_max_or(zr, zt, am, bad, s_red);
     if (tid == 0) {
-      p[0] = zr; p[1] = zt; p[2] = am; p[3] = bad;
+      p[0] = zr; p[1] = zt; p[2] = am; p[3] = decision_word(bad, s_err, j, s_u);
     }
   } else {
     // per-row argmax keys of this chunk, rows 0..K, and an invalid-value flag
     uint64_t bad = 0;
     for (int i = 0; i <= K; ++i) {
-      const float* Tr = Tb + (size_t)i * V;
+      const __amdgpu_buffer_rsrc_t rT = row_rsrc(Tb + (size_t)i * V, V);
       uint64_t am = 0;
-      for (int v = lo + tid; v < hi; v += kArThreads) {
-        const float tv = Tr[v];
-        if (!prob_valid(tv)) { bad = 1; continue; }
-        am = max(am, argmax_key(tv, (uint32_t)v));
+      for (int base = lo; base < hi; base += kArPass) {
+        float tv[kArSeg];
+#pragma unroll
+        for (int q = 0; q < kArSeg; ++q) {
+          const int v = base + tid + q * kArThreads;
+          tv[q] = row_at(rT, v, v < hi);
+        }
+#pragma unroll
+        for (int q = 0; q < kArSeg; ++q) {
+          const int v = base + tid + q * kArThreads;
+          if (v >= hi) continue;
+          if (!prob_valid(tv[q])) {
+            bad = 1;
+            continue;
+          }
+          am = max(am, argmax_key(tv[q], (uint32_t)v));
+        }
       }
       am = block_max_u64(am, s_red);
       if (tid == 0) p[i] = am;
     }
     bad = block_max_u64(bad, s_red);
-    if (tid == 0) p[K + 1] = bad;
+    if (tid == 0) p[K + 1] = decision_word(bad, s_err, K, 0);
   }
 }
 
 __global__ __launch_bounds__(kArThreads) void ar_finish_kernel(ArArgs a) {
-  __shared__ int32_t s_j, s_err, s_tok, s_c;
-  __shared__ uint64_t s_red[4], s_before;
+  __shared__ int32_t s_tok, s_c, s_found;
+  __shared__ uint64_t s_red[16], s_before, s_total;
   __shared__ int32_t s_am[64];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int K = a.K, V = a.V, C = a.n_chunks;
-  const uint64_t P = seq_pos(a, b);
   const float* Tb = a.T + (size_t)b * (K + 1) * V;
   const float* Db = a.D ? a.D + (size_t)b * K * V : nullptr;
   const int32_t* db = a.d + (size_t)b * K;
   const int W = ar_ws_words(K);
   const uint64_t* ws_b = a.ws + (size_t)b * C * W;
   int32_t* ob = a.out + (size_t)b * (K + 1);
-  decide_first_reject(a, b, P, &s_j, &s_err);
-  const int j = s_j;
 
   if (a.greedy) {
     uint64_t badv = 0;
     for (int cc = tid; cc < C; cc += kArThreads) badv |= ws_b[(size_t)cc * W + K + 1];
-    const bool bad = block_max_u64(badv, s_red) != 0;
+    badv = block_max_u64(badv, s_red);  // every chunk's word has the same bits 1..
+    const bool bad = (badv & 3) != 0;
     for (int i = 0; i <= K; ++i) {
       uint64_t acc = 0;
       for (int cc = tid; cc < C; cc += kArThreads) acc = max(acc, ws_b[(size_t)cc * W + i]);
@@ -180,7 +271,7 @@ __global__ __launch_bounds__(kArThreads) void ar_finish_kernel(ArArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      const bool err = s_err || bad;
+      const bool err = bad;
       int n = K;
       if (!err) {
         for (int i = 0; i < K; ++i) {
@@ -194,33 +285,37 @@ __global__ __launch_bounds__(kArThreads) void ar_finish_kernel(ArArgs a) {
   }
 
   // sampling: fold the chunk partials (integer sums / maxima: order-free)
-  uint64_t zr = 0, zt = 0, am = 0, bad = 0;
-  for (int cc = tid; cc < C; cc += kArThreads) {
-    const uint64_t* p = ws_b + (size_t)cc * W;
-    zr += p[0];
-    zt += p[1];
-    am = max(am, p[2]);
-    bad |= p[3];
+  // thread tid owns chunks 2 tid and 2 tid + 1 (C <= kArMaxChunks): their
+  // partials serve both the fold and the needle's chunk search below
+  const int c0 = 2 * tid, c1 = 2 * tid + 1;
+  uint64_t q0[4] = {0, 0, 0, 0}, q1[4] = {0, 0, 0, 0};
+  if (c0 < C) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) q0[w] = ws_b[(size_t)c0 * W + w];
   }
-  zr = block_sum_u64(zr, s_red);
-  zt = block_sum_u64(zt, s_red);
-  am = block_max_u64(am, s_red);
-  bad = block_max_u64(bad, s_red);
-  if (bad || s_err) {
+  if (c1 < C) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) q1[w] = ws_b[(size_t)c1 * W + w];
+  }
+  uint64_t zr = q0[0] + q1[0], zt = q0[1] + q1[1], am = max(q0[2], q1[2]), word = q0[3] | q1[3];
+  block_sum2_max_or(zr, zt, am, word, s_red);
+  const int j = __builtin_amdgcn_readfirstlane((int)((word >> 8) & 0xFF));
+  const uint32_t u = (uint32_t)(word >> 32);
+  if (word & 3) {
     if (tid <= K) ob[tid] = -1;
     if (tid == 0 && a.n_acc) a.n_acc[b] = -1;
     return;
   }
   // weights to sample: residual (or bonus row), else fix(T_j), else the argmax
-  const int use = zr > 0 ? 0 : ((j < K && zt > 0) ? 1 : 2);
-  if (tid == 0) s_tok = (int32_t)argmax_key_index(am);
+  const int use = __builtin_amdgcn_readfirstlane(zr > 0 ? 0 : ((j < K && zt > 0) ? 1 : 2));
+  if (tid == 0) {
+    s_tok = (int32_t)argmax_key_index(am);
+    s_found = 0;
+  }
   if (use < 2) {
-    const uint32_t u = uniform_u24(a.seed, P + j, b, a.stream_id, a.word);
     const uint64_t t = icdf_needle(u, use == 0 ? zr : zt);
-    // chunk holding the needle: thread owns chunks 2*tid and 2*tid + 1
-    const int c0 = 2 * tid, c1 = 2 * tid + 1;
-    const uint64_t z0 = c0 < C ? ws_b[(size_t)c0 * W + use] : 0;
-    const uint64_t z1 = c1 < C ? ws_b[(size_t)c1 * W + use] : 0;
+    // chunk holding the needle
+    const uint64_t z0 = q0[use], z1 = q1[use];
     const uint64_t ex = block_exclusive_scan_u64_256(z0 + z1, s_red);
     if (ex <= t && t < ex + z0) {
       s_c = c0;
@@ -230,25 +325,48 @@ __global__ __launch_bounds__(kArThreads) void ar_finish_kernel(ArArgs a) {
       s_before = ex + z0;
     }
     __syncthreads();
-    const int cs = s_c;
-    const uint64_t before = s_before;
-    // rescan chunk cs: one contiguous segment per thread, block prefix sum
+    const int cs = __builtin_amdgcn_readfirstlane(s_c);
+    uint64_t before = s_before;
+    // rescan chunk cs in passes: thread tid owns the contiguous segment
+    // [base + kArSeg tid, + kArSeg) of a pass, loaded whole into registers;
+    // a block prefix sum over the segments locates the needle's segment and
+    // its thread finds the token among its registers
     const int clo = cs * a.chunk, chi = min(V, clo + a.chunk);
-    const int per = (chi - clo + kArThreads - 1) / kArThreads;
-    const int slo = clo + tid * per, shi = min(chi, slo + per);
-    const float* Tr = Tb + (size_t)j * V;
-    const float* Dr = (j < K && use == 0) ? Db + (size_t)j * V : nullptr;
-    uint64_t seg = 0;
-    for (int v = slo; v < shi; ++v) seg += row_weight(Tr, Dr, v);
-    uint64_t run = before + block_exclusive_scan_u64_256(seg, s_red);
-    if (run <= t && t < run + seg) {
-      for (int v = slo; v < shi; ++v) {
-        run += row_weight(Tr, Dr, v);
-        if (run > t) {
-          s_tok = v;
-          break;
+    const bool res = j < K && use == 0;
+    const __amdgpu_buffer_rsrc_t rT = row_rsrc(Tb + (size_t)j * V, V);
+    const __amdgpu_buffer_rsrc_t rD = res ? row_rsrc(Db + (size_t)j * V, V) : rT;
+    for (int base = clo; base < chi; base += kArPass) {  // uniform
+      const int v0 = base + kArSeg * tid;
+      float tv[kArSeg], dv[kArSeg];
+#pragma unroll
+      for (int q = 0; q < kArSeg; ++q) {
+        tv[q] = row_at(rT, v0 + q, v0 + q < chi);
+        dv[q] = res ? row_at(rD, v0 + q, v0 + q < chi) : 0.0f;
+      }
+      uint64_t w[kArSeg], seg = 0;
+#pragma unroll
+      for (int q = 0; q < kArSeg; ++q) {
+        w[q] = v0 + q < chi ? token_weight(tv[q], dv[q], res) : 0;
+        seg += w[q];
+      }
+      const uint64_t run0 = before + block_exclusive_scan_u64_256(seg, s_red);
+      if (run0 <= t && t < run0 + seg) {
+        uint64_t run = run0;
+#pragma unroll
+        for (int q = 0; q < kArSeg; ++q) {
+          run += w[q];
+          if (run > t) {
+            s_tok = v0 + q;
+            s_found = 1;
+            break;
+          }
         }
       }
+      if (tid == kArThreads - 1) s_total = run0 - before + seg;
+      __syncthreads();
+      if (s_found) break;
+      before += s_total;
+      __syncthreads();
     }
   }
   __syncthreads();
