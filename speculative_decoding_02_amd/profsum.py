@@ -19,6 +19,14 @@ short text summaries:
       factor that makes the same counter read the known size of a plain copy
       kernel (N bytes read and N bytes written per launch).
 
+  counters DIR [DIR ...] [--kernels "SUB1;SUB2;..."] [--cus N] [--ses N]
+      L1 / address-unit / SQ counters of several `rocprofv3 --pmc` passes,
+      averaged per launch for every kernel instance (or those matching the
+      substrings) over the steady state, with the derived shares: kernel
+      cycles (SQ_CYCLES over the shader engines), mean L2 read latency
+      (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ), and per-CU busy or stall
+      cycles (TCP_*, TA_* over the CUs) as a share of the kernel's cycles.
+
 Usage:  python -m speculative_decoding_02_amd.profsum trace prof/kt
 """
 from __future__ import annotations
@@ -194,6 +202,57 @@ def pmc_summary(dfetch: str, dwrite: str, kernel: str, copy_kernel: str, copy_by
     return "\n".join(lines)
 
 
+def counters_summary(dirs, kernels, cus: int, ses: int) -> str:
+    """Per kernel instance: counter averages per launch over the steady state
+    of each pass, merged across passes, and the derived shares."""
+    per = collections.defaultdict(dict)   # kernel -> counter -> mean per launch
+    launches = collections.defaultdict(dict)
+    for d in dirs:
+        cnt = load_counters(d)
+        ids = sorted(cnt)
+        marks = [k for k in ids if ROUND_MARK in cnt[k][0]]
+        first = marks[0] if marks else -1
+        acc = collections.defaultdict(lambda: collections.defaultdict(list))
+        for k in ids:
+            if k <= first:
+                continue
+            name, vals = cnt[k]
+            if kernels and not any(sub in name for sub in kernels):
+                continue
+            for c, v in vals.items():
+                acc[name][c].append(v)
+        for name, cs in acc.items():
+            for c, v in cs.items():
+                per[name][c] = sum(v) / len(v)
+                launches[name][c] = len(v)
+    lines = []
+    for name in sorted(per):
+        c = per[name]
+        lines.append(short(name, 90))
+        cyc = c.get("SQ_CYCLES", 0.0) / ses if "SQ_CYCLES" in c else None
+        if cyc:
+            lines.append(f"  kernel cycles (SQ_CYCLES / {ses} SE): {cyc / 1e3:.1f} k")
+        if "TCP_TCC_READ_REQ" in c and "TCP_TCC_READ_REQ_LATENCY" in c and c["TCP_TCC_READ_REQ"]:
+            lines.append(f"  L1->L2 read requests: {c['TCP_TCC_READ_REQ'] / 1e6:.2f} M, mean L2 read "
+                         f"latency {c['TCP_TCC_READ_REQ_LATENCY'] / c['TCP_TCC_READ_REQ']:.0f} cycles")
+        for cname, label in (("TCP_PENDING_STALL_CYCLES", "L1 stalled on pending misses"),
+                             ("TCP_UTCL1_STALL_INFLIGHT_MAX", "L1 TLB stalled at max in flight"),
+                             ("TA_TA_BUSY", "address unit busy"),
+                             ("TA_ADDR_STALLED_BY_TC_CYCLES", "address unit stalled by the cache"),
+                             ("TA_DATA_STALLED_BY_TC_CYCLES", "address unit data stalled by the cache")):
+            if cname in c and cyc:
+                lines.append(f"  {label}: {100 * c[cname] / cus / cyc:.0f}% of the kernel's cycles")
+        if "TCP_UTCL1_TRANSLATION_MISS" in c:
+            lines.append(f"  TLB misses / hits: {c['TCP_UTCL1_TRANSLATION_MISS']:.0f} / "
+                         f"{c.get('TCP_UTCL1_TRANSLATION_HIT', 0.0) / 1e6:.2f} M")
+        if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"]:
+            lines.append(f"  wave time in s_waitcnt: {100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.0f}%")
+        n = max(launches[name].values())
+        lines.append(f"  ({n} launches; raw means: " +
+                     ", ".join(f"{k} {v:.4g}" for k, v in sorted(c.items())) + ")")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -209,9 +268,17 @@ def main(argv=None):
     p.add_argument("--kernel", required=True)
     p.add_argument("--copy-kernel", required=True)
     p.add_argument("--copy-bytes", type=int, required=True)
+    q = sub.add_parser("counters")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--kernels", default="")
+    q.add_argument("--cus", type=int, default=256)
+    q.add_argument("--ses", type=int, default=32)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last, a.kernel_window))
+    elif a.cmd == "counters":
+        ks = [k for k in a.kernels.split(";") if k]
+        print(counters_summary(a.dirs, ks, a.cus, a.ses))
     else:
         print(pmc_summary(a.fetch_dir, a.write_dir, a.kernel, a.copy_kernel, a.copy_bytes))
 
