@@ -414,7 +414,7 @@ def main():
                                          "tokens_per_round")}))
 
     if not args.no_cpu_baseline and args.drafter == "model":
-        res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr)
+        res["cpu_baseline"] = cpu_baseline(tcfg, dcfg, tw, dw, K, args, tpr, plen)
     sd.spec_destroy(ctx)
     print(json.dumps(res), flush=True)
 
@@ -708,7 +708,7 @@ def adaptive_k_run(sd, torch, ctx, stream, d, D, out, nacc, seed, args, tcfg, dc
     }
 
 
-def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
+def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round, plen):
     """The oracle (plain C, fp64 forward over the bf16 weights widened exactly,
     fp32 probability rows, OpenMP over output features) on the host cores,
     on bounded samples of the same workload:
@@ -717,8 +717,12 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
         attention over 8 instead of ~1000 keys is ~4% of the oracle's per-row
         work, so this bounds the sample without changing what a round
         computes;
-      * one (K+1)-row verify pass of the target after that prompt, with GB/s
-        on the same algorithmic-bytes model as the GPU's verify pass;
+      * one (K+1)-row verify pass of the target at the GPU run's context
+        length (the prompt's length minus the pending token): the oracle's
+        cache starts zero-filled, so the positions before the pass hold zero
+        keys and values -- the same attention arithmetic as a prefilled
+        cache, without an fp64 prefill of ~1000 tokens -- with GB/s on the
+        same algorithmic-bytes model as the GPU's verify pass;
       * the rule alone on one 64 x 8 x 32000 batch (draft noise 0.5), GB/s on
         the same model as the GPU's --ar-bench."""
     import numpy as np
@@ -742,16 +746,16 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
     t_rounds = max(t_all - t_pre, 1e-9)
     rounds = st["rounds"]
     val = rounds * gpu_tokens_per_round / t_rounds
-    # one verify pass: K+1 rows after the 8-token prompt, logits and rows
-    kv = oracle.KV(T, 64)
-    ctx = [int(x) for x in prompt]
-    oracle.forward(T, kv, ctx[:-1], 0, want_logits=False)
-    rows = [ctx[-1]] + [int(x) for x in synth.prompt(tcfg.vocab, K, seed=8)]
+    # one verify pass: K+1 rows at the GPU run's context length, logits and rows
+    n_ctx = max(plen - 1, 0)
+    kv = oracle.KV(T, n_ctx + K + 2)
+    rows = [int(x) for x in synth.prompt(tcfg.vocab, K + 1, seed=8)]
     t0 = time.perf_counter()
-    lg = oracle.forward(T, kv, rows, len(ctx) - 1)
+    lg = oracle.forward(T, kv, rows, n_ctx)
     _ = [oracle.softmax_f32(r) for r in lg]
     t_verify = time.perf_counter() - t0
-    vbytes = verify_pass_bytes(tcfg, K, len(ctx) - 1)
+    del kv
+    vbytes = verify_pass_bytes(tcfg, K, n_ctx)
     # the rule alone on the isolated-rule workload
     Bq, Kq, Vq = 64, 8, 32000
     Tq, Dq = synth.logit_pair(Bq, Kq, Vq, 0.5)
@@ -769,7 +773,7 @@ def cpu_baseline(tcfg, dcfg, tw, dw, K, args, gpu_tokens_per_round):
                       f"({t_pre:.1f}s); tokens/round taken from the GPU run "
                       f"({gpu_tokens_per_round:.3f}); oracle's own rounds emitted {st['emitted']}",
             "seconds": round(t_rounds, 3),
-            "verify_pass": {"ms": round(t_verify * 1e3, 1), "context_tokens": len(ctx) - 1,
+            "verify_pass": {"ms": round(t_verify * 1e3, 1), "context_tokens": n_ctx,
                             "algorithmic_GB": round(vbytes / 1e9, 4),
                             "GB_s": round(vbytes / t_verify / 1e9, 3)},
             "accept_reject": {"workload": f"B={Bq}, K={Kq}, V={Vq}, sigma=0.5, sampling",

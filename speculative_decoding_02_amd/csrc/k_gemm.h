@@ -62,8 +62,9 @@ struct GemmArgs {
 };
 
 struct GemmShape {
-  int nb;      // 16-column blocks per workgroup
-  int waves;   // waves per workgroup, splitting K
+  int nb;        // 16-column blocks per workgroup
+  int waves;     // waves per workgroup, splitting K
+  int half = 0;  // nb == 1 only: two workgroups per block, 8 columns each
 };
 hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
 // Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
@@ -75,10 +76,12 @@ hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_grou
                        hipStream_t s);
 
 // ------------------------------------------------------------ GEMM plans --
-// One workgroup per group of `nb` 16-column blocks, `waves` waves splitting K.
+// One workgroup per group of `nb` 16-column blocks (or per half block),
+// `waves` waves splitting K.
 struct GemmPlan {
   GemmShape shape{1, 4};
   int n_groups = 0, Kb = 0;
+  int workgroups() const { return n_groups * (shape.half ? 2 : 1); }
 };
 
 // Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4,7} and
@@ -94,7 +97,14 @@ struct GemmPlan {
 // workgroup once that still leaves >= 192 workgroups, four waves, except
 // for narrow matrices with a long K, where only eight waves per workgroup
 // keep enough loads in flight.
-inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu) {
+//
+// A matrix with at most n_cu / 2 column blocks would leave half the CUs
+// idle, and one CU streams at most ~35 GB/s: with allow_half each block is
+// split between two workgroups of 8 columns (each lane of a wave loads only
+// the B-fragment slots of its own half, the others read as zero without a
+// fetch), so every CU gets a share.  Not for epilogues that pair columns
+// across the halves of a block (RoPE pairs w, w^8; gate/up pairs).
+inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_half = false) {
   GemmPlan p;
   const int n_blocks = n_cols / 16;
   p.Kb = K / 32;
@@ -108,6 +118,7 @@ inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu) {
   p.shape.nb = std::max(nb_min, (n_blocks >= 384 && n_blocks % 2 == 0) ? 2 : 1);
   p.n_groups = n_blocks / p.shape.nb;
   p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
+  if (allow_half && p.shape.nb == 1 && n_cu > 0 && 2 * n_blocks <= n_cu) p.shape.half = 1;
   return p;
 }
 

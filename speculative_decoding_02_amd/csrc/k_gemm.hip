@@ -39,9 +39,12 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int NB, int W, int EPI>
+// HALF (NB == 1): workgroup 2b + h owns columns 8h .. 8h + 7 of block b.
+template <int NB, int W, int EPI, bool HALF>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
-  constexpr int YW = NB * 16;            // columns owned by the workgroup
+  static_assert(!HALF || (NB == 1 && EPI != EPI_SILU && EPI != EPI_QKV),
+                "half blocks split column pairs of the SiLU and RoPE epilogues");
+  constexpr int YW = HALF ? 8 : NB * 16;  // columns owned by the workgroup
   constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : (NB <= 4 ? 4 : 2));  // k-blocks per batch
   __shared__ float s_red[W * NB * 256];
   __shared__ float s_y[kMaxRows * YW];
@@ -51,7 +54,9 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int g = blockIdx.x;
+  const int g = blockIdx.x;                 // workgroup: stamps and partial outputs
+  const int gb = HALF ? g >> 1 : g;         // column group of the packed weights
+  const int hc = HALF ? (g & 1) * 8 : 0;    // first column of the half within its block
   int n_rows = a.rows->n_rows;
   int row_base = 0;
   if (a.last_row_only) {
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
 
   // Epilogue operands that do not depend on the product, fetched now so their
   // latency hides behind the weight stream.
-  const int col0 = g * YW;
+  const int col0 = gb * NB * 16 + hc;
   constexpr int C8 = YW / 8;
   float4 pre_x0 = make_float4(0.f, 0.f, 0.f, 0.f), pre_x1 = pre_x0;
   uint4 pre_g = make_uint4(0, 0, 0, 0);
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   if constexpr (EPI == EPI_QKV) {
     const int m = tid / YW, c = tid % YW;
     const int pos = a.rows->pos0 + m;
-    const int b = g * NB + c / 16, w = c % 16;
+    const int b = gb * NB + c / 16, w = c % 16;
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16, half_hd = a.head_dim / 2;
     if (m < kMaxRows && pos < a.max_seq) {
       pre_blk = a.block_table[pos / kBlock];
@@ -122,7 +127,13 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Ap), 0, a.Kb * 1024, 0x00020000);
   const uint32_t a_off = aload ? (uint32_t)lane * 16 : 0x80000000u;
-  const uint4* wp = (const uint4*)a.Wp + (size_t)g * a.Kb * NB * 64 + lane;
+  const uint4* wp = (const uint4*)a.Wp + (size_t)gb * a.Kb * NB * 64 + lane;
+  // Half blocks: lanes of the other half's columns read at an out-of-range
+  // offset of a buffer resource over the group's weights (zero, no fetch);
+  // aux bit 1 is the non-temporal hint.
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(wp - lane), 0, HALF ? a.Kb * NB * 1024 : 0, 0x00020000);
+  const uint32_t w_off = (unsigned)((lane & 15) - hc) < 8u ? (uint32_t)lane * 16 : 0x80000000u;
   floatx4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -141,7 +152,16 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < UB; ++u)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (HALF) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+              rW, (int)(w_off < 0x80000000u ? w_off + (uint32_t)((kb + u) * NB + j) * 1024 : w_off), 0,
+              2);
+          wv[u][j] = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+          wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
+        }
+      }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
@@ -190,7 +210,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     const int mm = 4 * (ln >> 4) + r;  // MFMA row = activation row
     // with last_row_only the one used row (row_base) becomes output row 0
     const int m = a.last_row_only ? (mm == row_base ? 0 : -1) : mm;
-    if (m >= 0) s_y[m * YW + j * 16 + (ln & 15)] = v * s_scale[m];
+    const int cy = j * 16 + (ln & 15) - hc;  // column within the workgroup's share
+    if (m >= 0 && (!HALF || (unsigned)cy < 8u)) s_y[m * YW + cy] = v * s_scale[m];
   }
   __syncthreads();
 
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
       a.ssq_out[g * kMaxRows + tid] = s;
     }
   } else if constexpr (EPI == EPI_SILU) {
-    // block b = g*NB + j: columns 0-7 are the gate and 8-15 the up outputs of
+    // block b = gb*NB + j: columns 0-7 are the gate and 8-15 the up outputs of
     // features 8b .. 8b+7
     for (int idx = tid; idx < n_rows * NB; idx += W * 64) {
       const int m = idx / NB, j = idx % NB;
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
         const float up = s_y[m * YW + j * 16 + 8 + e];
         v[e] = gt / (1.0f + expf(-gt)) * up;
       }
-      apack_store8(a.Ap_out, m, (g * NB + j) * 8, v);
+      apack_store8(a.Ap_out, m, (gb * NB + j) * 8, v);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
     const int pos0 = a.rows->pos0;
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
-      const int b = g * NB + c / 16, w = c % 16;
+      const int b = gb * NB + c / 16, w = c % 16;
       const int pos = pos0 + m;
       if (pos >= a.max_seq) continue;
       const float mine = s_y[m * YW + c];
@@ -318,21 +339,36 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   }
 }
 
-template <int NB, int W>
+template <int NB, int W, bool HALF = false>
 static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_groups), block(W * 64);
-  switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE>), grid, block, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID>), grid, block, 0, s, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV>), grid, block, 0, s, a); break;
-    case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS>), grid, block, 0, s, a); break;
-    case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  const dim3 grid(a.n_groups * (HALF ? 2 : 1)), block(W * 64);
+  if constexpr (HALF) {
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true>), grid, block, 0, s, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true>), grid, block, 0, s, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false>), grid, block, 0, s, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false>), grid, block, 0, s, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false>), grid, block, 0, s, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false>), grid, block, 0, s, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) {
+  if (sh.half) {
+    if (sh.nb != 1) return hipErrorInvalidValue;
+    if (sh.waves == 4) return launch_epi<1, 4, true>(epi, a, s);
+    if (sh.waves == 8) return launch_epi<1, 8, true>(epi, a, s);
+    return hipErrorInvalidValue;
+  }
   if (sh.waves == 4) {
     if (sh.nb == 1) return launch_epi<1, 4>(epi, a, s);
     if (sh.nb == 2) return launch_epi<2, 4>(epi, a, s);

@@ -232,17 +232,18 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   const int L = m.L, d = m.d;
   int n_cu = 0;
   HIPTRY(c, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
-  auto mk = [n_cu](int N, int K) {
+  // half blocks only where the epilogue keeps each column on its own (O, down)
+  auto mk = [n_cu](int N, int K, bool allow_half) {
     Mat x;
     x.N = N; x.K = K;
-    x.plan = plan_gemm(N, 1, K, n_cu);
+    x.plan = plan_gemm(N, 1, K, n_cu, allow_half);
     return x;
   };
-  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, d));
-  m.o.assign(L, mk(d, m.qd));
-  m.gu.assign(L, mk(2 * m.F, d));
-  m.dn.assign(L, mk(d, m.F));
-  m.lm = mk(m.V, d);
+  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, d, false));
+  m.o.assign(L, mk(d, m.qd, true));
+  m.gu.assign(L, mk(2 * m.F, d, false));
+  m.dn.assign(L, mk(d, m.F, true));
+  m.lm = mk(m.V, d, false);
   m.lm_shared = share_from && share_desc && md.lm_head == share_desc->lm_head &&
                 md.d_model == share_desc->d_model && md.vocab == share_desc->vocab;
   m.embed_shared = share_from && share_desc && md.embed == share_desc->embed &&
@@ -408,7 +409,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     e = launch_gemm(m.o[l].plan.shape, EPI_RESID, b, s);
     if (e != hipSuccess) break;
     std::swap(ssq_in, ssq_other);
-    ssq_groups = m.o[l].plan.n_groups;
+    ssq_groups = m.o[l].plan.workgroups();
     // RMSNorm + gate/up + SiLU*mul -> packed A of the down projection
     GemmArgs g = gemm_base(c, m.gu[l], c->ap_x);
     g.ssq = ssq_in; g.ssq_groups = ssq_groups; g.eps = m.eps; g.Ap_out = c->ap_a;
@@ -422,14 +423,14 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     if (stamp_last_down && l == m.L - 1) dn.ts_end = c->ts_head;
     e = launch_gemm(m.dn[l].plan.shape, EPI_RESID, dn, s);
     std::swap(ssq_in, ssq_other);
-    ssq_groups = m.dn[l].plan.n_groups;
+    ssq_groups = m.dn[l].plan.workgroups();
   }
   return e;
 }
 
 // Sums of squares left by the last layer's down projection (each layer ends
 // with them back in ssq_a) for the final RMSNorm.
-int final_ssq_groups(const Model& m) { return m.dn[m.L - 1].plan.n_groups; }
+int final_ssq_groups(const Model& m) { return m.dn[m.L - 1].plan.workgroups(); }
 float* final_ssq(spec_ctx* c, const Model&) { return c->ssq_a; }
 
 // final norm + LM head (+ logits partials) + softmax into `dst`
@@ -443,7 +444,7 @@ hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row
   hipError_t e = launch_gemm(m.lm.plan.shape, EPI_LOGITS, a, s);
   if (e != hipSuccess) return e;
   SoftmaxArgs sm{};
-  sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.n_groups; sm.V = m.V;
+  sm.logits = logits_dst; sm.part = c->lm_part; sm.G = m.lm.plan.workgroups(); sm.V = m.V;
   sm.rows = c->rows; sm.last_row_only = last_row_only; sm.out = dst; sm.chunk = c->sm_chunk;
   return launch_softmax(sm, c->sm_nchunks, last_row_only ? 1 : n_rows, s);
 }
@@ -525,7 +526,7 @@ hipError_t enqueue_heads_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed,
   e = launch_gemm(m.lm.plan.shape, EPI_LOGITS, lm, s);
   if (e != hipSuccess) return e;
   SoftmaxArgs sm{};
-  sm.logits = c->logits; sm.part = c->lm_part; sm.G = m.lm.plan.n_groups; sm.V = m.V;
+  sm.logits = c->logits; sm.part = c->lm_part; sm.G = m.lm.plan.workgroups(); sm.V = m.V;
   sm.rows = c->rows; sm.last_row_only = 0; sm.out = Dp; sm.chunk = c->sm_chunk;
   e = launch_softmax(sm, c->sm_nchunks, K, s);
   for (int k = 0; k < K && e == hipSuccess; ++k) {
@@ -680,16 +681,16 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
     dmax = std::max(dmax, m->d);
     qmax = std::max(qmax, m->qd);
     fmax = std::max(fmax, m->F);
-    lm_groups = std::max(lm_groups, m->lm.plan.n_groups);
+    lm_groups = std::max(lm_groups, m->lm.plan.workgroups());
     ssq_groups = std::max(ssq_groups, m->d / 64);
     for (int l = 0; l < m->L; ++l)
-      ssq_groups = std::max({ssq_groups, m->o[l].plan.n_groups, m->dn[l].plan.n_groups});
+      ssq_groups = std::max({ssq_groups, m->o[l].plan.workgroups(), m->dn[l].plan.workgroups()});
     // every RMSNorm consumer must be able to fold its producer's partials
     auto cap = [](const Mat& x) { return x.plan.shape.waves * 64 / kMaxRows * kGemmMaxSsqPerThread; };
-    bool ok = m->d / 64 <= cap(m->qkv[0]) && m->dn[m->L - 1].plan.n_groups <= cap(m->lm);
+    bool ok = m->d / 64 <= cap(m->qkv[0]) && m->dn[m->L - 1].plan.workgroups() <= cap(m->lm);
     for (int l = 0; l < m->L; ++l) {
-      ok = ok && m->o[l].plan.n_groups <= cap(m->gu[l]);
-      if (l > 0) ok = ok && m->dn[l - 1].plan.n_groups <= cap(m->qkv[l]);
+      ok = ok && m->o[l].plan.workgroups() <= cap(m->gu[l]);
+      if (l > 0) ok = ok && m->dn[l - 1].plan.workgroups() <= cap(m->qkv[l]);
     }
     if (!ok) return bail(fail(c, SPEC_ERR_ARG, "d_model too large for the RMSNorm partial fold"));
     const int qg = (m->nq / m->nkv) * kMaxRows;
@@ -726,9 +727,9 @@ int spec_init(const spec_init_params* p, const int32_t* prompt_host, int32_t n_p
   c->ts_cap = p->k_max * c->D.L + c->T.L;
   for (const Model* m : ms)
     for (int l = 0; l < m->L; ++l)
-      c->ts_groups = std::max({c->ts_groups, m->o[l].plan.n_groups, m->gu[l].plan.n_groups});
+      c->ts_groups = std::max({c->ts_groups, m->o[l].plan.workgroups(), m->gu[l].plan.workgroups()});
   TRYH(dalloc(&c->ts, (size_t)c->ts_cap * 2 * c->ts_groups));
-  c->ts_head_groups = std::max(c->T.lm.plan.n_groups, c->T.dn[c->T.L - 1].plan.n_groups);
+  c->ts_head_groups = std::max(c->T.lm.plan.workgroups(), c->T.dn[c->T.L - 1].plan.workgroups());
   TRYH(dalloc(&c->ts_head, (size_t)2 * c->ts_head_groups));
   TRYH(hipDeviceGetAttribute(&c->wall_khz, hipDeviceAttributeWallClockRate, c->device));
   if (c->wall_khz <= 0) return bail(fail(c, SPEC_ERR_HIP, "device reports no wall-clock rate"));
@@ -1001,8 +1002,8 @@ int spec_kernel_times(spec_ctx* c, float* ms_out, int32_t cap, int32_t* n_out) {
       const unsigned long long* g = o + c->ts_groups;
       unsigned long long o_end = 0, g_end = 0;
       bool ok = true;
-      for (int w = 0; w < m.o[l].plan.n_groups; ++w) { ok = ok && o[w] != 0; o_end = std::max(o_end, o[w]); }
-      for (int w = 0; w < m.gu[l].plan.n_groups; ++w) { ok = ok && g[w] != 0; g_end = std::max(g_end, g[w]); }
+      for (int w = 0; w < m.o[l].plan.workgroups(); ++w) { ok = ok && o[w] != 0; o_end = std::max(o_end, o[w]); }
+      for (int w = 0; w < m.gu[l].plan.workgroups(); ++w) { ok = ok && g[w] != 0; g_end = std::max(g_end, g[w]); }
       const float ms = ok && g_end > o_end ? (float)((double)(g_end - o_end) / c->wall_khz) : -1.0f;
       if (n < cap) ms_out[n] = ms;
       ++n;
@@ -1025,8 +1026,8 @@ int spec_head_time(spec_ctx* c, float* ms_out) {
   const Model& m = c->T;
   unsigned long long d_end = 0, l_end = 0;
   bool ok = true;
-  for (int w = 0; w < m.dn[m.L - 1].plan.n_groups; ++w) { ok = ok && h[w] != 0; d_end = std::max(d_end, h[w]); }
-  for (int w = 0; w < m.lm.plan.n_groups; ++w) {
+  for (int w = 0; w < m.dn[m.L - 1].plan.workgroups(); ++w) { ok = ok && h[w] != 0; d_end = std::max(d_end, h[w]); }
+  for (int w = 0; w < m.lm.plan.workgroups(); ++w) {
     const unsigned long long t = h[(size_t)c->ts_head_groups + w];
     ok = ok && t != 0;
     l_end = std::max(l_end, t);
