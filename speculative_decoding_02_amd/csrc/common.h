@@ -84,15 +84,20 @@ SPEC_DEVICE size_t qfrag_index(int h, int G, int n_es, int qi, int part, int dim
 
 // ------------------------------------------------- packed MFMA A operand --
 // Activations enter the skinny GEMM as the A operand of
-// v_mfma_f32_16x16x32_bf16: 16 rows x 32 k per 1 KiB block, lane l holding 8
+// v_mfma_f32_16x16x32_bf16: 16 rows x 32 k per 1 KiB block, lane l taking 8
 // bf16 of row l%16 at k = 32*kb + 8*(l/16) + 0..7.  Rows 0-7 carry the bf16
 // high part of the fp32 activation rows 0-7, rows 8-15 the bf16 low part
 // (x - hi), so products against bf16 weights keep ~16 mantissa bits.
-// Producers write this layout directly; [Kb][64 lanes][8] bf16 per matrix.
+// Within a block each row's 32 values are contiguous ([Kb][16 rows][32]
+// bf16 per matrix): a pass over n rows touches 2n 64-byte runs per block
+// (the four lanes of a row read one run), not every line of it.  Producers
+// write this layout directly.
 SPEC_DEVICE size_t apack_index(int m, int part, int k) {
-  const int kk = k & 31;
-  const int lane = (m + 8 * part) + 16 * (kk >> 3);
-  return ((size_t)(k >> 5) * 64 + lane) * 8 + (kk & 7);
+  return ((size_t)(k >> 5) * 16 + (m + 8 * part)) * 32 + (k & 31);
+}
+// Byte offset of lane l's A fragment within a k-block of that layout.
+SPEC_DEVICE uint32_t apack_lane_offset(int lane) {
+  return (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16);
 }
 
 SPEC_DEVICE uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {

@@ -316,8 +316,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = acc[1 + e] * inv;
     const int r = qi / G, gi = qi % G;
-    apack_store8_rt(a.Ap_out, seq * a.seq_rows + r, (h * G + gi) * hd + tid * 8, out,
-                    a.a_tiles > 1 ? a.a_tiles : 1);
+    if (a.a_tiles == 0)  // the single pass's GEMM layout
+      apack_store8(a.Ap_out, r, (h * G + gi) * hd + tid * 8, out);
+    else  // the rows GEMM's tiles (a batch of sequences)
+      apack_store8_rt(a.Ap_out, seq * a.seq_rows + r, (h * G + gi) * hd + tid * 8, out, a.a_tiles);
   }
 }
 

@@ -11,10 +11,11 @@
 //    wave is one B fragment of v_mfma_f32_16x16x32_bf16 and a wave's k-range
 //    is one contiguous span: [group][k-block][NB][64 lanes][8 bf16].
 //  * A arrives already packed by its producer (see apack_index): bf16 high
-//    and low halves of up to 8 fp32 rows in one 16-row MFMA tile.  It is
-//    small and shared by every workgroup, so it is read from L2; lanes of
-//    rows the pass does not use are given an out-of-range buffer offset,
-//    which reads as zero without a memory access.
+//    and low halves of up to 8 fp32 rows in one 16-row MFMA tile, each row's
+//    32 values of a k-block contiguous.  It is small and shared by every
+//    workgroup, so it is read from L2; lanes of rows the pass does not use
+//    are given an out-of-range buffer offset, which reads as zero without a
+//    memory access.
 //  * A workgroup owns NB 16-column blocks for the whole of K; its waves split
 //    K and are reduced through LDS in wave order (deterministic, and no
 //    workgroup ever waits for another).
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   // use read at an out-of-range offset, which returns zero without a fetch.
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Ap), 0, a.Kb * 1024, 0x00020000);
-  const uint32_t a_off = aload ? (uint32_t)lane * 16 : 0x80000000u;
+  const uint32_t a_off = aload ? apack_lane_offset(lane) : 0x80000000u;
   const uint4* wp = (const uint4*)a.Wp + (size_t)gb * a.Kb * NB * 64 + lane;
   // Half blocks: lanes of the other half's columns read at an out-of-range
   // offset of a buffer resource over the group's weights (zero, no fetch);

@@ -31,8 +31,9 @@ struct AttnArgs {
   // reads rows[b], block_table + b * n_blocks, the query fragments
   // qf + b * qf_bytes / 2 (qf_bytes is then one sequence's share), its own
   // workspace slice, and writes its rows as rows b * seq_rows + r of the
-  // packed output, laid out in a_tiles row tiles (rows GEMM layout; 0 or 1:
-  // the single pass's 16-row tile).
+  // packed output, laid out in a_tiles row tiles (the rows GEMM's layout,
+  // a_tiles >= 1); a_tiles = 0: a single pass, written in the skinny GEMM's
+  // layout (apack_index).
   int n_seq, seq_rows, a_tiles;
   int qt_per_wave;           // 2: one wave scores both 16-query tiles of a chunk (0 or 1: one)
 };
@@ -109,7 +110,8 @@ inline int rows_tiles(int M) {
 }
 // Packed A of the rows GEMM, [K/32][RT][64 lanes][8 bf16]: tile t holds the
 // bf16 high parts of rows 8t..8t+7 in its MFMA rows 0-7 and their low parts
-// in rows 8-15.  With RT = 1 it is the single pass's layout (apack_index).
+// in rows 8-15, lane-major within a tile (the single pass's skinny GEMM
+// keeps each row's 32 values of a k-block contiguous instead: apack_index).
 SPEC_DEVICE size_t apack_index_rt(int m, int part, int k, int RT) {
   const int kk = k & 31;
   const int lane = (m & 7) + 8 * part + 16 * (kk >> 3);
