@@ -219,8 +219,8 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 // Merge of the chunk partials of query vector qi of kv head h.  Thread
 // (chunk group cg, 8-dim group d8) takes chunks cg, cg + ncg, ... and keeps a
 // running (max, sum, value sum), rescaling by exp(m_old - m_new); the thread
-// states are then brought to the block-wide maximum and summed in cg order
-// (deterministic).
+// states are then brought to the block-wide maximum and summed over the
+// chunk groups in a fixed order (deterministic).
 constexpr int kMergeBatch = 4;
 
 struct MergeState {
@@ -299,14 +299,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __syncthreads();
   const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
   const float sc = st.m == -INFINITY ? 0.0f : expf(st.m - M);
-  float* my = s_o + tid * 9;
-  my[0] = st.l * sc;
+  float v[9];
+  v[0] = st.l * sc;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) my[1 + e] = st.o[e] * sc;
+  for (int e = 0; e < 8; ++e) v[1 + e] = st.o[e] * sc;
+  // Sum over the chunk groups, in a fixed order.  When n8 divides 64 the
+  // lanes of one 8-dim slice d8 sit n8 apart in every wave: a butterfly
+  // over those lanes, then the four waves' sums in wave order.  Otherwise
+  // (hd 168) one thread per slice adds the groups one after another.
+  const bool butterfly = 64 % n8 == 0;
+  if (butterfly) {
+    for (int off = n8; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 9; ++e) v[e] += __shfl_xor(v[e], off);
+    if (lane < n8) {
+#pragma unroll
+      for (int e = 0; e < 9; ++e) s_o[(wave * n8 + lane) * 9 + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 9; ++e) s_o[tid * 9 + e] = v[e];
+  }
   __syncthreads();
   if (tid < n8) {
     float acc[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < ncg; ++g) {
+    const int n_parts = butterfly ? 4 : ncg;  // waves, or chunk groups
+    for (int g = 0; g < n_parts; ++g) {
       const float* q = s_o + (g * n8 + tid) * 9;
 #pragma unroll
       for (int e = 0; e < 9; ++e) acc[e] += q[e];
