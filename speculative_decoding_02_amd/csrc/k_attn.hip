@@ -153,6 +153,10 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
       vf[et][p] = make_uint4(w0.x, w0.y, w1.x, w1.y);
     }
   }
+  // Every key and value load is issued before the first MFMA waits on one:
+  // left alone, the scheduler interleaves them with the score MFMAs and the
+  // wave pays several dependent memory round trips instead of one.
+  __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
   for (int q = 0; q < QTW; ++q) {
