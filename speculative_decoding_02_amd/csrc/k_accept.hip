@@ -51,7 +51,11 @@ SPEC_DEVICE void decide_first_reject(const ArArgs& a, int b, uint64_t P, int* s_
     if (sample && lane <= K) {
       const U64x4 w = philox4x64_10(P + lane, b, a.stream_id, 0, a.seed, 0);
       u_acc = (uint32_t)(w.w[1] >> 40);
-      u_fin = (uint32_t)(w.w[a.word] >> 40);
+      // a select, not w.w[a.word]: a runtime index would put the four words
+      // in per-thread LDS, whose address needs the work-group sizes read from
+      // the dispatch packet, on this path's critical chain
+      const uint64_t wf = a.word == 0 ? w.w[0] : a.word == 1 ? w.w[1] : a.word == 2 ? w.w[2] : w.w[3];
+      u_fin = (uint32_t)(wf >> 40);
     }
     bool stop = false, invalid = false;
     if (gather) {
