@@ -20,6 +20,8 @@ FLAGS = [
     "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-result",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (gfx950)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

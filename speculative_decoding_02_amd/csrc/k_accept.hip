@@ -155,7 +155,15 @@ SPEC_DEVICE float row_at(__amdgpu_buffer_rsrc_t r, int v, bool in) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)(in ? (uint32_t)v * 4 : kArOOB), 0, 0));
 }
 
-__global__ __launch_bounds__(kArThreads) void ar_partial_kernel(ArArgs a) {
+// The rule's kernels take the pointers their first loads need as leading
+// scalar arguments (preloaded in SGPRs) and use them in place of the copies
+// in the argument struct.
+__global__ __launch_bounds__(kArThreads) void ar_partial_kernel(const DevState* st,
+                                                               const uint64_t* pos, const int32_t* dd,
+                                                               const float* T, const float* D,
+                                                               ArArgs args) {
+  ArArgs a = args;
+  a.st = st; a.pos = pos; a.d = dd; a.T = T; a.D = D;
   __shared__ int32_t s_j, s_err;
   __shared__ uint32_t s_u;
   __shared__ uint64_t s_red[16];
@@ -248,7 +256,11 @@ __global__ __launch_bounds__(kArThreads) void ar_partial_kernel(ArArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kArThreads) void ar_finish_kernel(ArArgs a) {
+__global__ __launch_bounds__(kArThreads) void ar_finish_kernel(const uint64_t* ws, const int32_t* dd,
+                                                              const float* T, const float* D,
+                                                              ArArgs args) {
+  ArArgs a = args;
+  a.ws = const_cast<uint64_t*>(ws); a.d = dd; a.T = T; a.D = D;
   __shared__ int32_t s_tok, s_c, s_found;
   __shared__ uint64_t s_red[16], s_before, s_total;
   __shared__ int32_t s_am[64];
@@ -398,10 +410,11 @@ hipError_t launch_accept_reject(const ArArgs& a, hipStream_t s) {
   if (a.n_chunks > kArMaxChunks || a.K > 63 || (long long)a.n_chunks * a.B > 0x7fffffffLL)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(ar_partial_kernel, dim3((unsigned)(a.n_chunks * a.B)), dim3(kArThreads), 0, s,
-                     a);
+                     a.st, a.pos, a.d, a.T, a.D, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ar_finish_kernel, dim3(a.B), dim3(kArThreads), 0, s, a);
+  hipLaunchKernelGGL(ar_finish_kernel, dim3(a.B), dim3(kArThreads), 0, s, (const uint64_t*)a.ws, a.d,
+                     a.T, a.D, a);
   return hipGetLastError();
 }
 

@@ -72,8 +72,15 @@ SPEC_DEVICE uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // QTW query tiles per wave: with QTW = 2 one wave scores both tiles of a
 // chunk from one load of its keys and values (the batched pass); with 1 the
 // tiles run as separate waves.
+// The pointers and sizes the first loads need lead the arguments as scalars
+// (preloaded in SGPRs rather than loaded from the argument segment).
 template <int NES, int QTW>
-__global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_all,
+                                                          const int32_t* block_table,
+                                                          const uint16_t* qf_all,
+                                                          const uint16_t* k_cache,
+                                                          const uint16_t* v_cache, uint32_t qf_bytes,
+                                                          uint32_t kv_layer_bytes, AttnArgs a) {
   constexpr int NET = 2 * NES;            // e-tiles of 16 covering 32*NES dims
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
@@ -83,15 +90,15 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
   const int seq = blockIdx.z / n_qw;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
   const int key0 = c * kAttnChunk;
-  const int32_t* table = a.block_table + (size_t)seq * a.n_blocks;
-  const PassRows* rows = a.rows + seq;
+  const int32_t* table = block_table + (size_t)seq * a.n_blocks;
+  const PassRows* rows = rows_all + seq;
 
   // Buffer loads: an offset at or past the resource's size reads as zero,
   // which masks padded dims and absent tiles without branches, so every load
   // of the wave is in flight at once.
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.kv_layer_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.kv_layer_bytes);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qf + (size_t)seq * (a.qf_bytes / 2), a.qf_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_cache, kv_layer_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_cache, kv_layer_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qf_all + (size_t)seq * (qf_bytes / 2), qf_bytes);
   // Query fragments of this wave's tile.  Columns beyond this pass's query
   // vectors hold finite values from earlier passes; their scores are masked
   // below.  Issued before the pass descriptor is read, with the chunk's two
@@ -242,7 +249,8 @@ SPEC_DEVICE void merge_in(MergeState& st, float m, float l, const float* o) {
   st.m = mn;
 }
 
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(const PassRows* rows, const float2* ws_ml,
+                                                        const float* ws_o, AttnArgs a) {
   __shared__ float s_o[256 * 9];
   __shared__ float s_m[4];
   const int qi = blockIdx.x, h = blockIdx.y % a.n_kv, seq = blockIdx.y / a.n_kv;
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid / n8, d8 = tid % n8;
   const size_t cs_ml = (size_t)a.qg_max, cs_o = (size_t)a.qg_max * E16;
-  const float2* ml = a.ws_ml + hs * a.max_chunks * a.qg_max + qi;
-  const float* wo = a.ws_o + (hs * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
+  const float2* ml = ws_ml + hs * a.max_chunks * a.qg_max + qi;
+  const float* wo = ws_o + (hs * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
   const bool worker = cg < ncg;
 
   float4 v0[kMergeBatch], v1[kMergeBatch];
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   // the first batch is issued before the pass descriptor is read
   load(worker ? cg : 0);
 
-  const int n_rows = a.rows[seq].n_rows, pos0 = a.rows[seq].pos0;
+  const int n_rows = rows[seq].n_rows, pos0 = rows[seq].pos0;
   const int QG = G * n_rows;
   if (n_rows <= 0 || qi >= QG) return;
   const int n_keys = pos0 + n_rows;
@@ -350,10 +358,12 @@ static void launch_partial(const AttnArgs& a, int n_seq, hipStream_t s) {
   const int n_qt_max = (a.n_q / a.n_kv + 1) / 2;  // 16-query tiles of kMaxRows rows
   if (a.qt_per_wave == 2 && n_qt_max > 1) {
     hipLaunchKernelGGL((attn_partial_kernel<NES, 2>),
-                       dim3(a.max_chunks, a.n_kv, (n_qt_max + 1) / 2 * n_seq), dim3(64), 0, s, a);
+                       dim3(a.max_chunks, a.n_kv, (n_qt_max + 1) / 2 * n_seq), dim3(64), 0, s, a.rows,
+                       a.block_table, a.qf, a.k_cache, a.v_cache, a.qf_bytes, a.kv_layer_bytes, a);
   } else {
     hipLaunchKernelGGL((attn_partial_kernel<NES, 1>), dim3(a.max_chunks, a.n_kv, n_qt_max * n_seq),
-                       dim3(64), 0, s, a);
+                       dim3(64), 0, s, a.rows, a.block_table, a.qf, a.k_cache, a.v_cache, a.qf_bytes,
+                       a.kv_layer_bytes, a);
   }
 }
 
@@ -376,7 +386,7 @@ hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_q / a.n_kv) * n_rows, a.n_kv * n_seq), dim3(256),
-                     0, s, a);
+                     0, s, a.rows, a.ws_ml, a.ws_o, a);
   return hipGetLastError();
 }
 

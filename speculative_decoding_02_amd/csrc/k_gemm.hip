@@ -41,8 +41,13 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
 }
 
 // HALF (NB == 1): workgroup 2b + h owns columns 8h .. 8h + 7 of block b.
+// The pass descriptor, weights, activations and K lead the arguments as
+// scalars: they are what the first loads need, and leading scalar arguments
+// can arrive preloaded in SGPRs instead of through a load of the argument
+// segment.
 template <int NB, int W, int EPI, bool HALF>
-__global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
+__global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, const uint16_t* Wp,
+                                                     const uint16_t* Ap, int Kb, GemmArgs a) {
   static_assert(!HALF || (NB == 1 && EPI != EPI_SILU && EPI != EPI_QKV),
                 "half blocks split column pairs of the SiLU and RoPE epilogues");
   constexpr int YW = HALF ? 8 : NB * 16;  // columns owned by the workgroup
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   const int g = blockIdx.x;                 // workgroup: stamps and partial outputs
   const int gb = HALF ? g >> 1 : g;         // column group of the packed weights
   const int hc = HALF ? (g & 1) * 8 : 0;    // first column of the half within its block
-  int n_rows = a.rows->n_rows;
+  int n_rows = rows->n_rows;
   int row_base = 0;
   if (a.last_row_only) {
     row_base = n_rows - 1;
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   int pre_blk = 0;
   if constexpr (EPI == EPI_QKV) {
     const int m = tid / YW, c = tid % YW;
-    const int pos = a.rows->pos0 + m;
+    const int pos = rows->pos0 + m;
     const int b = gb * NB + c / 16, w = c % 16;
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16, half_hd = a.head_dim / 2;
     if (m < kMaxRows && pos < a.max_seq) {
@@ -120,20 +125,20 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   }
 
   // ---- main loop: this wave's share of K ---------------------------------
-  const int kb0 = (a.Kb * wave) / W, kb1 = (a.Kb * (wave + 1)) / W;
+  const int kb0 = (Kb * wave) / W, kb1 = (Kb * (wave + 1)) / W;
   const int am = lane & 7;  // activation row of this lane (hi rows 0-7, lo rows 8-15)
   const bool aload = a.last_row_only ? (am == row_base) : (am < n_rows);
   // A through a range-checked buffer resource: lanes of rows the pass does not
   // use read at an out-of-range offset, which returns zero without a fetch.
   const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Ap), 0, a.Kb * 1024, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Ap), 0, Kb * 1024, 0x00020000);
   const uint32_t a_off = aload ? apack_lane_offset(lane) : 0x80000000u;
-  const uint4* wp = (const uint4*)a.Wp + (size_t)gb * a.Kb * NB * 64 + lane;
+  const uint4* wp = (const uint4*)Wp + (size_t)gb * Kb * NB * 64 + lane;
   // Half blocks: lanes of the other half's columns read at an out-of-range
   // offset of a buffer resource over the group's weights (zero, no fetch);
   // aux bit 1 is the non-temporal hint.
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint4*>(wp - lane), 0, HALF ? a.Kb * NB * 1024 : 0, 0x00020000);
+      const_cast<uint4*>(wp - lane), 0, HALF ? Kb * NB * 1024 : 0, 0x00020000);
   const uint32_t w_off = (unsigned)((lane & 15) - hc) < 8u ? (uint32_t)lane * 16 : 0x80000000u;
   floatx4 acc[NB];
 #pragma unroll
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(GemmArgs a) {
   } else if constexpr (EPI == EPI_QKV) {
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
     const int half_hd = a.head_dim / 2;
-    const int pos0 = a.rows->pos0;
+    const int pos0 = rows->pos0;
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
       const int b = gb * NB + c / 16, w = c % 16;
@@ -345,18 +350,18 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.n_groups * (HALF ? 2 : 1)), block(W * 64);
   if constexpr (HALF) {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true>), grid, block, 0, s, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true>), grid, block, 0, s, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true>), grid, block, 0, s, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false>), grid, block, 0, s, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false>), grid, block, 0, s, a); break;
-      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false>), grid, block, 0, s, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false>), grid, block, 0, s, a); break;
-      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false>), grid, block, 0, s, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
       default: return hipErrorInvalidValue;
     }
   }

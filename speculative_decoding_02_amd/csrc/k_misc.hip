@@ -11,7 +11,13 @@ namespace spec {
 // the packed A operand of the QKV projection, and publishes per-64-column
 // sums of squares.  Grid: one block of 64 threads per 64 columns; thread t
 // handles row t/8, columns 8*(t%8)..+7.
-__global__ __launch_bounds__(64) void embed_kernel(EmbedArgs a) {
+// Pointers of the first loads lead the arguments as scalars (preloaded in
+// SGPRs) and replace the copies in the argument struct.
+__global__ __launch_bounds__(64) void embed_kernel(DevState* st, const int32_t* hist,
+                                                   const int32_t* dtok, const uint16_t* E,
+                                                   EmbedArgs args) {
+  EmbedArgs a = args;
+  a.st = st; a.hist = hist; a.dtok = dtok; a.E = E;
   const int LT = a.st->LT, LD = a.st->LD;
   int n_rows = 0, pos0 = 0;
   int tok[kMaxRows];
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(64) void embed_kernel(EmbedArgs a) {
 }
 
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(a.d / 64), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(embed_kernel, dim3(a.d / 64), dim3(64), 0, s, a.st, a.hist, a.dtok, a.E, a);
   return hipGetLastError();
 }
 
@@ -99,7 +105,12 @@ constexpr int kSoftmaxThreads = 256;
 constexpr int kSoftmaxVec = 4;          // float4 per thread per chunk: chunk = 4096
 constexpr int kSoftmaxMaxPart = 32;     // partials per thread: G <= 8192
 
-__global__ __launch_bounds__(kSoftmaxThreads) void softmax_kernel(SoftmaxArgs a) {
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_kernel(const float* logits,
+                                                                 const float2* part,
+                                                                 const PassRows* rows,
+                                                                 SoftmaxArgs args) {
+  SoftmaxArgs a = args;
+  a.logits = logits; a.part = part; a.rows = rows;
   __shared__ float s_m[16], s_s[16];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int lo = c * a.chunk;
@@ -143,7 +154,8 @@ hipError_t launch_softmax(const SoftmaxArgs& a, int n_chunks, int n_rows, hipStr
   if (a.chunk != kSoftmaxThreads * kSoftmaxVec * 4 || a.G > kSoftmaxThreads * kSoftmaxMaxPart ||
       a.V % 4 != 0 || n_rows < 1 || n_rows > kMaxRows)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(softmax_kernel, dim3(n_chunks, n_rows), dim3(kSoftmaxThreads), 0, s, a);
+  hipLaunchKernelGGL(softmax_kernel, dim3(n_chunks, n_rows), dim3(kSoftmaxThreads), 0, s, a.logits,
+                     a.part, a.rows, a);
   return hipGetLastError();
 }
 
