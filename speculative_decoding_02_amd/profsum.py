@@ -121,7 +121,7 @@ def _by_name_and_grid(sel, kernel: str, lines: list) -> None:
 
 
 def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0,
-                  kernel_window: int = 0) -> str:
+                  kernel_window: int = 0, by_parity: bool = False) -> str:
     rows = load_dispatches(d)
     lines = []
     tot = collections.defaultdict(lambda: [0, 0.0])
@@ -173,6 +173,20 @@ def trace_summary(d: str, rounds: int, kernel: str | None, skip_last: int = 0,
                 lines.append(f"kernel '{kernel}' in the {W} rounds ending {skip_last} before the "
                              f"last: {len(kw)} launches, avg {sum(kw) / len(kw):.2f} us")
                 _by_name_and_grid(win, kernel, lines)
+                if by_parity:
+                    # launches of one kernel that alternate within a round (e.g. the O and
+                    # down projections of each layer): even and odd occurrences apart
+                    par = ([], [])
+                    for r in range(end - W, end):
+                        k = 0
+                        for _, n, s_, e, _ in rows[marks[r] + 1: marks[r + 1] + 1]:
+                            if kernel in n:
+                                par[k % 2].append((e - s_) / 1e3)
+                                k += 1
+                    for i, v in enumerate(par):
+                        if v:
+                            lines.append(f"  {'even' if i == 0 else 'odd'} occurrences in a round: "
+                                         f"{len(v)} launches, avg {sum(v) / len(v):.2f} us")
     return "\n".join(lines)
 
 
@@ -262,6 +276,8 @@ def main(argv=None):
     t.add_argument("--kernel", default=None)
     t.add_argument("--skip-last", type=int, default=0)
     t.add_argument("--kernel-window", type=int, default=0)
+    t.add_argument("--by-parity", action="store_true",
+                   help="split the kernel's launches in the window by occurrence parity in a round")
     p = sub.add_parser("pmc")
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
@@ -275,7 +291,7 @@ def main(argv=None):
     q.add_argument("--ses", type=int, default=32)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last, a.kernel_window))
+        print(trace_summary(a.dir, a.rounds, a.kernel, a.skip_last, a.kernel_window, a.by_parity))
     elif a.cmd == "counters":
         ks = [k for k in a.kernels.split(";") if k]
         print(counters_summary(a.dirs, ks, a.cus, a.ses))
