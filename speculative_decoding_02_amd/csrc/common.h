@@ -132,6 +132,11 @@ SPEC_DEVICE void load_gain8(const uint16_t* g, int k0, float* out) {
 // ---------------------------------------------------------------- Philox --
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 64x64->128-bit multiplies, key bumped by two Weyl constants between rounds.
+// The decode loop evaluates it at counter (position, sequence, stream, 0)
+// with key (seed, 0) and uses word 0 for a draft sample, word 1 for the
+// accept test and word 2 for the target's sample, each as its top 24 bits.
+// Pick a word with constant indices or a select: a runtime index into w[]
+// sends the array to per-thread LDS addressed through the dispatch packet.
 struct U64x4 {
   uint64_t w[4];
 };
@@ -159,13 +164,6 @@ SPEC_DEVICE U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t 
   return o;
 }
 
-// Uniform word `word` (0: draft sample, 1: accept test, 2: target sample) for
-// the token decided at absolute position p of sequence s, stream c.  Returns
-// its top 24 bits: r = u24 * 2^-24 in [0, 1).
-SPEC_DEVICE uint32_t uniform_u24(uint64_t seed, uint64_t p, uint64_t s, uint64_t c, int word) {
-  const U64x4 w = philox4x64_10(p, s, c, 0, seed, 0);
-  return (uint32_t)(w.w[word] >> 40);
-}
 
 // -------------------------------------------------------- probabilities --
 SPEC_DEVICE bool prob_valid(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
