@@ -86,7 +86,10 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_a
   const int hd = a.hd, G = a.n_q / a.n_kv, n_kv = a.n_kv;
   const int n_qt_max = (G + 1) / 2;
   const int n_qw = (n_qt_max + QTW - 1) / QTW;  // waves per (chunk, kv head, sequence)
-  const int c = blockIdx.x, h = blockIdx.y, qw = blockIdx.z % n_qw;
+  // grid.x interleaves (chunk, kv head) with the head fastest: workgroup ids
+  // congruent mod 8 share an XCD, so every chunk of a head runs on the XCD(s)
+  // the head maps to, where the merge of that head reads their partials
+  const int c = blockIdx.x / n_kv, h = blockIdx.x % n_kv, qw = blockIdx.z % n_qw;
   const int seq = blockIdx.z / n_qw;
   const int n_et = (hd + 15) / 16, E16 = n_et * 16, n_es = (hd + 31) / 32;
   const int key0 = c * kAttnChunk;
@@ -253,7 +256,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const PassRows* rows, c
                                                         const float* ws_o, AttnArgs a) {
   __shared__ float s_o[256 * 9];
   __shared__ float s_m[4];
-  const int qi = blockIdx.x, h = blockIdx.y % a.n_kv, seq = blockIdx.y / a.n_kv;
+  // one-dimensional grid, kv head fastest (the XCD its partials were written on)
+  const int n_seq = a.n_seq > 1 ? a.n_seq : 1;
+  const int qg_launch = gridDim.x / (a.n_kv * n_seq);  // query vectors per head in this launch
+  const int h = blockIdx.x % a.n_kv, qi = (blockIdx.x / a.n_kv) % qg_launch;
+  const int seq = blockIdx.x / (a.n_kv * qg_launch);
   const size_t hs = (size_t)seq * a.n_kv + h;  // (sequence, kv head) slice of the workspace
   const int hd = a.hd, G = a.n_q / a.n_kv;
   const int E16 = (hd + 15) / 16 * 16;
@@ -358,10 +365,10 @@ static void launch_partial(const AttnArgs& a, int n_seq, hipStream_t s) {
   const int n_qt_max = (a.n_q / a.n_kv + 1) / 2;  // 16-query tiles of kMaxRows rows
   if (a.qt_per_wave == 2 && n_qt_max > 1) {
     hipLaunchKernelGGL((attn_partial_kernel<NES, 2>),
-                       dim3(a.max_chunks, a.n_kv, (n_qt_max + 1) / 2 * n_seq), dim3(64), 0, s, a.rows,
+                       dim3(a.max_chunks * a.n_kv, 1, (n_qt_max + 1) / 2 * n_seq), dim3(64), 0, s, a.rows,
                        a.block_table, a.qf, a.k_cache, a.v_cache, a.qf_bytes, a.kv_layer_bytes, a);
   } else {
-    hipLaunchKernelGGL((attn_partial_kernel<NES, 1>), dim3(a.max_chunks, a.n_kv, n_qt_max * n_seq),
+    hipLaunchKernelGGL((attn_partial_kernel<NES, 1>), dim3(a.max_chunks * a.n_kv, 1, n_qt_max * n_seq),
                        dim3(64), 0, s, a.rows, a.block_table, a.qf, a.k_cache, a.v_cache, a.qf_bytes,
                        a.kv_layer_bytes, a);
   }
@@ -385,7 +392,7 @@ hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_q / a.n_kv) * n_rows, a.n_kv * n_seq), dim3(256),
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_kv * (a.n_q / a.n_kv) * n_rows * n_seq), dim3(256),
                      0, s, a.rows, a.ws_ml, a.ws_o, a);
   return hipGetLastError();
 }
