@@ -60,6 +60,33 @@ SPEC_DEVICE uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return make_uint2(v.x, v.y);
 }
 
+// Cross-lane folds with gfx950's lane-swap instructions instead of the LDS
+// permute unit: swapping a value with itself through v_permlane16_swap
+// (odd and even 16-lane rows) or v_permlane32_swap (the wave's halves) gives
+// every lane both its own value and that of lane l^16 (l^32).  Each lane
+// computes op(x, y) on the same pair the xor shuffle would give it (op
+// commutative), so results are unchanged.
+template <class Op>
+SPEC_DEVICE float fold_xor16(float v, Op op) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint32_t x = p[0], y = p[1];  // bit_cast straight off a vector element reads element 0
+  return op(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+template <class Op>
+SPEC_DEVICE float fold_xor32(float v, Op op) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  const uint32_t x = p[0], y = p[1];  // bit_cast straight off a vector element reads element 0
+  return op(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+struct OpMax {
+  SPEC_DEVICE float operator()(float x, float y) const { return fmaxf(x, y); }
+};
+struct OpAdd {
+  SPEC_DEVICE float operator()(float x, float y) const { return x + y; }
+};
+
 // Fragment layouts (lane l, l16 = l % 16, grp = l / 16):
 //   A (16 x 32):  lane l holds row l16, k = 8 grp .. 8 grp + 7
 //   B (32 x 16):  lane l holds column l16, k = 8 grp .. 8 grp + 7
@@ -197,8 +224,8 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_a
       sc[kt][r] = vis ? s[kt][r] * scale : -INFINITY;
       mx = fmaxf(mx, sc[kt][r]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = fold_xor16(mx, OpMax{});
+  mx = fold_xor32(mx, OpMax{});
   float lsum = 0.0f;
   uint16_t ph[8], pl[8];
 #pragma unroll
@@ -209,8 +236,8 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_a
     ph[j] = f32_to_bf16_rne(pv);
     pl[j] = f32_to_bf16_rne(pv - bf16_to_f32(ph[j]));
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = fold_xor16(lsum, OpAdd{});
+  lsum = fold_xor32(lsum, OpAdd{});
   const uint4 pfh = make_uint4(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
                                pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7]));
   const uint4 pfl = make_uint4(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]),
