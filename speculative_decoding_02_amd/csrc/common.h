@@ -121,6 +121,13 @@ SPEC_DEVICE void apack_store8(uint16_t* Ap, int m, int k0, const float* v) {
                  pack_bf16x2(l[6], l[7]));
 }
 
+// Stores one activation of row m at column k as its high and low bf16 parts.
+SPEC_DEVICE void apack_store1(uint16_t* Ap, int m, int k, float v) {
+  const uint16_t h = f32_to_bf16_rne(v);
+  Ap[apack_index(m, 0, k)] = h;
+  Ap[apack_index(m, 1, k)] = f32_to_bf16_rne(v - bf16_to_f32(h));
+}
+
 // 8 bf16 gains starting at k0 -> fp32
 SPEC_DEVICE void load_gain8(const uint16_t* g, int k0, float* out) {
   const uint4 v = *(const uint4*)(g + k0);

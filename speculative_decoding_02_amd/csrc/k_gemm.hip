@@ -34,6 +34,13 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 SPEC_DEVICE bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// DPP move of a float within 16-lane rows (all lanes active, bound_ctrl on).
+template <int CTRL>
+SPEC_DEVICE float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
 SPEC_DEVICE uint4 load_stream(const uint4* p) {
   // weights are read once per pass: non-temporal hint
   const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
@@ -52,11 +59,10 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
                 "half blocks split column pairs of the SiLU and RoPE epilogues");
   constexpr int YW = HALF ? 8 : NB * 16;  // columns owned by the workgroup
   constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : (NB <= 4 ? 4 : 2));  // k-blocks per batch
-  __shared__ float s_red[W * NB * 256];
-  __shared__ float s_y[kMaxRows * YW];
-  __shared__ float s_scale[kMaxRows];
+  __shared__ float s_red[W * NB * 128];
+  __shared__ float s_y[(EPI == EPI_STORE || EPI == EPI_LOGITS) ? kMaxRows * YW : 1];
   __shared__ float s_ssq[W * kMaxRows];
-  __shared__ float s_part[kMaxRows][YW / 8];
+  __shared__ float s_part[kMaxRows][(EPI == EPI_RESID && YW > 16) ? YW / 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -96,16 +102,18 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   // Epilogue operands that do not depend on the product, fetched now so their
   // latency hides behind the weight stream.
   const int col0 = gb * NB * 16 + hc;
-  constexpr int C8 = YW / 8;
-  float4 pre_x0 = make_float4(0.f, 0.f, 0.f, 0.f), pre_x1 = pre_x0;
-  uint4 pre_g = make_uint4(0, 0, 0, 0);
-  if constexpr (EPI == EPI_RESID) {
-    if (tid < kMaxRows * C8) {  // resid rows exist for all kMaxRows rows
-      const int m = tid / C8, k0 = col0 + (tid % C8) * 8;
-      const float* px = a.resid + (size_t)m * a.ldr + k0;
-      pre_x0 = *(const float4*)px;
-      pre_x1 = *(const float4*)(px + 4);
-      pre_g = *(const uint4*)(a.gain_next + k0);
+  // residual epilogue: item i = tid + i*W*64 is (row i / YW, column i % YW)
+  constexpr int RI = EPI == EPI_RESID ? (kMaxRows * YW + W * 64 - 1) / (W * 64) : 1;
+  float pre_x[RI], pre_gn[RI];
+#pragma unroll
+  for (int i = 0; i < RI; ++i) {
+    pre_x[i] = 0.0f;
+    pre_gn[i] = 0.0f;
+    const int idx = tid + i * W * 64;
+    if (EPI == EPI_RESID && idx < kMaxRows * YW) {  // resid rows exist for all kMaxRows rows
+      const int k = col0 + idx % YW;
+      pre_x[i] = a.resid[(size_t)(idx / YW) * a.ldr + k];
+      pre_gn[i] = bf16_to_f32(a.gain_next[k]);
     }
   }
   float2 pre_rope = make_float2(1.f, 0.f);
@@ -183,12 +191,24 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   for (; kb < kb1; ++kb) batch(std::integral_constant<int, 1>{}, kb);
 
   // ---- hi + lo rows, then the waves' partial sums in wave order ----------
-  // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); rows
-  // 8-15 (lanes 32-63) are the low-part products of rows 0-7.
+  // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); lanes
+  // 32-63 hold the low-part products of the rows of lanes 0-31.  Each lane
+  // swaps its accumulators with lane l^32 (v_permlane32_swap) and lanes 0-31
+  // publish hi + lo, so the cross-wave sum reads one value per wave.
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-    *(float4*)&s_red[((wave * NB + j) * 64 + lane) * 4] =
-        make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  for (int j = 0; j < NB; ++j) {
+    float hl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f = acc[j][r];  // bit_cast straight off a vector element reads element 0
+      const uint32_t u = __builtin_bit_cast(uint32_t, f);
+      const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      const uint32_t hi = p[0], lo = p[1];
+      hl[r] = __builtin_bit_cast(float, hi) + __builtin_bit_cast(float, lo);
+    }
+    if (lane < 32)
+      *(float4*)&s_red[((wave * NB + j) * 32 + lane) * 4] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+  }
   // sums of squares: lanes of one wave with the same row (lane % 8) first
   float sq = ssq_part;
   sq += __shfl_xor(sq, 8);
@@ -196,32 +216,34 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   sq += __shfl_xor(sq, 32);
   if (lane < kMaxRows) s_ssq[wave * kMaxRows + lane] = sq;
   __syncthreads();
-  if (tid < kMaxRows) {
-    float sc = 1.0f;
-    if (a.ssq != nullptr && tid < n_rows) {
-      float ss = 0.0f;
+
+  // From here each thread produces its own outputs straight from the wave
+  // partials: output row m (MFMA row mm, which differs only with
+  // last_row_only) and column cb of the workgroup's NB*16 block columns.
+  auto row_scale = [&](int m) -> float {
+    if (a.ssq == nullptr || m >= n_rows) return 1.0f;
+    float ss = 0.0f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) ss += s_ssq[w * kMaxRows + tid];
-      sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-    }
-    s_scale[tid] = sc;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < NB * 128; idx += W * 64) {
-    const int j = idx >> 7, ln = (idx >> 2) & 31, r = idx & 3;
+    for (int w = 0; w < W; ++w) ss += s_ssq[w * kMaxRows + m];
+    return 1.0f / sqrtf(ss / (float)a.K + a.eps);
+  };
+  auto col_sum = [&](int mm, int cb) -> float {
+    const int ln = (mm >> 2) * 16 + (cb & 15), r = mm & 3, j = cb >> 4;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w)  // high-part rows (lanes 0-31), then low-part rows (lanes 32-63)
-      v += s_red[((w * NB + j) * 64 + ln) * 4 + r] + s_red[((w * NB + j) * 64 + ln + 32) * 4 + r];
-    const int mm = 4 * (ln >> 4) + r;  // MFMA row = activation row
-    // with last_row_only the one used row (row_base) becomes output row 0
-    const int m = a.last_row_only ? (mm == row_base ? 0 : -1) : mm;
-    const int cy = j * 16 + (ln & 15) - hc;  // column within the workgroup's share
-    if (m >= 0 && (!HALF || (unsigned)cy < 8u)) s_y[m * YW + cy] = v * s_scale[m];
-  }
-  __syncthreads();
+    for (int w = 0; w < W; ++w) v += s_red[((w * NB + j) * 32 + ln) * 4 + r];
+    return v;
+  };
+  auto src_row = [&](int m) { return a.last_row_only ? row_base : m; };
 
-  // ---- epilogues on the [8][YW] tile ---------------------------------------
+  // ---- epilogues -------------------------------------------------------------
+  if constexpr (EPI == EPI_STORE || EPI == EPI_LOGITS) {
+    for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
+      const int m = idx / YW, c = idx % YW;
+      s_y[m * YW + c] = col_sum(src_row(m), c + hc) * row_scale(m);
+    }
+    __syncthreads();
+  }
   if constexpr (EPI == EPI_STORE) {
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
@@ -244,53 +266,49 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
       a.lm_part[g * kMaxRows + m] = make_float2(M, S);
     }
   } else if constexpr (EPI == EPI_RESID) {
-    // x += y; next GEMM's packed A = x * gain_next; sums of squares of x
-    static_assert(kMaxRows * C8 <= W * 64, "one epilogue item per thread");
-    if (tid < kMaxRows * C8) {
-      const int m = tid / C8, c8 = tid % C8;
+    // x += y; next GEMM's packed A = x * gain_next; sums of squares of x.
+    // One element per item: a row's elements sit on consecutive lanes, 16
+    // (or, for half blocks, 8) to an aligned 16-lane DPP row.
+    static_assert(YW == 8 || YW % 16 == 0, "rows fill whole DPP rows or half rows");
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+      const int idx = tid + i * W * 64, m = idx / YW, c = idx % YW;
       float sq = 0.0f;
-      if (m < n_rows) {
-        const int k0 = col0 + c8 * 8;
-        float* px = a.resid + (size_t)m * a.ldr + k0;
-        const float4 x0 = pre_x0, x1 = pre_x1;
-        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        float gn[8], xg[8];
-        {
-          const uint32_t gw[4] = {pre_g.x, pre_g.y, pre_g.z, pre_g.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gn[e] = bf16_to_f32((uint16_t)(gw[e >> 1] >> ((e & 1) * 16)));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] += s_y[m * YW + c8 * 8 + e];
-          sq += x[e] * x[e];
-          xg[e] = x[e] * gn[e];
-        }
-        *(float4*)px = make_float4(x[0], x[1], x[2], x[3]);
-        *(float4*)(px + 4) = make_float4(x[4], x[5], x[6], x[7]);
-        apack_store8(a.Ap_out, m, k0, xg);
+      if (idx < kMaxRows * YW && m < n_rows) {
+        const float x = pre_x[i] + col_sum(src_row(m), c + hc) * row_scale(m);
+        a.resid[(size_t)m * a.ldr + col0 + c] = x;
+        apack_store1(a.Ap_out, m, col0 + c, x * pre_gn[i]);
+        sq = x * x;
       }
-      s_part[m][c8] = sq;
+      // sum over the lanes of one row (up to 16), fixed order: quads, then
+      // pairs of quads (row_half_mirror pairs quad 0 with 1 and 2 with 3),
+      // then the two halves
+      sq += dpp_f32<0xb1>(sq);   // quad_perm [1,0,3,2]: lane l^1
+      sq += dpp_f32<0x4e>(sq);   // quad_perm [2,3,0,1]: lane l^2
+      sq += dpp_f32<0x141>(sq);  // row_half_mirror: the other quad of the 8-lane half
+      if constexpr (YW >= 16) sq += dpp_f32<0x128>(sq);  // row_ror:8: the other half
+      if (idx < kMaxRows * YW && (c & 15) == 0) {
+        if constexpr (YW <= 16) a.ssq_out[g * kMaxRows + m] = sq;
+        else s_part[m][c >> 4] = sq;
+      }
     }
-    __syncthreads();
-    if (tid < kMaxRows) {
-      float s = 0.0f;
-      for (int c8 = 0; c8 < C8; ++c8) s += s_part[tid][c8];
-      a.ssq_out[g * kMaxRows + tid] = s;
+    if constexpr (YW > 16) {
+      __syncthreads();
+      if (tid < kMaxRows) {
+        float s2 = 0.0f;
+        for (int q = 0; q < YW / 16; ++q) s2 += s_part[tid][q];
+        a.ssq_out[g * kMaxRows + tid] = s2;
+      }
     }
   } else if constexpr (EPI == EPI_SILU) {
     // block b = gb*NB + j: columns 0-7 are the gate and 8-15 the up outputs of
-    // features 8b .. 8b+7
-    for (int idx = tid; idx < n_rows * NB; idx += W * 64) {
-      const int m = idx / NB, j = idx % NB;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gt = s_y[m * YW + j * 16 + e];
-        const float up = s_y[m * YW + j * 16 + 8 + e];
-        v[e] = gt / (1.0f + expf(-gt)) * up;
-      }
-      apack_store8(a.Ap_out, m, (gb * NB + j) * 8, v);
+    // features 8b .. 8b+7; one feature per thread
+    for (int idx = tid; idx < n_rows * NB * 8; idx += W * 64) {
+      const int m = idx / (NB * 8), f = idx % (NB * 8), j = f >> 3, e = f & 7;
+      const float sc = row_scale(m);
+      const float gt = col_sum(src_row(m), j * 16 + e) * sc;
+      const float up = col_sum(src_row(m), j * 16 + 8 + e) * sc;
+      apack_store1(a.Ap_out, m, (gb * NB + j) * 8 + e, gt / (1.0f + expf(-gt)) * up);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
@@ -301,14 +319,15 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
       const int b = gb * NB + c / 16, w = c % 16;
       const int pos = pos0 + m;
       if (pos >= a.max_seq) continue;
-      const float mine = s_y[m * YW + c];
+      const float sc = row_scale(m);
+      const float mine = col_sum(src_row(m), c) * sc;
       if (b < q_blocks + k_blocks) {
         // pair-interleaved block: columns w and w^8 are the two halves of one pair
         const bool is_q = b < q_blocks;
         const int bl = is_q ? b : b - q_blocks;
         const int pair = bl * 8 + (w & 7), hf = w >> 3;
         const int head = pair / half_hd, jj = pair % half_hd;
-        const float other = s_y[m * YW + (c ^ 8)];
+        const float other = col_sum(src_row(m), c ^ 8) * sc;
         // (cos, sin) of pos * theta^(-2jj/hd); this thread's first item was prefetched
         const float2 r = idx == tid ? pre_rope : a.rope[(size_t)pos * half_hd + jj];
         const float lo = hf ? other : mine;
