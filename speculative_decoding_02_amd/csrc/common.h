@@ -42,12 +42,15 @@ struct PassRows {
 // ------------------------------------------------------------------ bf16 --
 SPEC_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN stays a quiet NaN).
-SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 with round-to-nearest-even (NaN stays a quiet NaN): the
+// language conversion, which gfx950 carries out in one v_cvt_pk_bf16_f32.
+SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two values at once, packed low half first (one instruction).
+typedef float spec_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 spec_bf16x2 __attribute__((ext_vector_type(2)));
+SPEC_DEVICE uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  const spec_bf16x2 v = __builtin_convertvector((spec_f32x2){lo, hi}, spec_bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ------------------------------------------------------------- KV cache --

@@ -227,31 +227,40 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_a
   mx = fold_xor16(mx, OpMax{});
   mx = fold_xor32(mx, OpMax{});
   float lsum = 0.0f;
-  uint16_t ph[8], pl[8];
+  float pv[8];
+  uint32_t ph[4], pl[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float x = sc[j >> 2][j & 3];
-    const float pv = x == -INFINITY ? 0.0f : expf(x - mx);
-    lsum += pv;
-    ph[j] = f32_to_bf16_rne(pv);
-    pl[j] = f32_to_bf16_rne(pv - bf16_to_f32(ph[j]));
+    pv[j] = x == -INFINITY ? 0.0f : expf(x - mx);
+    lsum += pv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // high and low bf16 parts, two values per conversion
+    ph[j] = f32x2_to_bf16x2_rne(pv[2 * j], pv[2 * j + 1]);
+    pl[j] = f32x2_to_bf16x2_rne(pv[2 * j] - __uint_as_float(ph[j] << 16),
+                                pv[2 * j + 1] - __uint_as_float(ph[j] & 0xffff0000u));
   }
   lsum = fold_xor16(lsum, OpAdd{});
   lsum = fold_xor32(lsum, OpAdd{});
-  const uint4 pfh = make_uint4(pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
-                               pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7]));
-  const uint4 pfl = make_uint4(pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]),
-                               pack_bf16x2(pl[4], pl[5]), pack_bf16x2(pl[6], pl[7]));
+  const uint4 pfh = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+  const uint4 pfl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
   // ---- unnormalised value sums O^T = V^T P^T --------------------------
+  // Every e-tile is computed (tiles past the head dimension read zeros), so
+  // the NET independent chains overlap; only the stores are guarded.
+  floatx4 o[NET];
 #pragma unroll
   for (int et = 0; et < NET; ++et) {
-    if (et >= n_et) continue;  // wave-uniform
-    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
-    o = mfma16(vf[et][0], pfh, o);
-    o = mfma16(vf[et][0], pfl, o);
-    o = mfma16(vf[et][1], pfh, o);
-    if (qi < QG)
-      *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = make_float4(o[0], o[1], o[2], o[3]);
+    o[et] = mfma16(vf[et][0], pfh, floatx4{0.f, 0.f, 0.f, 0.f});
+    o[et] = mfma16(vf[et][0], pfl, o[et]);
+    o[et] = mfma16(vf[et][1], pfh, o[et]);
+  }
+  if (qi < QG) {
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const float4 v = make_float4(o[et][0], o[et][1], o[et][2], o[et][3]);
+      if (et < n_et) *(float4*)(wso + (size_t)qi * E16 + 16 * et + 4 * grp) = v;
+    }
   }
   if (grp == 0 && qi < QG) wsml[qi] = make_float2(mx, lsum);
   }  // query tiles
