@@ -42,6 +42,14 @@ struct PassRows {
 // ------------------------------------------------------------------ bf16 --
 SPEC_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// floor(x / d) for 0 <= x < 2^21 and d >= 1, given inv = 1/d to within a
+// relative 2^-23 (v_rcp_f32 is within one ulp): (x + 1/2)/d lies at least
+// 1/(2d) from an integer, and inv's error plus the product's rounding move it
+// by less than (x/d) * 2^-22 < 1/(2d), so the truncation is exact.  A few
+// instructions instead of a software integer division.
+SPEC_DEVICE float rcp_small(int d) { return __builtin_amdgcn_rcpf((float)d); }
+SPEC_DEVICE int div_small(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
+
 // fp32 -> bf16 with round-to-nearest-even (NaN stays a quiet NaN): the
 // language conversion, which gfx950 carries out in one v_cvt_pk_bf16_f32.
 SPEC_DEVICE uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }

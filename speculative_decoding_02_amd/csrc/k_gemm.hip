@@ -313,6 +313,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   } else if constexpr (EPI == EPI_QKV) {
     const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
     const int half_hd = a.head_dim / 2;
+    const int G = div_small(a.q_dim, rcp_small(a.kv_dim)), n_es = (a.head_dim + 31) / 32;
+    const float inv_half = rcp_small(half_hd), inv_hd = rcp_small(a.head_dim), inv_G = rcp_small(G);
     const int pos0 = rows->pos0;
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
         const bool is_q = b < q_blocks;
         const int bl = is_q ? b : b - q_blocks;
         const int pair = bl * 8 + (w & 7), hf = w >> 3;
-        const int head = pair / half_hd, jj = pair % half_hd;
+        const int head = div_small(pair, inv_half), jj = pair - head * half_hd;
         const float other = col_sum(src_row(m), c ^ 8) * sc;
         // (cos, sin) of pos * theta^(-2jj/hd); this thread's first item was prefetched
         const float2 r = idx == tid ? pre_rope : a.rope[(size_t)pos * half_hd + jj];
@@ -335,11 +337,10 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
         const float val = hf ? hi * r.x + lo * r.y : lo * r.x - hi * r.y;
         const int dim = jj + hf * half_hd;
         if (is_q) {
-          const int G = a.q_dim / a.kv_dim, n_es = (a.head_dim + 31) / 32;
-          const int qi = m * G + head % G;
+          const int h_kv = div_small(head, inv_G), qi = m * G + (head - h_kv * G);
           const uint16_t hb = f32_to_bf16_rne(val);
-          a.qf[qfrag_index(head / G, G, n_es, qi, 0, dim)] = hb;
-          a.qf[qfrag_index(head / G, G, n_es, qi, 1, dim)] = f32_to_bf16_rne(val - bf16_to_f32(hb));
+          a.qf[qfrag_index(h_kv, G, n_es, qi, 0, dim)] = hb;
+          a.qf[qfrag_index(h_kv, G, n_es, qi, 1, dim)] = f32_to_bf16_rne(val - bf16_to_f32(hb));
         } else {
           const int blk = idx == tid ? pre_blk : a.block_table[pos / kBlock];
           const uint16_t hb = f32_to_bf16_rne(val);
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
         }
       } else {
         const int f0 = (b - q_blocks - k_blocks) * 16 + w;
-        const int head = f0 / a.head_dim, dim = f0 % a.head_dim;
+        const int head = div_small(f0, inv_hd), dim = f0 - head * a.head_dim;
         const int blk = idx == tid ? pre_blk : a.block_table[pos / kBlock];
         const uint16_t hb = f32_to_bf16_rne(mine);
         a.v_cache[vt_index(blk, a.n_kv, head, 0, a.head_dim, dim, pos % kBlock)] = hb;
