@@ -31,6 +31,8 @@
 // A batch of sequences runs in the same two launches: the sequence index
 // extends grid.z of the partial kernel and grid.y of the merge, and selects
 // the sequence's pass descriptor, block table, query fragments and workspace.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace spec {
@@ -266,32 +268,57 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(const PassRows* rows_a
   }  // query tiles
 }
 
-// Merge of the chunk partials of query vector qi of kv head h.  Thread
-// (chunk group cg, 8-dim group d8) takes chunks cg, cg + ncg, ... and keeps a
-// running (max, sum, value sum), rescaling by exp(m_old - m_new); the thread
-// states are then brought to the block-wide maximum and summed over the
-// chunk groups in a fixed order (deterministic).
-constexpr int kMergeBatch = 4;
+// Merge of the chunk partials of query vector qi of kv head h, one wave per
+// (head, query vector): lane (chunk group cg, 8-dim group d8) takes chunks
+// cg, cg + ncg, ... (ncg = 64 / n8 groups of n8 = hd/8 lanes).  Each batch of
+// a lane's chunks is folded in two passes -- its maximum, then the weights
+// exp(m_c - max), the running sums rescaled once per batch -- and the chunk
+// groups are then brought to the wave's maximum and summed in a fixed order
+// (deterministic), all inside the wave: no LDS and no barrier.
+constexpr int kMergeBatch = 10;  // chunks per lane in flight at once
 
-struct MergeState {
-  float m, l, o[8];
-};
-
-// branch-free: a chunk with no visible key has m = -inf and weight 0
-SPEC_DEVICE void merge_in(MergeState& st, float m, float l, const float* o) {
-  const float mn = fmaxf(st.m, m);
-  const float a = st.m == -INFINITY ? 0.0f : expf(st.m - mn);
-  const float b = m == -INFINITY ? 0.0f : expf(m - mn);
-  st.l = st.l * a + l * b;
+// v + (the value of lane l ^ OFF), by the cheapest exchange for that offset
+template <int OFF>
+SPEC_DEVICE float add_xor(float v) {
+  if constexpr (OFF == 32) return fold_xor32(v, OpAdd{});
+  else if constexpr (OFF == 16) return fold_xor16(v, OpAdd{});
+  else if constexpr (OFF == 8)
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                      0x128, 0xf, 0xf, true));
+  else if constexpr (OFF == 2)
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                      0x4e, 0xf, 0xf, true));
+  else if constexpr (OFF == 1)
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                      0xb1, 0xf, 0xf, true));
+  else return v + __shfl_xor(v, OFF);
+}
+template <int OFF>
+SPEC_DEVICE void butterfly_add(float* v) {  // over lanes OFF, 2*OFF, ... < 64 apart
+  if constexpr (OFF < 64) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = st.o[e] * a + o[e] * b;
-  st.m = mn;
+    for (int e = 0; e < 9; ++e) v[e] = add_xor<OFF>(v[e]);
+    butterfly_add<2 * OFF>(v);
+  }
+}
+// maximum over the wave (max is exact, so any exchange order gives the same value)
+SPEC_DEVICE float wave_max_dpp(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xf, 0xf, true));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xb1>{}));   // lane l^1
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4e>{}));   // lane l^2
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // the other quad of the 8-lane half
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x128>{}));  // the other half of the 16-lane row
+  v = fold_xor16(v, OpMax{});
+  return fold_xor32(v, OpMax{});
 }
 
-__global__ __launch_bounds__(256) void attn_merge_kernel(const PassRows* rows, const float2* ws_ml,
-                                                        const float* ws_o, AttnArgs a) {
-  __shared__ float s_o[256 * 9];
-  __shared__ float s_m[4];
+// N8 > 0: hd / 8, a power of two known at compile time; 0: any hd (multiple of 8)
+template <int N8>
+__global__ __launch_bounds__(64) void attn_merge_kernel(const PassRows* rows, const float2* ws_ml,
+                                                       const float* ws_o, AttnArgs a) {
   // one-dimensional grid, kv head fastest (the XCD its partials were written on)
   const int n_seq = a.n_seq > 1 ? a.n_seq : 1;
   const int qg_launch = gridDim.x / (a.n_kv * n_seq);  // query vectors per head in this launch
@@ -300,9 +327,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const PassRows* rows, c
   const size_t hs = (size_t)seq * a.n_kv + h;  // (sequence, kv head) slice of the workspace
   const int hd = a.hd, G = a.n_q / a.n_kv;
   const int E16 = (hd + 15) / 16 * 16;
-  const int n8 = hd / 8, ncg = 256 / n8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cg = tid / n8, d8 = tid % n8;
+  const int n8 = N8 > 0 ? N8 : hd / 8, ncg = 64 / n8;
+  const int lane = threadIdx.x;
+  const int cg = lane / n8, d8 = lane % n8;
   const size_t cs_ml = (size_t)a.qg_max, cs_o = (size_t)a.qg_max * E16;
   const float2* ml = ws_ml + hs * a.max_chunks * a.qg_max + qi;
   const float* wo = ws_o + (hs * a.max_chunks * a.qg_max + qi) * E16 + d8 * 8;
@@ -328,71 +355,70 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const PassRows* rows, c
   const int n_keys = pos0 + n_rows;
   const int n_active = (n_keys + kAttnChunk - 1) / kAttnChunk;
 
-  MergeState st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
+  float mx = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
+  for (int e = 0; e < 8; ++e) o[e] = 0.0f;
   for (int c0 = worker ? cg : n_active; c0 < n_active; c0 += kMergeBatch * ncg) {
     if (c0 != cg) load(c0);
     __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before any use
+    // slots past the active chunks were loaded from clamped indices: their
+    // workspace contents may be anything (not even finite), so they are
+    // replaced, not weighted by zero; a chunk with no visible key has m = -inf
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (c0 + u * ncg < n_active) bm = fmaxf(bm, mv[u].x);
+    const float mn = fmaxf(mx, bm);
+    const float sa = mx == -INFINITY ? 0.0f : expf(mx - mn);
+    l *= sa;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= sa;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      // slots past the active chunks were loaded from clamped indices: their
-      // workspace contents may be anything (not even finite), so they are
-      // replaced, not weighted by zero
       const bool ok = c0 + u * ncg < n_active;
-      const float o[8] = {ok ? v0[u].x : 0.f, ok ? v0[u].y : 0.f, ok ? v0[u].z : 0.f,
-                          ok ? v0[u].w : 0.f, ok ? v1[u].x : 0.f, ok ? v1[u].y : 0.f,
-                          ok ? v1[u].z : 0.f, ok ? v1[u].w : 0.f};
-      merge_in(st, ok ? mv[u].x : -INFINITY, ok ? mv[u].y : 0.0f, o);
+      const float m = ok ? mv[u].x : -INFINITY;
+      const float w = m == -INFINITY ? 0.0f : expf(m - mn);
+      const float ov[8] = {ok ? v0[u].x : 0.f, ok ? v0[u].y : 0.f, ok ? v0[u].z : 0.f,
+                           ok ? v0[u].w : 0.f, ok ? v1[u].x : 0.f, ok ? v1[u].y : 0.f,
+                           ok ? v1[u].z : 0.f, ok ? v1[u].w : 0.f};
+      l += w * (ok ? mv[u].y : 0.0f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += w * ov[e];
     }
+    mx = mn;
   }
-  // block-wide maximum
-  const float wm = wave_max_f32(st.m);
-  if (lane == 0) s_m[wave] = wm;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  const float sc = st.m == -INFINITY ? 0.0f : expf(st.m - M);
+  // the wave's maximum, then every chunk group's sums at that scale
+  const float M = wave_max_dpp(mx);
+  const float sc = mx == -INFINITY ? 0.0f : expf(mx - M);
   float v[9];
-  v[0] = st.l * sc;
+  v[0] = l * sc;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[1 + e] = st.o[e] * sc;
-  // Sum over the chunk groups, in a fixed order.  When n8 divides 64 the
-  // lanes of one 8-dim slice d8 sit n8 apart in every wave: a butterfly
-  // over those lanes, then the four waves' sums in wave order.  Otherwise
-  // (hd 168) one thread per slice adds the groups one after another.
-  const bool butterfly = 64 % n8 == 0;
-  if (butterfly) {
-    for (int off = n8; off < 64; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < 9; ++e) v[e] += __shfl_xor(v[e], off);
-    if (lane < n8) {
-#pragma unroll
-      for (int e = 0; e < 9; ++e) s_o[(wave * n8 + lane) * 9 + e] = v[e];
-    }
+  for (int e = 0; e < 8; ++e) v[1 + e] = o[e] * sc;
+  // sum over the chunk groups (lanes n8 apart): a butterfly when n8 is a
+  // power of two, else lane d8 adds the groups one after another
+  if constexpr (N8 > 0) {
+    butterfly_add<N8>(v);
   } else {
+    float acc[9];
 #pragma unroll
-    for (int e = 0; e < 9; ++e) s_o[tid * 9 + e] = v[e];
-  }
-  __syncthreads();
-  if (tid < n8) {
-    float acc[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int n_parts = butterfly ? 4 : ncg;  // waves, or chunk groups
-    for (int g = 0; g < n_parts; ++g) {
-      const float* q = s_o + (g * n8 + tid) * 9;
+    for (int e = 0; e < 9; ++e) acc[e] = v[e];
+    for (int g = 1; g < ncg; ++g) {
 #pragma unroll
-      for (int e = 0; e < 9; ++e) acc[e] += q[e];
+      for (int e = 0; e < 9; ++e) acc[e] += __shfl(v[e], d8 + g * n8);
     }
-    const float inv = 1.0f / acc[0];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) v[e] = acc[e];
+  }
+  if (lane < n8) {
+    const float inv = 1.0f / v[0];
     float out[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = acc[1 + e] * inv;
+    for (int e = 0; e < 8; ++e) out[e] = v[1 + e] * inv;
     const int r = qi / G, gi = qi % G;
     if (a.a_tiles == 0)  // the single pass's GEMM layout
-      apack_store8(a.Ap_out, r, (h * G + gi) * hd + tid * 8, out);
+      apack_store8(a.Ap_out, r, (h * G + gi) * hd + lane * 8, out);
     else  // the rows GEMM's tiles (a batch of sequences)
-      apack_store8_rt(a.Ap_out, seq * a.seq_rows + r, (h * G + gi) * hd + tid * 8, out, a.a_tiles);
+      apack_store8_rt(a.Ap_out, seq * a.seq_rows + r, (h * G + gi) * hd + lane * 8, out, a.a_tiles);
   }
 }
 
@@ -428,8 +454,16 @@ hipError_t launch_attn(const AttnArgs& a, int n_rows, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_kv * (a.n_q / a.n_kv) * n_rows * n_seq), dim3(256),
-                     0, s, a.rows, a.ws_ml, a.ws_o, a);
+  if (a.hd % 8 != 0 || a.hd / 8 > 64) return hipErrorInvalidValue;
+  const dim3 mg(a.n_kv * (a.n_q / a.n_kv) * n_rows * n_seq), mb(64);
+  switch (a.hd / 8) {
+    case 2: hipLaunchKernelGGL(attn_merge_kernel<2>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+    case 4: hipLaunchKernelGGL(attn_merge_kernel<4>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+    case 8: hipLaunchKernelGGL(attn_merge_kernel<8>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+    case 16: hipLaunchKernelGGL(attn_merge_kernel<16>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+    case 32: hipLaunchKernelGGL(attn_merge_kernel<32>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+    default: hipLaunchKernelGGL(attn_merge_kernel<0>, mg, mb, 0, s, a.rows, a.ws_ml, a.ws_o, a); break;
+  }
   return hipGetLastError();
 }
 
