@@ -12,6 +12,8 @@ sizes), with fewer layers so the fp64 oracle finishes in seconds:
   * 1.3B-shaped slice (MHA 16 x 128, vocab 32000) with a draft sharing the
     target's embedding and LM head;
   * a long context: 1500-token prompt through 32/8 x 128 attention;
+  * a d_model-8192 target with 256-dim heads and a draft with 32-dim heads
+    (GEMM and attention variants the pairs above do not reach);
   * the benchmark's own workload at full size (sampled outputs, below).
 
 Every round is teacher-forced: draft rows (1e-4) and samples (bit-exact),
@@ -92,6 +94,19 @@ def test_long_context_attention():
     t = synth.ModelConfig("long-ctx-1L", 1, 256, 32, 8, 128, 512, 1024)
     d = t.replace(name="long-ctx-draft")
     run_case(t, d, prompt_len=1500, K=4, rounds=3, greedy=False)
+
+
+def test_wide_model_and_narrow_heads():
+    """Launch variants the workload pairs do not reach: a d_model-8192 target
+    whose O and down projections take two column blocks per workgroup (each
+    residual row spans two 16-lane groups, whose sums of squares meet in LDS),
+    with 256-dim heads (eight 32-dim steps in the attention partial, 32 lanes
+    per chunk group in the merge); and a draft with 32-dim heads (one step,
+    4 lanes per chunk group).  The 200-token prompt gives every head seven
+    chunks to merge."""
+    t = synth.ModelConfig("wide-d8192-hd256-1L", 1, 8192, 32, 8, 256, 1024, 1024)
+    d = synth.ModelConfig("hd32-draft-1L", 1, 512, 16, 4, 32, 1024, 1024)
+    run_case(t, d, prompt_len=200, K=4, rounds=2, greedy=False)
 
 
 def test_8b_bench_workload_sampled():
