@@ -12,8 +12,9 @@ sizes), with fewer layers so the fp64 oracle finishes in seconds:
   * 1.3B-shaped slice (MHA 16 x 128, vocab 32000) with a draft sharing the
     target's embedding and LM head;
   * a long context: 1500-token prompt through 32/8 x 128 attention;
-  * a d_model-8192 target with 256-dim heads and a draft with 32-dim heads
-    (GEMM and attention variants the pairs above do not reach);
+  * a d_model-8192 target with 256-dim heads and a draft with 32-dim heads,
+    and a d_model-16384 target (GEMM and attention variants the pairs above
+    do not reach);
   * the benchmark's own workload at full size (sampled outputs, below).
 
 Every round is teacher-forced: draft rows (1e-4) and samples (bit-exact),
@@ -107,6 +108,15 @@ def test_wide_model_and_narrow_heads():
     t = synth.ModelConfig("wide-d8192-hd256-1L", 1, 8192, 32, 8, 256, 1024, 1024)
     d = synth.ModelConfig("hd32-draft-1L", 1, 512, 16, 4, 32, 1024, 1024)
     run_case(t, d, prompt_len=200, K=4, rounds=2, greedy=False)
+
+
+def test_very_wide_residual():
+    """d_model 16384: the O and down projections take four column blocks per
+    workgroup, so each thread of the residual epilogue handles two items and
+    a row's sums of squares meet from four 16-lane groups."""
+    t = synth.ModelConfig("wide-d16384-1L", 1, 16384, 16, 4, 64, 512, 1024)
+    d = synth.ModelConfig("small-draft-1L", 1, 256, 8, 2, 32, 512, 1024)
+    run_case(t, d, prompt_len=40, K=3, rounds=2, greedy=False)
 
 
 def test_8b_bench_workload_sampled():
