@@ -21,6 +21,8 @@
 namespace spec {
 
 constexpr int kBatchThreads = 256;
+constexpr uint32_t kBatchOOB = 0x80000000u;  // buffer offset past any range: reads zero, no fetch
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // --------------------------------------------------------------- embed --
 __global__ __launch_bounds__(kBatchThreads) void batch_embed_kernel(BatchEmbedArgs a) {
@@ -83,6 +85,11 @@ __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a
     return;
   }
   float* x = a.x + (size_t)m * d;
+  // split partials through a range-checked buffer: the loads of every slice
+  // of a chunk are issued together (slices past S read zero without a fetch
+  // and are not added), so a chunk costs one round trip, not one per slice
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.P), 0, a.S > 0 ? (int)((size_t)a.S * a.M * d * 4) : 0, 0x00020000);
   float v[kNormChunks][8];
   float ss = 0.0f;
 #pragma unroll
@@ -92,11 +99,19 @@ __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a
       const float4 x0 = *(const float4*)(x + k0), x1 = *(const float4*)(x + k0 + 4);
       float r[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       if (a.S > 0) {
-        for (int sl = 0; sl < a.S; ++sl) {
-          const float* p = a.P + ((size_t)sl * a.M + m) * d + k0;
-          const float4 p0 = *(const float4*)p, p1 = *(const float4*)(p + 4);
-          r[0] += p0.x; r[1] += p0.y; r[2] += p0.z; r[3] += p0.w;
-          r[4] += p1.x; r[5] += p1.y; r[6] += p1.z; r[7] += p1.w;
+        f32x4_t p0[kRowsMaxSplit], p1[kRowsMaxSplit];
+#pragma unroll
+        for (int sl = 0; sl < kRowsMaxSplit; ++sl) {
+          const uint32_t off = sl < a.S ? (uint32_t)((((size_t)sl * a.M + m) * d + k0) * 4) : kBatchOOB;
+          p0[sl] = __builtin_amdgcn_raw_buffer_load_b128(rP, (int)off, 0, 0);
+          p1[sl] = __builtin_amdgcn_raw_buffer_load_b128(rP, (int)(off == kBatchOOB ? off : off + 16), 0, 0);
+        }
+#pragma unroll
+        for (int sl = 0; sl < kRowsMaxSplit; ++sl) {  // slice order, as a plain loop would add
+          if (sl < a.S) {
+            r[0] += p0[sl][0]; r[1] += p0[sl][1]; r[2] += p0[sl][2]; r[3] += p0[sl][3];
+            r[4] += p1[sl][0]; r[5] += p1[sl][1]; r[6] += p1[sl][2]; r[7] += p1[sl][3];
+          }
         }
         *(float4*)(x + k0) = make_float4(r[0], r[1], r[2], r[3]);
         *(float4*)(x + k0 + 4) = make_float4(r[4], r[5], r[6], r[7]);
@@ -107,6 +122,7 @@ __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a
         ss += r[e] * r[e];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // one chunk's loads in flight at a time (registers)
   }
   ss = block_reduce(ss, s_red, [](float p, float q) { return p + q; });
   const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(kBatchThreads) void norm_pack_kernel(NormPackArgs a
 
 hipError_t launch_norm_pack(const NormPackArgs& a, hipStream_t s) {
   if (a.M < 1 || a.M > 8 * a.RT || a.RT > kRowsMaxM / 8 || a.d % 32 || a.d > kNormPackMaxD ||
-      a.S < 0 || (a.S > 0 && a.P == nullptr))
+      a.S < 0 || a.S > kRowsMaxSplit || (a.S > 0 && a.P == nullptr))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(norm_pack_kernel, dim3(8 * a.RT), dim3(kBatchThreads), 0, s, a);
   return hipGetLastError();
@@ -139,11 +155,23 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
   const int ldy = a.q_dim + 2 * a.kv_dim;
   const int G = a.q_dim / a.kv_dim, n_es = (a.hd + 31) / 32;
   const size_t total = (size_t)a.M * per_row;
-  // column c of row m: the product, or the sum of its split partials
+  // column c of row m: the product, or the sum of its split partials in
+  // slice order; every slice's load is issued before the first add (slices
+  // past S read zero without a fetch through the range-checked buffer and
+  // are not added)
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.P), 0, a.S > 0 ? (int)((size_t)a.S * a.M * ldy * 4) : 0, 0x00020000);
   auto yv = [&](int m, int c) -> float {
     if (a.S == 0) return a.y[(size_t)m * ldy + c];
+    float p[kRowsMaxSplit];
+#pragma unroll
+    for (int sl = 0; sl < kRowsMaxSplit; ++sl) {
+      const uint32_t off = sl < a.S ? (uint32_t)((((size_t)sl * a.M + m) * ldy + c) * 4) : kBatchOOB;
+      p[sl] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rP, (int)off, 0, 0));
+    }
     float v = 0.0f;
-    for (int sl = 0; sl < a.S; ++sl) v += a.P[((size_t)sl * a.M + m) * ldy + c];
+#pragma unroll
+    for (int sl = 0; sl < kRowsMaxSplit; ++sl) v = sl < a.S ? v + p[sl] : v;
     return v;
   };
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -190,7 +218,7 @@ __global__ __launch_bounds__(kBatchThreads) void qkv_post_kernel(QkvPostArgs a) 
 
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
   if (a.M < 1 || a.R < 1 || a.R > kMaxRows || a.M % a.R || a.hd % 2 || a.kv_dim <= 0 ||
-      a.q_dim % a.kv_dim || a.S < 0 || (a.S > 0 ? a.P == nullptr : a.y == nullptr))
+      a.q_dim % a.kv_dim || a.S < 0 || a.S > kRowsMaxSplit || (a.S > 0 ? a.P == nullptr : a.y == nullptr))
     return hipErrorInvalidValue;
   const size_t total = (size_t)a.M * (a.q_dim / 2 + a.kv_dim / 2 + a.kv_dim);
   size_t blocks = (total + kBatchThreads - 1) / kBatchThreads;
