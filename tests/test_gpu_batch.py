@@ -179,6 +179,20 @@ def test_mid_batch_wide_gemm_rounds_match_oracle(B, K):
     assert acc > 0
 
 
+HD168 = synth.ModelConfig("hd168-g5-1L", 1, 512, 20, 4, 168, 512, 1024)
+
+
+def test_batch_hd168_five_query_heads():
+    """168-dim heads (the merge's general chunk-group fold: 21 lanes to a
+    group, three groups) with five query heads per KV head, four sequences
+    (one wave scores both 16-query tiles of a chunk), 80-token prompts
+    (three key chunks per head), through the rows GEMM (QKV 4704 columns)."""
+    import speculative_decoding_02_amd as sd
+    w = synth.weights_np(HD168)
+    acc = run_teacher_forced(sd, HD168, w, 4, 4, False, rounds=3, prompt_len=80)
+    assert acc > 0
+
+
 def test_greedy_streams_equal_plain_greedy_with_ngram_drafts(toy_w):
     """Greedy speculative output is the target's own greedy text whatever the
     drafts; here the batched prompt-lookup drafter, on prompts that repeat so
