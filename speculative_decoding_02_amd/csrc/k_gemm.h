@@ -93,7 +93,7 @@ struct GemmPlan {
 // shape end between 14 and 39 us; 256 workgroups of 7 blocks all end
 // together, 37.0 instead of 40.1 us).  So when the column blocks divide
 // evenly over the CUs (n_cu > 0) a workgroup takes n_blocks / n_cu of them
-// (up to 7, eight waves from four blocks on).  Otherwise: two blocks per
+// (2, 4, 5 or 7, eight waves from four blocks on).  Otherwise: two blocks per
 // workgroup once that still leaves >= 192 workgroups, four waves, except
 // for narrow matrices with a long K, where only eight waves per workgroup
 // keep enough loads in flight.
@@ -109,7 +109,7 @@ inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_ha
   const int n_blocks = n_cols / 16;
   p.Kb = K / 32;
   const int q = n_cu > 0 && n_blocks % n_cu == 0 ? n_blocks / n_cu : 0;
-  if ((q == 2 || q == 4 || q == 7) && q >= nb_min) {
+  if ((q == 2 || q == 4 || q == 5 || q == 7) && q >= nb_min) {
     p.shape.nb = q;
     p.n_groups = n_cu;
     p.shape.waves = q >= 4 ? 8 : 4;
@@ -119,6 +119,21 @@ inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_ha
   p.n_groups = n_blocks / p.shape.nb;
   p.shape.waves = (p.n_groups <= 128 && p.Kb >= 256) ? 8 : 4;
   if (allow_half && p.shape.nb == 1 && n_cu > 0 && 2 * n_blocks <= n_cu) p.shape.half = 1;
+  // More workgroups than CUs but not a whole number per CU: the CUs that
+  // hold one more stream alone at the end.  One equal workgroup per CU on
+  // fewer CUs is faster (each CU's share of the bandwidth grows as fewer
+  // stream; 1.3B-shaped gate/up, 688 blocks: 344 two-block workgroups
+  // 11.3 us, 172 four-block 10.3 us): take the smallest block count that
+  // divides the blocks into at most one workgroup per CU.
+  if (n_cu > 0 && !p.shape.half && p.workgroups() > n_cu && p.workgroups() % n_cu != 0) {
+    for (const int nb : {2, 4, 5, 7}) {
+      if (nb < nb_min || n_blocks % nb || n_blocks / nb > n_cu) continue;
+      p.shape.nb = nb;
+      p.n_groups = n_blocks / nb;
+      p.shape.waves = nb >= 5 ? 8 : 4;  // five and seven blocks are built with eight waves only
+      break;
+    }
+  }
   return p;
 }
 

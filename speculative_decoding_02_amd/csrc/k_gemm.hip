@@ -403,6 +403,7 @@ hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) 
     if (sh.nb == 1) return launch_epi<1, 8>(epi, a, s);
     if (sh.nb == 2) return launch_epi<2, 8>(epi, a, s);
     if (sh.nb == 4) return launch_epi<4, 8>(epi, a, s);
+    if (sh.nb == 5) return launch_epi<5, 8>(epi, a, s);
     if (sh.nb == 7) return launch_epi<7, 8>(epi, a, s);
   }
   return hipErrorInvalidValue;
