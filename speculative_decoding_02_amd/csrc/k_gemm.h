@@ -24,9 +24,11 @@ enum Epi : int {
 };
 
 struct GemmArgs {
-  // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16]
+  // packed weights: [n_groups][Kb][NB][64 lanes][8 bf16], or for column
+  // slices [n_groups]{[Kb][NB-1][64 lanes][8 bf16], [Kb][live lanes][8 bf16]}
   const uint16_t* Wp;
   int n_groups;      // one workgroup per group of NB 16-column blocks
+  int slice_cols;    // column slices: columns per workgroup (0: whole blocks)
   int Kb;            // K / 32
   int K;
   // A operand: packed rows (see apack_index) of length K
@@ -65,15 +67,47 @@ struct GemmShape {
   int nb;        // 16-column blocks per workgroup
   int waves;     // waves per workgroup, splitting K
   int half = 0;  // nb == 1 only: two workgroups per block, 8 columns each
+  int slice = 0; // column slices: columns per workgroup, the last of the nb blocks partial
 };
+
+// Column slices.  A workgroup owns `slice` consecutive columns: nb - 1 whole
+// 16-column blocks and a last block with t = slice - 16 (nb - 1) live
+// columns.  For epilogues that pair columns (RoPE halves, gate/up) the unit
+// is a pair -- column w and w + 8 of a block -- and the last block holds
+// t / 2 pairs, columns w with (w & 7) < t / 2.  The last block is stored
+// compacted, only its live lanes (4 per live column, one per 8-value k
+// group), so every workgroup reads a contiguous span of exactly its bytes.
+enum SliceKind : int { kSliceNone = 0, kSliceCols = 1, kSlicePairs = 2 };
+constexpr int kSliceMaxNb = 4;
+// Slices only for matrices of at least this many bytes per CU: below it the
+// launch's fixed cost dominates and the extra CUs do not pay for the partial
+// block's loads (measured: 31B-shaped QKV, O, gate/up and down at 0.23-1.8 MB
+// per CU and the 4B-shaped down at 205 KB faster; the 8B-shaped QKV at 197 KB
+// and smaller QKV and O projections slower).
+constexpr double kSliceMinBytesPerCu = 200e3;
+
+// Lane of the partial block: live, and its index in the compacted k-block.
+__host__ __device__ inline bool slice_tail_lane(int lane, int t, bool paired, int* idx) {
+  const int w = lane & 15, q = lane >> 4;
+  if (paired) {
+    const int tp = t >> 1;
+    *idx = q * t + (w & 7) + (w >> 3) * tp;
+    return (w & 7) < tp;
+  }
+  *idx = q * t + w;
+  return w < t;
+}
 hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s);
 // Norm partials each GEMM thread folds: ssq_groups <= waves * 64 / 8 * this.
 constexpr int kGemmMaxSsqPerThread = 16;
 
 // Packs a [N][K] bf16 matrix given as row pointers into the MFMA stream
-// layout.  row_ptr[n] (device array, n < n_groups*NB*16) may be null (zero row).
-hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, uint16_t* out,
-                       hipStream_t s);
+// layout.  row_ptr[(g * nb + j) * 16 + w] (device array) is the row of column
+// w of block j of workgroup g, or null (zero row); with column slices
+// (slice_cols > 0, paired as the epilogue pairs columns) the dead columns of
+// the last block are not stored.
+hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, int slice_cols,
+                       int paired, uint16_t* out, hipStream_t s);
 
 // ------------------------------------------------------------ GEMM plans --
 // One workgroup per group of `nb` 16-column blocks (or per half block),
@@ -82,6 +116,12 @@ struct GemmPlan {
   GemmShape shape{1, 4};
   int n_groups = 0, Kb = 0;
   int workgroups() const { return n_groups * (shape.half ? 2 : 1); }
+  // bf16 elements of the packed matrix
+  size_t packed_elems() const {
+    const size_t per_kb = shape.slice ? (size_t)(shape.nb - 1) * 512 + 32 * (shape.slice - 16 * (shape.nb - 1))
+                                      : (size_t)shape.nb * 512;
+    return (size_t)n_groups * Kb * per_kb;
+  }
 };
 
 // Shapes measured on MI355X (graph-replayed sweeps over nb in {1,2,4,7} and
@@ -104,7 +144,8 @@ struct GemmPlan {
 // the B-fragment slots of its own half, the others read as zero without a
 // fetch), so every CU gets a share.  Not for epilogues that pair columns
 // across the halves of a block (RoPE pairs w, w^8; gate/up pairs).
-inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_half = false) {
+inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_half = false,
+                          int slice_kind = kSliceNone) {
   GemmPlan p;
   const int n_blocks = n_cols / 16;
   p.Kb = K / 32;
@@ -131,6 +172,23 @@ inline GemmPlan plan_gemm(int n_cols, int nb_min, int K, int n_cu, bool allow_ha
       p.shape.nb = nb;
       p.n_groups = n_blocks / nb;
       p.shape.waves = nb >= 5 ? 8 : 4;  // five and seven blocks are built with eight waves only
+      break;
+    }
+  }
+  // Still not a whole number of workgroups per CU, and a large matrix:
+  // column slices, r workgroups per CU with n_cols / (r n_cu) columns each,
+  // the smallest r that keeps a workgroup within kSliceMaxNb blocks.
+  if (slice_kind != kSliceNone && n_cu > 0 && p.workgroups() % n_cu != 0 &&
+      2.0 * n_cols * K / n_cu >= kSliceMinBytesPerCu) {
+    for (int r = 1; r <= 8; ++r) {
+      const int G = r * n_cu;
+      if (n_cols % G) continue;
+      const int cw = n_cols / G;
+      if (cw % 16 == 0 || (slice_kind == kSlicePairs && cw % 2)) continue;
+      const int nb = (cw + 15) / 16;
+      if (nb > kSliceMaxNb || nb < nb_min) continue;
+      p.shape = GemmShape{nb, 4, 0, cw};
+      p.n_groups = G;
       break;
     }
   }

@@ -48,15 +48,19 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
 }
 
 // HALF (NB == 1): workgroup 2b + h owns columns 8h .. 8h + 7 of block b.
+// SLICE: workgroup g owns the column slice g (a.slice_cols columns, see
+// GemmShape): NB - 1 whole blocks and a compacted partial block.
 // The pass descriptor, weights, activations and K lead the arguments as
 // scalars: they are what the first loads need, and leading scalar arguments
 // can arrive preloaded in SGPRs instead of through a load of the argument
 // segment.
-template <int NB, int W, int EPI, bool HALF>
+template <int NB, int W, int EPI, bool HALF, bool SLICE>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, const uint16_t* Wp,
                                                      const uint16_t* Ap, int Kb, GemmArgs a) {
   static_assert(!HALF || (NB == 1 && EPI != EPI_SILU && EPI != EPI_QKV),
                 "half blocks split column pairs of the SiLU and RoPE epilogues");
+  static_assert(!SLICE || (!HALF && (EPI == EPI_RESID || EPI == EPI_QKV || EPI == EPI_SILU)),
+                "column slices for the residual, QKV and SiLU epilogues");
   constexpr int YW = HALF ? 8 : NB * 16;  // columns owned by the workgroup
   constexpr int U = NB == 1 ? 16 : (NB == 2 ? 8 : (NB <= 4 ? 4 : 2));  // k-blocks per batch
   __shared__ float s_red[W * NB * 128];
@@ -69,6 +73,18 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   const int g = blockIdx.x;                 // workgroup: stamps and partial outputs
   const int gb = HALF ? g >> 1 : g;         // column group of the packed weights
   const int hc = HALF ? (g & 1) * 8 : 0;    // first column of the half within its block
+  constexpr bool PAIRED = EPI == EPI_QKV || EPI == EPI_SILU;  // epilogues on column pairs
+  constexpr int NBF = SLICE ? NB - 1 : NB;  // whole 16-column blocks of the workgroup
+  const int cw = SLICE ? a.slice_cols : 0;  // columns of a slice
+  const int tcols = SLICE ? cw - 16 * NBF : 0;  // live columns of its partial block
+  // column c of the workgroup (block c / 16, MFMA column c % 16) holds an output
+  auto live_col = [&](int c) -> bool {
+    if constexpr (!SLICE) return true;
+    else if constexpr (PAIRED) return (c >> 4) < NBF || (c & 7) < (tcols >> 1);
+    else return c < cw;
+  };
+  // first pair (RoPE pair, gate/up feature) of the workgroup
+  const int pair0 = SLICE ? g * (cw >> 1) : gb * NB * 8;
   int n_rows = rows->n_rows;
   int row_base = 0;
   if (a.last_row_only) {
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
 
   // Epilogue operands that do not depend on the product, fetched now so their
   // latency hides behind the weight stream.
-  const int col0 = gb * NB * 16 + hc;
+  const int col0 = SLICE ? g * cw : gb * NB * 16 + hc;
   // residual epilogue: item i = tid + i*W*64 is (row i / YW, column i % YW)
   constexpr int RI = EPI == EPI_RESID ? (kMaxRows * YW + W * 64 - 1) / (W * 64) : 1;
   float pre_x[RI], pre_gn[RI];
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
     pre_x[i] = 0.0f;
     pre_gn[i] = 0.0f;
     const int idx = tid + i * W * 64;
-    if (EPI == EPI_RESID && idx < kMaxRows * YW) {  // resid rows exist for all kMaxRows rows
+    if (EPI == EPI_RESID && idx < kMaxRows * YW && live_col(idx % YW)) {  // resid rows exist for all kMaxRows rows
       const int k = col0 + idx % YW;
       pre_x[i] = a.resid[(size_t)(idx / YW) * a.ldr + k];
       pre_gn[i] = bf16_to_f32(a.gain_next[k]);
@@ -121,14 +137,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   if constexpr (EPI == EPI_QKV) {
     const int m = tid / YW, c = tid % YW;
     const int pos = rows->pos0 + m;
-    const int b = gb * NB + c / 16, w = c % 16;
-    const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16, half_hd = a.head_dim / 2;
+    const int P = pair0 + (c >> 4) * 8 + (c & 7);  // pair of the projection's q, k, v pairs
+    const int q_pairs = a.q_dim / 2, qk_pairs = (a.q_dim + a.kv_dim) / 2, half_hd = a.head_dim / 2;
     if (m < kMaxRows && pos < a.max_seq) {
       pre_blk = a.block_table[pos / kBlock];
-      if (b < q_blocks + k_blocks) {
-        const int bl = b < q_blocks ? b : b - q_blocks;
-        pre_rope = a.rope[(size_t)pos * half_hd + (bl * 8 + (w & 7)) % half_hd];
-      }
+      if (P < qk_pairs && live_col(c)) pre_rope = a.rope[(size_t)pos * half_hd + (P < q_pairs ? P : P - q_pairs) % half_hd];
     }
   }
 
@@ -141,13 +154,22 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Ap), 0, Kb * 1024, 0x00020000);
   const uint32_t a_off = aload ? apack_lane_offset(lane) : 0x80000000u;
-  const uint4* wp = (const uint4*)Wp + (size_t)gb * Kb * NB * 64 + lane;
+  // 16-byte units of one workgroup's weights
+  const size_t g_u4 = SLICE ? (size_t)Kb * (NBF * 64 + 4 * tcols) : (size_t)Kb * NB * 64;
+  const uint4* wp = (const uint4*)Wp + (size_t)(SLICE ? g : gb) * g_u4 + lane;
   // Half blocks: lanes of the other half's columns read at an out-of-range
   // offset of a buffer resource over the group's weights (zero, no fetch);
   // aux bit 1 is the non-temporal hint.
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint4*>(wp - lane), 0, HALF ? Kb * NB * 1024 : 0, 0x00020000);
   const uint32_t w_off = (unsigned)((lane & 15) - hc) < 8u ? (uint32_t)lane * 16 : 0x80000000u;
+  // Slices: the partial block's k-blocks follow the whole blocks, 4 * tcols
+  // lanes each; dead lanes read at an out-of-range offset (zero, no fetch).
+  int t_ci = 0;
+  const bool t_live = SLICE && slice_tail_lane(lane, tcols, PAIRED, &t_ci);
+  const __amdgpu_buffer_rsrc_t rT = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(wp - lane + (size_t)Kb * NBF * 64), 0, SLICE ? Kb * 64 * tcols : 0, 0x00020000);
+  const uint32_t t_off = t_live ? (uint32_t)t_ci * 16 : 0x80000000u;
   floatx4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -172,8 +194,12 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
               rW, (int)(w_off < 0x80000000u ? w_off + (uint32_t)((kb + u) * NB + j) * 1024 : w_off), 0,
               2);
           wv[u][j] = make_uint4(v.x, v.y, v.z, v.w);
+        } else if (j < NBF) {
+          wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NBF + j) * 64);
         } else {
-          wv[u][j] = load_stream(wp + ((size_t)(kb + u) * NB + j) * 64);
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+              rT, (int)(t_off < 0x80000000u ? t_off + (uint32_t)(kb + u) * 64 * tcols : t_off), 0, 2);
+          wv[u][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
@@ -274,7 +300,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
     for (int i = 0; i < RI; ++i) {
       const int idx = tid + i * W * 64, m = idx / YW, c = idx % YW;
       float sq = 0.0f;
-      if (idx < kMaxRows * YW && m < n_rows) {
+      if (idx < kMaxRows * YW && m < n_rows && live_col(c)) {
         const float x = pre_x[i] + col_sum(src_row(m), c + hc) * row_scale(m);
         a.resid[(size_t)m * a.ldr + col0 + c] = x;
         apack_store1(a.Ap_out, m, col0 + c, x * pre_gn[i]);
@@ -305,29 +331,30 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
     // features 8b .. 8b+7; one feature per thread
     for (int idx = tid; idx < n_rows * NB * 8; idx += W * 64) {
       const int m = idx / (NB * 8), f = idx % (NB * 8), j = f >> 3, e = f & 7;
+      if (SLICE && f >= (cw >> 1)) continue;
       const float sc = row_scale(m);
       const float gt = col_sum(src_row(m), j * 16 + e) * sc;
       const float up = col_sum(src_row(m), j * 16 + 8 + e) * sc;
-      apack_store1(a.Ap_out, m, (gb * NB + j) * 8 + e, gt / (1.0f + expf(-gt)) * up);
+      apack_store1(a.Ap_out, m, pair0 + f, gt / (1.0f + expf(-gt)) * up);
     }
   } else if constexpr (EPI == EPI_QKV) {
-    const int q_blocks = a.q_dim / 16, k_blocks = a.kv_dim / 16;
+    const int q_pairs = a.q_dim / 2, qk_pairs = (a.q_dim + a.kv_dim) / 2;
     const int half_hd = a.head_dim / 2;
     const int G = div_small(a.q_dim, rcp_small(a.kv_dim)), n_es = (a.head_dim + 31) / 32;
     const float inv_half = rcp_small(half_hd), inv_hd = rcp_small(a.head_dim), inv_G = rcp_small(G);
     const int pos0 = rows->pos0;
     for (int idx = tid; idx < n_rows * YW; idx += W * 64) {
       const int m = idx / YW, c = idx % YW;
-      const int b = gb * NB + c / 16, w = c % 16;
+      const int w = c & 15, hf = w >> 3;
+      const int P = pair0 + (c >> 4) * 8 + (w & 7);
       const int pos = pos0 + m;
-      if (pos >= a.max_seq) continue;
+      if (pos >= a.max_seq || !live_col(c)) continue;
       const float sc = row_scale(m);
       const float mine = col_sum(src_row(m), c) * sc;
-      if (b < q_blocks + k_blocks) {
+      if (P < qk_pairs) {
         // pair-interleaved block: columns w and w^8 are the two halves of one pair
-        const bool is_q = b < q_blocks;
-        const int bl = is_q ? b : b - q_blocks;
-        const int pair = bl * 8 + (w & 7), hf = w >> 3;
+        const bool is_q = P < q_pairs;
+        const int pair = is_q ? P : P - q_pairs;
         const int head = div_small(pair, inv_half), jj = pair - head * half_hd;
         const float other = col_sum(src_row(m), c ^ 8) * sc;
         // (cos, sin) of pos * theta^(-2jj/hd); this thread's first item was prefetched
@@ -349,7 +376,9 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
               f32_to_bf16_rne(val - bf16_to_f32(hb));
         }
       } else {
-        const int f0 = (b - q_blocks - k_blocks) * 16 + w;
+        // v: pair pv covers features w and w + 8 of block pv / 8
+        const int pv = P - qk_pairs;
+        const int f0 = (pv >> 3) * 16 + (pv & 7) + 8 * hf;
         const int head = div_small(f0, inv_hd), dim = f0 - head * a.head_dim;
         const int blk = idx == tid ? pre_blk : a.block_table[pos / kBlock];
         const uint16_t hb = f32_to_bf16_rne(mine);
@@ -365,23 +394,30 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   }
 }
 
-template <int NB, int W, bool HALF = false>
+template <int NB, int W, bool HALF = false, bool SLICE = false>
 static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.n_groups * (HALF ? 2 : 1)), block(W * 64);
-  if constexpr (HALF) {
+  if constexpr (SLICE) {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if constexpr (HALF) {
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -389,6 +425,19 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.slice_cols != sh.slice) return hipErrorInvalidValue;
+  if (sh.slice) {
+    // nb - 1 whole blocks and a partial one; pairs stay whole
+    const bool paired = epi == EPI_QKV || epi == EPI_SILU;
+    if (sh.half || sh.waves != 4 || sh.slice <= 16 * (sh.nb - 1) || sh.slice >= 16 * sh.nb ||
+        (paired && sh.slice % 2))
+      return hipErrorInvalidValue;
+    if (sh.nb == 1) return launch_epi<1, 4, false, true>(epi, a, s);
+    if (sh.nb == 2) return launch_epi<2, 4, false, true>(epi, a, s);
+    if (sh.nb == 3) return launch_epi<3, 4, false, true>(epi, a, s);
+    if (sh.nb == 4) return launch_epi<4, 4, false, true>(epi, a, s);
+    return hipErrorInvalidValue;
+  }
   if (sh.half) {
     if (sh.nb != 1) return hipErrorInvalidValue;
     if (sh.waves == 4) return launch_epi<1, 4, true>(epi, a, s);
@@ -410,10 +459,14 @@ hipError_t launch_gemm(GemmShape sh, int epi, const GemmArgs& a, hipStream_t s) 
 }
 
 // ------------------------------------------------------------------ pack --
+// row_ptr lists the workgroups' column slots, (g * nb + j) * 16 + w; with
+// column slices (cw > 0) the dead slots of the last block are not stored.
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* const* row_ptr, int K, int nb,
-                                                   int n_groups, uint16_t* out) {
+                                                   int n_groups, int cw, int paired, uint16_t* out) {
   const int Kb = K / 32;
   const size_t total = (size_t)n_groups * Kb * nb * 64;
+  const int nbf = cw ? nb - 1 : nb, t = cw ? cw - 16 * nbf : 0;
+  const size_t per_g = (size_t)Kb * (nbf * 64 + 4 * t);  // 16-byte units per workgroup
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int lane = (int)(idx % 64);
@@ -422,20 +475,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* const* row_pt
     const size_t g = idx / (64 * (size_t)nb * Kb);
     const size_t n = (g * nb + j) * 16 + (lane & 15);
     const int k = kb * 32 + (lane >> 4) * 8;
+    size_t dst;
+    if (j < nbf) {
+      dst = g * per_g + ((size_t)kb * nbf + j) * 64 + lane;
+    } else {
+      int ci;
+      if (!slice_tail_lane(lane, t, paired != 0, &ci)) continue;
+      dst = g * per_g + (size_t)Kb * nbf * 64 + (size_t)kb * 4 * t + ci;
+    }
     const uint16_t* src = row_ptr[n];
     uint4 v = make_uint4(0, 0, 0, 0);
     if (src != nullptr) v = *(const uint4*)(src + k);
-    ((uint4*)out)[idx] = v;
+    ((uint4*)out)[dst] = v;
   }
 }
 
-hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, uint16_t* out,
-                       hipStream_t s) {
+hipError_t launch_pack(const uint16_t* const* row_ptr, int K, int nb, int n_groups, int slice_cols,
+                       int paired, uint16_t* out, hipStream_t s) {
+  if (slice_cols && (slice_cols <= 16 * (nb - 1) || slice_cols >= 16 * nb || (paired && slice_cols % 2)))
+    return hipErrorInvalidValue;
   const size_t total = (size_t)n_groups * (K / 32) * nb * 64;
   size_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, row_ptr, K, nb, n_groups,
-                     out);
+                     slice_cols, paired, out);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ struct Mat {
   uint16_t* p = nullptr;  // packed (inside the model arena)
   GemmPlan plan;
   int K = 0, N = 0;
-  size_t elems() const { return (size_t)plan.n_groups * plan.Kb * plan.shape.nb * 64 * 8; }
+  size_t elems() const { return plan.packed_elems(); }
 };
 
 struct Model {
@@ -208,15 +208,47 @@ hipError_t dalloc(T** p, size_t n) {
   return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
 }
 
-// Packs one matrix from row pointers (host list) into dst.
-int pack_rows(spec_ctx* c, const std::vector<const uint16_t*>& rows, const Mat& m) {
-  if (rows.size() != (size_t)m.plan.n_groups * m.plan.shape.nb * 16)
-    return fail(c, SPEC_ERR_ARG, "internal: row list does not match the packing plan");
+// Packs one matrix from row pointers (host list, in the column order the
+// epilogues number columns in, null past N) into m.p.  Column slices take the
+// columns (or, for epilogues on column pairs, the pairs: columns w, w + 8 of a
+// 16-column block) in consecutive runs, one per workgroup.
+int pack_rows(spec_ctx* c, const std::vector<const uint16_t*>& virt, const Mat& m,
+              bool paired = false) {
+  const GemmPlan& pl = m.plan;
+  const int nb = pl.shape.nb, cw = pl.shape.slice;
+  const size_t n_slots = (size_t)pl.n_groups * nb * 16;
+  std::vector<const uint16_t*> rows;
+  if (!cw) {
+    if (virt.size() != n_slots)
+      return fail(c, SPEC_ERR_ARG, "internal: row list does not match the packing plan");
+    rows = virt;
+  } else {
+    rows.assign(n_slots, nullptr);
+    for (int g = 0; g < pl.n_groups; ++g)
+      for (int j = 0; j < nb; ++j)
+        for (int w = 0; w < 16; ++w) {
+          size_t vc;
+          if (paired) {
+            const int lp = j * 8 + (w & 7);
+            if (lp >= cw / 2) continue;
+            const size_t P = (size_t)g * (cw / 2) + lp;
+            vc = P / 8 * 16 + P % 8 + 8 * (w >> 3);
+          } else {
+            const int cc = j * 16 + w;
+            if (cc >= cw) continue;
+            vc = (size_t)g * cw + cc;
+          }
+          if (vc >= virt.size())
+            return fail(c, SPEC_ERR_ARG, "internal: row list does not cover the column slices");
+          rows[((size_t)g * nb + j) * 16 + w] = virt[vc];
+        }
+  }
   const uint16_t** drows = nullptr;
   HIPTRY(c, dalloc(&drows, rows.size()));
   hipError_t e = hipMemcpyAsync(drows, rows.data(), rows.size() * sizeof(void*),
                                 hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess) e = launch_pack(drows, m.K, m.plan.shape.nb, m.plan.n_groups, m.p, c->stream);
+  if (e == hipSuccess)
+    e = launch_pack(drows, m.K, nb, pl.n_groups, cw, paired ? 1 : 0, m.p, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   (void)hipFree(drows);
   HIPTRY(c, e);
@@ -232,18 +264,20 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   const int L = m.L, d = m.d;
   int n_cu = 0;
   HIPTRY(c, hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
-  // half blocks only where the epilogue keeps each column on its own (O, down)
-  auto mk = [n_cu](int N, int K, bool allow_half) {
+  // half blocks only where the epilogue keeps each column on its own (O,
+  // down); column slices by column there and by column pair for QKV and
+  // gate/up; neither for the LM head
+  auto mk = [n_cu](int N, int K, bool allow_half, int slice_kind) {
     Mat x;
     x.N = N; x.K = K;
-    x.plan = plan_gemm(N, 1, K, n_cu, allow_half);
+    x.plan = plan_gemm(N, 1, K, n_cu, allow_half, slice_kind);
     return x;
   };
-  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, d, false));
-  m.o.assign(L, mk(d, m.qd, true));
-  m.gu.assign(L, mk(2 * m.F, d, false));
-  m.dn.assign(L, mk(d, m.F, true));
-  m.lm = mk(m.V, d, false);
+  m.qkv.assign(L, mk(m.qd + 2 * m.kvd, d, false, kSlicePairs));
+  m.o.assign(L, mk(d, m.qd, true, kSliceCols));
+  m.gu.assign(L, mk(2 * m.F, d, false, kSlicePairs));
+  m.dn.assign(L, mk(d, m.F, true, kSliceCols));
+  m.lm = mk(m.V, d, false, kSliceNone);
   m.lm_shared = share_from && share_desc && md.lm_head == share_desc->lm_head &&
                 md.d_model == share_desc->d_model && md.vocab == share_desc->vocab;
   m.embed_shared = share_from && share_desc && md.embed == share_desc->embed &&
@@ -273,7 +307,10 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
   for (int l = 0; l < L; ++l) {
     // QKV: q and k rows in pair-interleaved order (columns w, w+8 of a block
     // are the halves j, j+hd/2 of one RoPE pair), then v rows in order.
-    rows.assign((size_t)m.qkv[l].plan.n_groups * m.qkv[l].plan.shape.nb * 16, nullptr);
+    auto slots = [](const Mat& x) {
+      return x.plan.shape.slice ? (size_t)x.N : (size_t)x.plan.n_groups * x.plan.shape.nb * 16;
+    };
+    rows.assign(slots(m.qkv[l]), nullptr);
     for (int p = 0; p < m.qd + 2 * m.kvd; ++p) {
       const uint16_t* src;
       if (p < m.qd + m.kvd) {
@@ -289,19 +326,19 @@ int build_model(spec_ctx* c, const spec_model_desc& md, Model& m, const Model* s
       }
       rows[p] = src;
     }
-    if (int r = pack_rows(c, rows, m.qkv[l])) return r;
-    rows.assign((size_t)m.o[l].plan.n_groups * m.o[l].plan.shape.nb * 16, nullptr);
+    if (int r = pack_rows(c, rows, m.qkv[l], true)) return r;
+    rows.assign(slots(m.o[l]), nullptr);
     for (int n = 0; n < d; ++n) rows[n] = wo + ((size_t)l * d + n) * m.qd;
     if (int r = pack_rows(c, rows, m.o[l])) return r;
     // gate/up: 16-column block b holds the gate rows of features 8b..8b+7
     // in its columns 0-7 and the up rows of the same features in 8-15
-    rows.assign((size_t)m.gu[l].plan.n_groups * m.gu[l].plan.shape.nb * 16, nullptr);
+    rows.assign(slots(m.gu[l]), nullptr);
     for (int n = 0; n < 2 * m.F; ++n) {
       const size_t f = (size_t)(n / 16) * 8 + (n % 8);
       rows[n] = ((n % 16) < 8 ? wg : wu) + ((size_t)l * m.F + f) * d;
     }
-    if (int r = pack_rows(c, rows, m.gu[l])) return r;
-    rows.assign((size_t)m.dn[l].plan.n_groups * m.dn[l].plan.shape.nb * 16, nullptr);
+    if (int r = pack_rows(c, rows, m.gu[l], true)) return r;
+    rows.assign(slots(m.dn[l]), nullptr);
     for (int n = 0; n < d; ++n) rows[n] = wdn + ((size_t)l * d + n) * m.F;
     if (int r = pack_rows(c, rows, m.dn[l])) return r;
   }
@@ -362,6 +399,7 @@ GemmArgs gemm_base(spec_ctx* c, const Mat& w, const uint16_t* ap) {
   GemmArgs a{};
   a.Wp = w.p;
   a.n_groups = w.plan.n_groups;
+  a.slice_cols = w.plan.shape.slice;
   a.Kb = w.plan.Kb;
   a.K = w.K;
   a.Ap = ap;
@@ -1074,7 +1112,7 @@ int spec_mat_create(const void* W_dev, int32_t N, int32_t K, spec_mat** out) {
   if (e == hipSuccess) e = dalloc(&drows, (size_t)N);
   if (e == hipSuccess)
     e = hipMemcpy(drows, rows.data(), (size_t)N * sizeof(void*), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = launch_pack(drows, K, m->nb, N / (16 * m->nb), m->Wp, nullptr);
+  if (e == hipSuccess) e = launch_pack(drows, K, m->nb, N / (16 * m->nb), 0, 0, m->Wp, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipFree(drows);
   if (e != hipSuccess) {

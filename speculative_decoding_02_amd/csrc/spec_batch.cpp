@@ -119,7 +119,7 @@ int pack_mat(spec_batch* c, const std::vector<const uint16_t*>& rows, const RMat
   BTRY(c, dalloc(&drows, rows.size()));
   hipError_t e = hipMemcpyAsync(drows, rows.data(), rows.size() * sizeof(void*),
                                 hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess) e = launch_pack(drows, m.K, m.nb, m.N / (16 * m.nb), m.p, c->stream);
+  if (e == hipSuccess) e = launch_pack(drows, m.K, m.nb, m.N / (16 * m.nb), 0, 0, m.p, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   (void)hipFree(drows);
   BTRY(c, e);

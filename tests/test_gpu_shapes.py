@@ -13,8 +13,9 @@ sizes), with fewer layers so the fp64 oracle finishes in seconds:
     target's embedding and LM head;
   * a long context: 1500-token prompt through 32/8 x 128 attention;
   * a d_model-8192 target with 256-dim heads and a draft with 32-dim heads,
-    and a d_model-16384 target (GEMM and attention variants the pairs above
-    do not reach);
+    a d_model-16384 target, and a d_model-10240 target whose QKV, gate/up
+    and O projections run as column slices (GEMM and attention variants the
+    pairs above do not reach);
   * the benchmark's own workload at full size (sampled outputs, below).
 
 Every round is teacher-forced: draft rows (1e-4) and samples (bit-exact),
@@ -102,9 +103,10 @@ def test_wide_model_and_narrow_heads():
     whose O and down projections take two column blocks per workgroup (each
     residual row spans two 16-lane groups, whose sums of squares meet in LDS),
     with 256-dim heads (eight 32-dim steps in the attention partial, 32 lanes
-    per chunk group in the merge); and a draft with 32-dim heads (one step,
-    4 lanes per chunk group).  The 200-token prompt gives every head seven
-    chunks to merge."""
+    per chunk group in the merge) and a QKV projection in column slices of
+    24 columns, two workgroups per CU; and a draft with 32-dim heads (one
+    step, 4 lanes per chunk group).  The 200-token prompt gives every head
+    seven chunks to merge."""
     t = synth.ModelConfig("wide-d8192-hd256-1L", 1, 8192, 32, 8, 256, 1024, 1024)
     d = synth.ModelConfig("hd32-draft-1L", 1, 512, 16, 4, 32, 1024, 1024)
     run_case(t, d, prompt_len=200, K=4, rounds=2, greedy=False)
@@ -117,6 +119,20 @@ def test_very_wide_residual():
     t = synth.ModelConfig("wide-d16384-1L", 1, 16384, 16, 4, 64, 512, 1024)
     d = synth.ModelConfig("small-draft-1L", 1, 256, 8, 2, 32, 512, 1024)
     run_case(t, d, prompt_len=40, K=3, rounds=2, greedy=False)
+
+
+def test_column_slice_shapes():
+    """Column-slice plans the workload pairs do not reach (the 31B-shaped
+    pair covers slices of two and three blocks for QKV, two for O and down,
+    four for gate/up; its 4B-shaped draft one for down): a d_model-10240
+    target whose QKV projection (3584 columns) runs as 14-column slices --
+    seven RoPE pairs in the partial block, none whole -- its gate/up (3072
+    columns) as 12-column slices (six gate/up pairs), and its O projection
+    as 40-column slices (two whole blocks and 8 columns), each at >= 200 KB
+    per CU."""
+    t = synth.ModelConfig("slices-d10240-1L", 1, 10240, 20, 4, 128, 1536, 1024)
+    d = synth.ModelConfig("small-draft-1L", 1, 256, 8, 2, 32, 512, 1024)
+    run_case(t, d, prompt_len=40, K=4, rounds=2, greedy=False)
 
 
 def test_8b_bench_workload_sampled():
