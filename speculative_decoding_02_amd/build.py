@@ -11,7 +11,7 @@ OBJ = os.path.join(ROOT, "_build", "libspec")
 LIB = os.path.join(HERE, "libspec.so")
 RUNNER = os.path.join(HERE, "spec_run")   # native driver of the C ABI (no Python in the process)
 SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_accept.hip", "k_ngram.hip", "k_gemm_rows.hip",
-           "k_heads.hip", "k_batch.hip", "spec_api.cpp", "spec_batch.cpp"]
+           "k_gemm_wide.hip", "k_heads.hip", "k_batch.hip", "spec_api.cpp", "spec_batch.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SPEC_ARCH", "gfx950")
@@ -24,11 +24,14 @@ FLAGS = [
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Per-file additions: the wide rows GEMM keeps its MFMA accumulators in VGPRs
+# (with them in AGPRs the compiler copies every accumulator at each k-block).
+FILE_FLAGS = {"k_gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,7 +60,8 @@ def build_sanitized(verbose: bool = False) -> str:
 
     def comp(src):
         obj = os.path.join(SAN_OBJ, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *SAN_FLAGS, "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

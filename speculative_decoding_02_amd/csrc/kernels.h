@@ -169,6 +169,9 @@ inline size_t rows_partials(int M, int N, int K) {
   return S > 1 ? (size_t)S * M * N : 0;
 }
 hipError_t launch_gemm_rows(const RowsGemmArgs& a, hipStream_t s);
+// The wide kernel (k_gemm_wide.hip) for RT > 1 row tiles and N % kRowsWideCols == 0,
+// with its slice sum unless a.defer_sum; the operand is already packed.
+hipError_t launch_gemm_wide(const RowsGemmArgs& a, int RT, int ldy, hipStream_t s);
 
 // ------------------------------------------------------ n-gram drafter --
 constexpr int kNgramMaxN = 8;   // longest key searched
