@@ -4,9 +4,10 @@ verify rows), against numpy's fp64 product of the same bf16 weights.
 
 The bound is the arithmetic's own: activations enter as bf16 high and low
 parts (|x - hi - lo| <= 2^-17 |x|), bf16 x bf16 products are exact in fp32,
-and fp32 accumulation over K terms (plus the split-K and hi/lo sums) adds at
-most (K + 8) 2^-24 of sum |x w| -- so every output must satisfy
-|y - ref| <= (2^-16 + (K + 8) 2^-24) * sum_k |x_k w_nk|."""
+and fp32 accumulation of the K high-part and K low-part products (the wide
+kernel sums both in one accumulator; the narrow one adds the two at the end)
+plus the split-K sums adds at most (2K + 8) 2^-24 of sum |x w| -- so every
+output must satisfy |y - ref| <= (2^-16 + (2K + 8) 2^-24) * sum_k |x_k w_nk|."""
 import numpy as np
 import pytest
 
@@ -29,7 +30,7 @@ def _case(N, K, Ms, seed):
         y = Y.cpu().numpy().astype(np.float64)
         X64 = X.numpy().astype(np.float64)
         ref = X64 @ W64.T
-        bound = (2.0 ** -16 + (K + 8) * 2.0 ** -24) * (np.abs(X64) @ np.abs(W64).T)
+        bound = (2.0 ** -16 + (2 * K + 8) * 2.0 ** -24) * (np.abs(X64) @ np.abs(W64).T)
         err = np.abs(y - ref)
         assert np.all(np.isfinite(y)), M
         assert np.all(err <= bound), (M, float((err / bound).max()))
@@ -41,6 +42,12 @@ def test_rows_narrow():
 
 def test_rows_wide_two_blocks_per_workgroup():
     _case(12288, 512, [1, 7, 33, 128], seed=2)
+
+
+def test_rows_wide_unsplit():
+    # 192 column groups of 128: the wide kernel stores Y itself (no K split);
+    # every row-tile count, with the last 16-row tile partly filled
+    _case(24576, 256, [9, 17, 40, 100, 128], seed=3)
 
 
 def test_rows_errors():
