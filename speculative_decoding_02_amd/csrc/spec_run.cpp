@@ -8,6 +8,14 @@
 //
 //   spec_run [--pair 8b|1.3b|toy] [--k K] [--prompt N] [--rounds R]
 //            [--warmup W] [--greedy] [--no-graphs] [--copy-mib M]
+//   spec_run --gemm-rows M1,M2,... [--gemm-matrix gate|down|qkv] [--rounds R]
+//
+// --gemm-rows runs the batched-verify GEMM (spec_mat_mul) instead of the
+// decode loop: the 8B-shaped gate/up (28672 x 4096), down (4096 x 14336) and
+// QKV (6144 x 4096) matrices, each in enough copies (>= 1 GiB) that every
+// launch streams its weights from HBM, R launches per copy and row count M,
+// one JSON line per (matrix, M) with the mean time per launch; --gemm-matrix
+// keeps the matrices whose name contains the given word.
 //
 // Weights are random, N(0, 0.02) per element (Box-Muller over a counter
 // hash), rounded to bf16; norm gains are 1; the prompt is uniform token ids.
@@ -64,6 +72,12 @@ __global__ void fill_normal_bf16(uint16_t* p, size_t n, uint64_t tag, float std_
     b += 0x7FFF + ((b >> 16) & 1);  // round to nearest even
     p[i] = (uint16_t)(b >> 16);
   }
+}
+
+__global__ void fill_uniform_f32(float* p, size_t n, uint64_t tag) {  // (-1, 1)
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = (float)(mix64(tag * 0x100000001b3ull + i) >> 40) * (2.0f / 16777216.0f) - 1.0f;
 }
 
 __global__ void fill_const_bf16(uint16_t* p, size_t n, uint16_t v) {
@@ -135,7 +149,8 @@ void make_model(Weights& w, const Shape& s, uint64_t seed, int share, const spec
 void usage() {
   fprintf(stderr,
           "usage: spec_run [--pair 8b|1.3b|toy] [--k K] [--prompt N] [--rounds R] [--warmup W]\n"
-          "                [--greedy] [--no-graphs] [--copy-mib M]\n");
+          "                [--greedy] [--no-graphs] [--copy-mib M]\n"
+          "       spec_run --gemm-rows M1,M2,... [--gemm-matrix gate|down|qkv] [--rounds R]\n");
   exit(2);
 }
 
@@ -147,11 +162,62 @@ int check(int rc, spec_ctx* ctx, const char* what) {
   return rc;
 }
 
+// The batched-verify GEMM over row counts Ms (see the header).
+int gemm_rows(const std::vector<int>& Ms, int reps, const std::string& only) {
+  struct Shp { const char* name; int N, K; };
+  const Shp shapes[] = {{"8b gate/up", 28672, 4096}, {"8b down", 4096, 14336}, {"8b qkv", 6144, 4096}};
+  int max_m = 1;
+  for (int M : Ms) max_m = std::max(max_m, M);
+  float *X, *Y;
+  HCK(hipMalloc(&X, (size_t)max_m * 14336 * sizeof(float)));
+  HCK(hipMalloc(&Y, (size_t)max_m * 28672 * sizeof(float)));
+  hipLaunchKernelGGL(fill_uniform_f32, dim3(1024), dim3(256), 0, 0, X, (size_t)max_m * 14336, 77);
+  HCK(hipGetLastError());
+  hipEvent_t e0, e1;
+  HCK(hipEventCreate(&e0));
+  HCK(hipEventCreate(&e1));
+  for (const Shp& sh : shapes) {
+    if (!only.empty() && std::string(sh.name).find(only) == std::string::npos) continue;
+    const size_t bytes = (size_t)sh.N * sh.K * 2;
+    const int copies = std::max<int>(2, (int)(((size_t)1 << 30) / bytes + 1));
+    std::vector<uint16_t*> W(copies);
+    std::vector<spec_mat*> mats(copies);
+    for (int c = 0; c < copies; ++c) {
+      HCK(hipMalloc(&W[c], bytes));
+      hipLaunchKernelGGL(fill_normal_bf16, dim3(4096), dim3(256), 0, 0, W[c], bytes / 2, 500 + c, 0.02f);
+      HCK(hipGetLastError());
+      check(spec_mat_create(W[c], sh.N, sh.K, &mats[c]), nullptr, "spec_mat_create");
+      HCK(hipFree(W[c]));  // the packed copy is the library's
+    }
+    for (int M : Ms) {
+      for (int c = 0; c < copies; ++c) check(spec_mat_mul(mats[c], X, M, Y, nullptr), nullptr, "spec_mat_mul");
+      HCK(hipEventRecord(e0, nullptr));
+      const int n = reps * copies;
+      for (int i = 0; i < n; ++i) check(spec_mat_mul(mats[i % copies], X, M, Y, nullptr), nullptr, "spec_mat_mul");
+      HCK(hipEventRecord(e1, nullptr));
+      HCK(hipEventSynchronize(e1));
+      float ms = 0.0f;
+      HCK(hipEventElapsedTime(&ms, e0, e1));
+      printf("{\"matrix\": \"%s\", \"N\": %d, \"K\": %d, \"M\": %d, \"launches\": %d, \"us_per_launch\": %.2f}\n",
+             sh.name, sh.N, sh.K, M, n, ms * 1e3f / n);
+      fflush(stdout);
+    }
+    for (spec_mat* m : mats) check(spec_mat_destroy(m), nullptr, "spec_mat_destroy");
+  }
+  HCK(hipEventDestroy(e0));
+  HCK(hipEventDestroy(e1));
+  HCK(hipFree(X));
+  HCK(hipFree(Y));
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
   std::string pair = "8b";
   int K = 4, prompt_len = -1, rounds = 20, warmup = 3, greedy = 0, graphs = 1, copy_mib = 0;
+  std::vector<int> gemm_ms;
+  std::string gemm_only;
   for (int i = 1; i < argc; ++i) {
     const std::string a = argv[i];
     auto next = [&]() -> const char* {
@@ -166,7 +232,21 @@ int main(int argc, char** argv) {
     else if (a == "--greedy") greedy = 1;
     else if (a == "--no-graphs") graphs = 0;
     else if (a == "--copy-mib") copy_mib = atoi(next());
+    else if (a == "--gemm-rows") {
+      for (const char* t = next(); *t;) {
+        gemm_ms.push_back(atoi(t));
+        while (*t && *t != ',') ++t;
+        if (*t == ',') ++t;
+      }
+    } else if (a == "--gemm-matrix") gemm_only = next();
     else usage();
+  }
+  if (!gemm_ms.empty()) {
+    for (int M : gemm_ms)
+      if (M < 1 || M > 128) usage();
+    if (rounds < 1) usage();
+    HCK(hipSetDevice(0));
+    return gemm_rows(gemm_ms, rounds, gemm_only);
   }
   Shape ts, ds;
   int dshare;
