@@ -81,3 +81,17 @@ def test_noalloc_size_limit_needs_no_device(lib):
     assert b"scratch" in lib.spec_last_error(None)
     assert f(None, None, None, 0, 0, 10, ctypes.c_uint64(0), None, ctypes.c_uint64(0), 0, None,
              None, None) == sd.SPEC_ERR_ARG
+
+
+def test_native_driver_rejects_bad_arguments():
+    """spec_run (the native driver of the C ABI) validates its arguments
+    before it touches a device: usage text and exit status 2."""
+    import subprocess
+    exe = os.path.join(ROOT, "speculative_decoding_02_amd", "spec_run")
+    if not os.path.exists(exe):
+        pytest.skip("spec_run is not built")
+    for args in (["--gemm-rows", "0"], ["--gemm-rows", "129"], ["--gemm-rows", "16", "--rounds", "0"],
+                 ["--k", "0"], ["--pair", "nope"], ["--no-such-flag"]):
+        r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 2, (args, r.returncode, r.stderr)
+        assert "usage: spec_run" in r.stderr

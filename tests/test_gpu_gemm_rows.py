@@ -63,3 +63,22 @@ def test_rows_errors():
     with pytest.raises(sd.SpecError) as e:
         sd.spec_mat_create(torch.zeros(24, 64, dtype=torch.bfloat16, device="cuda"))
     assert e.value.code == sd.SPEC_ERR_ARG
+
+
+def test_native_driver_gemm_sweep():
+    """spec_run --gemm-rows drives spec_mat_mul natively (the process the
+    counter profiles are taken on): one JSON line per (matrix, M) with a
+    finite, positive time per launch."""
+    import json
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "speculative_decoding_02_amd", "spec_run")
+    r = subprocess.run([exe, "--gemm-rows", "5,16,128", "--gemm-matrix", "qkv", "--rounds", "1"],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr
+    lines = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    assert [(d["matrix"], d["M"]) for d in lines] == [("8b qkv", 5), ("8b qkv", 16), ("8b qkv", 128)]
+    for d in lines:
+        assert (d["N"], d["K"]) == (6144, 4096) and d["launches"] > 0
+        assert 0.0 < d["us_per_launch"] < 1e5
