@@ -135,6 +135,17 @@ def test_column_slice_shapes():
     run_case(t, d, prompt_len=40, K=4, rounds=2, greedy=False)
 
 
+def test_column_slices_two_per_cu_residual():
+    """d_model 17408: the O and down projections (residual epilogue, >= 200 KB
+    per CU) take column slices of 34 columns, two workgroups per CU (512):
+    two whole blocks and a partial block of 2 live columns each, 512 partial
+    sums of squares for the next RMSNorm (the most a four-wave consumer
+    folds); the QKV projection runs as 24-column pair slices."""
+    t = synth.ModelConfig("slices-d17408-1L", 1, 17408, 32, 8, 128, 2048, 1024)
+    d = synth.ModelConfig("small-draft-1L", 1, 256, 8, 2, 32, 512, 1024)
+    run_case(t, d, prompt_len=24, K=3, rounds=2, greedy=False)
+
+
 def test_8b_bench_workload_sampled():
     """The benchmark's workload at full size: the 8B-shaped target and
     1B-shaped draft at full depth, bench.py's 1024-token prompt, K = 4,
