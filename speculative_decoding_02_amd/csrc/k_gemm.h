@@ -34,6 +34,12 @@ struct GemmArgs {
   // A operand: packed rows (see apack_index) of length K
   const uint16_t* Ap;
   const PassRows* rows;
+  // Rows of the pass when they are fixed at the time the launch is recorded
+  // (a verify pass: K + 1; a later draft step: 1), so the kernel need not
+  // wait for the pass descriptor before its first loads; 0: read n_rows from
+  // the descriptor.  Only for passes whose descriptor would give the same
+  // count (or 0 after a recorded error, when the pass's results are void).
+  int fixed_rows;
   int last_row_only;  // use only row n_rows-1 (written as output row 0)
   // RMSNorm of the consumer: y[m][.] *= 1/sqrt(sum_g ssq[g][m] / K + eps)
   const float* ssq;   // [ssq_groups][8] or null (no norm)

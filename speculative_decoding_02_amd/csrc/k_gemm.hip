@@ -50,13 +50,19 @@ SPEC_DEVICE uint4 load_stream(const uint4* p) {
 // HALF (NB == 1): workgroup 2b + h owns columns 8h .. 8h + 7 of block b.
 // SLICE: workgroup g owns the column slice g (a.slice_cols columns, see
 // GemmShape): NB - 1 whole blocks and a compacted partial block.
-// The pass descriptor, weights, activations and K lead the arguments as
-// scalars: they are what the first loads need, and leading scalar arguments
-// can arrive preloaded in SGPRs instead of through a load of the argument
-// segment.
+// Everything the first weight and activation loads need leads the arguments
+// as scalars (preloaded in SGPRs with the wave instead of loaded from the
+// argument segment), and the row count is one of them whenever the pass's
+// row count is fixed when the launch is recorded (fixed_rows > 0; 0: read it
+// from the pass descriptor).  In most instances the first batch of loads is
+// issued before anything else, so it waits on no memory access; the norm
+// partials and epilogue operands are fetched behind it and the partials are
+// folded only after the main loop.
 template <int NB, int W, int EPI, bool HALF, bool SLICE>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, const uint16_t* Wp,
-                                                     const uint16_t* Ap, int Kb, GemmArgs a) {
+                                                     const uint16_t* Ap, const float* ssq, int Kb,
+                                                     int fixed_rows, int ssq_groups, int slice_cols,
+                                                     int last_row_only, GemmArgs a) {
   static_assert(!HALF || (NB == 1 && EPI != EPI_SILU && EPI != EPI_QKV),
                 "half blocks split column pairs of the SiLU and RoPE epilogues");
   static_assert(!SLICE || (!HALF && (EPI == EPI_RESID || EPI == EPI_QKV || EPI == EPI_SILU)),
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   const int hc = HALF ? (g & 1) * 8 : 0;    // first column of the half within its block
   constexpr bool PAIRED = EPI == EPI_QKV || EPI == EPI_SILU;  // epilogues on column pairs
   constexpr int NBF = SLICE ? NB - 1 : NB;  // whole 16-column blocks of the workgroup
-  const int cw = SLICE ? a.slice_cols : 0;  // columns of a slice
+  const int cw = SLICE ? slice_cols : 0;    // columns of a slice
   const int tcols = SLICE ? cw - 16 * NBF : 0;  // live columns of its partial block
   // column c of the workgroup (block c / 16, MFMA column c % 16) holds an output
   auto live_col = [&](int c) -> bool {
@@ -85,70 +91,18 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   };
   // first pair (RoPE pair, gate/up feature) of the workgroup
   const int pair0 = SLICE ? g * (cw >> 1) : gb * NB * 8;
-  int n_rows = rows->n_rows;
+  int n_rows = fixed_rows;
+  if (n_rows <= 0) n_rows = rows->n_rows;
   int row_base = 0;
-  if (a.last_row_only) {
+  if (last_row_only) {
     row_base = n_rows - 1;
     n_rows = n_rows > 0 ? 1 : 0;
   }
 
-  // Row scale of the consumer's RMSNorm.  The producer's partial sums of
-  // squares are spread over all threads (thread t: row t%8, partials
-  // q = t/8, t/8 + P, ...), loaded before the main loop so their latency
-  // hides behind the weight stream, and folded in a fixed order after it.
-  constexpr int P = W * 64 / kMaxRows;
-  constexpr int kMaxSsq = kGemmMaxSsqPerThread;  // ssq_groups <= P * kMaxSsq
-  // The loads are unconditional (clamped indices) so they are issued without
-  // waiting for anything; entries outside the pass are dropped afterwards.
-  float ssq_part = 0.0f;
-  if (a.ssq != nullptr) {
-    const int m = tid % kMaxRows, p0 = tid / kMaxRows;
-    const int mr = a.last_row_only ? row_base : m;  // row of the producer's partials
-    float v[kMaxSsq];
-#pragma unroll
-    for (int i = 0; i < kMaxSsq; ++i) {
-      const int q = p0 + i * P;
-      v[i] = a.ssq[(q < a.ssq_groups ? q : 0) * kMaxRows + (mr & (kMaxRows - 1))];
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxSsq; ++i)
-      ssq_part += (p0 + i * P < a.ssq_groups && m < n_rows) ? v[i] : 0.0f;
-  }
-
-  // Epilogue operands that do not depend on the product, fetched now so their
-  // latency hides behind the weight stream.
-  const int col0 = SLICE ? g * cw : gb * NB * 16 + hc;
-  // residual epilogue: item i = tid + i*W*64 is (row i / YW, column i % YW)
-  constexpr int RI = EPI == EPI_RESID ? (kMaxRows * YW + W * 64 - 1) / (W * 64) : 1;
-  float pre_x[RI], pre_gn[RI];
-#pragma unroll
-  for (int i = 0; i < RI; ++i) {
-    pre_x[i] = 0.0f;
-    pre_gn[i] = 0.0f;
-    const int idx = tid + i * W * 64;
-    if (EPI == EPI_RESID && idx < kMaxRows * YW && live_col(idx % YW)) {  // resid rows exist for all kMaxRows rows
-      const int k = col0 + idx % YW;
-      pre_x[i] = a.resid[(size_t)(idx / YW) * a.ldr + k];
-      pre_gn[i] = bf16_to_f32(a.gain_next[k]);
-    }
-  }
-  float2 pre_rope = make_float2(1.f, 0.f);
-  int pre_blk = 0;
-  if constexpr (EPI == EPI_QKV) {
-    const int m = tid / YW, c = tid % YW;
-    const int pos = rows->pos0 + m;
-    const int P = pair0 + (c >> 4) * 8 + (c & 7);  // pair of the projection's q, k, v pairs
-    const int q_pairs = a.q_dim / 2, qk_pairs = (a.q_dim + a.kv_dim) / 2, half_hd = a.head_dim / 2;
-    if (m < kMaxRows && pos < a.max_seq) {
-      pre_blk = a.block_table[pos / kBlock];
-      if (P < qk_pairs && live_col(c)) pre_rope = a.rope[(size_t)pos * half_hd + (P < q_pairs ? P : P - q_pairs) % half_hd];
-    }
-  }
-
-  // ---- main loop: this wave's share of K ---------------------------------
+  // ---- main-loop operands: this wave's share of K ------------------------
   const int kb0 = (Kb * wave) / W, kb1 = (Kb * (wave + 1)) / W;
   const int am = lane & 7;  // activation row of this lane (hi rows 0-7, lo rows 8-15)
-  const bool aload = a.last_row_only ? (am == row_base) : (am < n_rows);
+  const bool aload = last_row_only ? (am == row_base) : (am < n_rows);
   // A through a range-checked buffer resource: lanes of rows the pass does not
   // use read at an out-of-range offset, which returns zero without a fetch.
   const __amdgpu_buffer_rsrc_t rA =
@@ -176,9 +130,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   // Batches of k-blocks: all loads of a batch are issued before its first
   // MFMA (the scheduling barrier keeps the compiler from interleaving them),
   // so each wave keeps UB*NB KiB of weights in flight.
-  auto batch = [&](auto ub_tag, int kb) {
+  auto load_batch = [&](auto ub_tag, int kb, uint4* av, uint4 (*wv)[NB]) {
     constexpr int UB = decltype(ub_tag)::value;
-    uint4 av[UB], wv[UB][NB];
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -202,7 +155,9 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
           wv[u][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
       }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma_batch = [&](auto ub_tag, const uint4* av, const uint4 (*wv)[NB]) {
+    constexpr int UB = decltype(ub_tag)::value;
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
 #pragma unroll
@@ -211,10 +166,93 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
                                                          acc[j], 0, 0, 0);
     }
   };
+  auto batch = [&](auto ub_tag, int kb) {
+    constexpr int UB = decltype(ub_tag)::value;
+    uint4 av[UB], wv[UB][NB];
+    load_batch(ub_tag, kb, av, wv);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_batch(ub_tag, av, wv);
+  };
+  // The first full batch is issued now, ahead of every other load (where
+  // that is faster, see kPeel).
+  uint4 av0[U], wv0[U][NB];
+  // Issuing the first batch ahead of the prologue was measured per instance
+  // (rocprofv3, same box, graph-replayed rounds): it shortens the half-block,
+  // the four-and-more-block and the one-block QKV launches by 0.15-0.5 us and
+  // lengthens the whole-block residual launches with one block (8B-shaped O
+  // and down, +2.2 us) and the two-block QKV (+0.4 us), which therefore issue
+  // it in the loop as before.
+  constexpr bool kPeel = HALF || NB >= 4 || (EPI == EPI_QKV && NB == 1);
+  const bool peel = kPeel && kb0 + U <= kb1;  // wave-uniform
+  if (peel) load_batch(std::integral_constant<int, U>{}, kb0, av0, wv0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Row scale of the consumer's RMSNorm.  The producer's partial sums of
+  // squares are spread over all threads (thread t: row t%8, partials
+  // q = t/8, t/8 + P, ...), loaded here and folded in a fixed order after the
+  // main loop.  The loads are unconditional (clamped indices) so they wait
+  // for nothing; entries outside the pass are dropped when folded.
+  constexpr int P = W * 64 / kMaxRows;
+  constexpr int kMaxSsq = kGemmMaxSsqPerThread;  // ssq_groups <= P * kMaxSsq
+  const int ssq_m = tid % kMaxRows, ssq_p0 = tid / kMaxRows;
+  float ssq_v[kMaxSsq];
+  if (ssq != nullptr) {
+    const int mr = last_row_only ? row_base : ssq_m;  // row of the producer's partials
+#pragma unroll
+    for (int i = 0; i < kMaxSsq; ++i) {
+      const int q = ssq_p0 + i * P;
+      ssq_v[i] = ssq[(q < ssq_groups ? q : 0) * kMaxRows + (mr & (kMaxRows - 1))];
+    }
+  }
+
+  // Epilogue operands that do not depend on the product, fetched now so their
+  // latency hides behind the weight stream (the gains stay bf16 until used).
+  const int col0 = SLICE ? g * cw : gb * NB * 16 + hc;
+  // residual epilogue: item i = tid + i*W*64 is (row i / YW, column i % YW)
+  constexpr int RI = EPI == EPI_RESID ? (kMaxRows * YW + W * 64 - 1) / (W * 64) : 1;
+  float pre_x[RI];
+  uint16_t pre_gn[RI];
+#pragma unroll
+  for (int i = 0; i < RI; ++i) {
+    pre_x[i] = 0.0f;
+    pre_gn[i] = 0;
+    const int idx = tid + i * W * 64;
+    if (EPI == EPI_RESID && idx < kMaxRows * YW && live_col(idx % YW)) {  // resid rows exist for all kMaxRows rows
+      const int k = col0 + idx % YW;
+      pre_x[i] = a.resid[(size_t)(idx / YW) * a.ldr + k];
+      pre_gn[i] = a.gain_next[k];
+    }
+  }
+  float2 pre_rope = make_float2(1.f, 0.f);
+  int pre_blk = 0;
+  if constexpr (EPI == EPI_QKV) {
+    const int m = tid / YW, c = tid % YW;
+    const int pos = rows->pos0 + m;
+    const int P = pair0 + (c >> 4) * 8 + (c & 7);  // pair of the projection's q, k, v pairs
+    const int q_pairs = a.q_dim / 2, qk_pairs = (a.q_dim + a.kv_dim) / 2, half_hd = a.head_dim / 2;
+    if (m < kMaxRows && pos < a.max_seq) {
+      pre_blk = a.block_table[pos / kBlock];
+      if (P < qk_pairs && live_col(c)) pre_rope = a.rope[(size_t)pos * half_hd + (P < q_pairs ? P : P - q_pairs) % half_hd];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- main loop -----------------------------------------------------------
   int kb = kb0;
+  if (peel) {
+    mma_batch(std::integral_constant<int, U>{}, av0, wv0);
+    kb += U;
+  }
   for (; kb + U <= kb1; kb += U) batch(std::integral_constant<int, U>{}, kb);
   for (; kb + 4 <= kb1; kb += 4) batch(std::integral_constant<int, 4>{}, kb);
   for (; kb < kb1; ++kb) batch(std::integral_constant<int, 1>{}, kb);
+
+  float ssq_part = 0.0f;
+  if (ssq != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kMaxSsq; ++i)
+      ssq_part += (ssq_p0 + i * P < ssq_groups && ssq_m < n_rows) ? ssq_v[i] : 0.0f;
+  }
 
   // ---- hi + lo rows, then the waves' partial sums in wave order ----------
   // MFMA output: lane l, element r is (row 4*(l/16)+r, column l%16); lanes
@@ -247,7 +285,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   // partials: output row m (MFMA row mm, which differs only with
   // last_row_only) and column cb of the workgroup's NB*16 block columns.
   auto row_scale = [&](int m) -> float {
-    if (a.ssq == nullptr || m >= n_rows) return 1.0f;
+    if (ssq == nullptr || m >= n_rows) return 1.0f;
     float ss = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) ss += s_ssq[w * kMaxRows + m];
@@ -260,7 +298,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
     for (int w = 0; w < W; ++w) v += s_red[((w * NB + j) * 32 + ln) * 4 + r];
     return v;
   };
-  auto src_row = [&](int m) { return a.last_row_only ? row_base : m; };
+  auto src_row = [&](int m) { return last_row_only ? row_base : m; };
 
   // ---- epilogues -------------------------------------------------------------
   if constexpr (EPI == EPI_STORE || EPI == EPI_LOGITS) {
@@ -303,7 +341,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
       if (idx < kMaxRows * YW && m < n_rows && live_col(c)) {
         const float x = pre_x[i] + col_sum(src_row(m), c + hc) * row_scale(m);
         a.resid[(size_t)m * a.ldr + col0 + c] = x;
-        apack_store1(a.Ap_out, m, col0 + c, x * pre_gn[i]);
+        apack_store1(a.Ap_out, m, col0 + c, x * bf16_to_f32(pre_gn[i]));
         sq = x * x;
       }
       // sum over the lanes of one row (up to 16), fixed order: quads, then
@@ -399,25 +437,25 @@ static hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.n_groups * (HALF ? 2 : 1)), block(W * 64);
   if constexpr (SLICE) {
     switch (epi) {
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, true>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
       default: return hipErrorInvalidValue;
     }
   } else if constexpr (HALF) {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_STORE, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_RESID, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<1, W, EPI_LOGITS, true, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
-      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.Kb, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_STORE, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_RESID, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_QKV: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_QKV, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_LOGITS, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
+      case EPI_SILU: hipLaunchKernelGGL((gemm_skinny<NB, W, EPI_SILU, false, false>), grid, block, 0, s, a.rows, a.Wp, a.Ap, a.ssq, a.Kb, a.fixed_rows, a.ssq_groups, a.slice_cols, a.last_row_only, a); break;
       default: return hipErrorInvalidValue;
     }
   }

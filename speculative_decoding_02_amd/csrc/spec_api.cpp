@@ -410,9 +410,11 @@ GemmArgs gemm_base(spec_ctx* c, const Mat& w, const uint16_t* ap) {
 // Per layer: QKV (norm scale, RoPE, KV append) -> attention -> O (+residual)
 // -> gate/up (norm scale, SiLU*up) -> down (+residual).  The sums of squares
 // for each RMSNorm alternate between two buffers so a producer never writes
-// the partials its own consumer-to-be is still to read.
-hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows, bool profile,
-                          bool stamp_last_down = false) {
+// the partials its own consumer-to-be is still to read.  fixed_rows: the
+// pass's row count when it is known as the launches are recorded (0: the
+// kernels read it from the pass descriptor).
+hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows, int fixed_rows,
+                          bool profile, bool stamp_last_down = false) {
   hipError_t e = hipSuccess;
   int ssq_groups = m.d / 64;  // produced by the embedding
   float* ssq_in = c->ssq_a;
@@ -420,6 +422,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
   for (int l = 0; l < m.L && e == hipSuccess; ++l) {
     // RMSNorm + QKV + RoPE + KV append
     GemmArgs a = gemm_base(c, m.qkv[l], c->ap_x);
+    a.fixed_rows = fixed_rows;
     a.ssq = ssq_in; a.ssq_groups = ssq_groups; a.eps = m.eps;
     a.qf = c->qf;
     a.q_dim = m.qd; a.kv_dim = m.kvd; a.head_dim = m.hd; a.n_kv = m.nkv;
@@ -440,6 +443,7 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     if (e != hipSuccess) break;
     // O projection + residual; packs x * ffn_norm for gate/up
     GemmArgs b = gemm_base(c, m.o[l], c->ap_o);
+    b.fixed_rows = fixed_rows;
     b.resid = c->x; b.ldr = m.d; b.gain_next = m.ffn_norm(l); b.Ap_out = c->ap_x;
     b.ssq_out = ssq_other;
     const bool stamp = profile && c->ts_next < c->ts_cap;
@@ -450,12 +454,14 @@ hipError_t enqueue_layers(spec_ctx* c, const Model& m, hipStream_t s, int n_rows
     ssq_groups = m.o[l].plan.workgroups();
     // RMSNorm + gate/up + SiLU*mul -> packed A of the down projection
     GemmArgs g = gemm_base(c, m.gu[l], c->ap_x);
+    g.fixed_rows = fixed_rows;
     g.ssq = ssq_in; g.ssq_groups = ssq_groups; g.eps = m.eps; g.Ap_out = c->ap_a;
     if (stamp) g.ts_end = c->ts + ((size_t)c->ts_next++ * 2 + 1) * c->ts_groups;
     e = launch_gemm(m.gu[l].plan.shape, EPI_SILU, g, s);
     if (e != hipSuccess) break;
     // down projection + residual; packs x * (next attn_norm or final norm)
     GemmArgs dn = gemm_base(c, m.dn[l], c->ap_a);
+    dn.fixed_rows = fixed_rows;
     dn.resid = c->x; dn.ldr = m.d; dn.Ap_out = c->ap_x; dn.ssq_out = ssq_other;
     dn.gain_next = l + 1 < m.L ? m.attn_norm(l + 1) : m.final_norm();
     if (stamp_last_down && l == m.L - 1) dn.ts_end = c->ts_head;
@@ -473,8 +479,9 @@ float* final_ssq(spec_ctx* c, const Model&) { return c->ssq_a; }
 
 // final norm + LM head (+ logits partials) + softmax into `dst`
 hipError_t enqueue_head(spec_ctx* c, const Model& m, hipStream_t s, int last_row_only, int n_rows,
-                        float* logits_dst, float* dst, bool stamp = false) {
+                        int fixed_rows, float* logits_dst, float* dst, bool stamp = false) {
   GemmArgs a = gemm_base(c, m.lm, c->ap_x);
+  a.fixed_rows = fixed_rows;
   if (stamp) a.ts_end = c->ts_head + c->ts_head_groups;
   a.ssq = final_ssq(c, m); a.ssq_groups = final_ssq_groups(m); a.eps = m.eps;
   a.last_row_only = last_row_only;
@@ -504,9 +511,9 @@ hipError_t enqueue_draft(spec_ctx* c, hipStream_t s, int K, uint64_t seed, int32
   for (int st = 0; st < K && e == hipSuccess; ++st) {
     e = enqueue_embed(c, m, s, st == 0 ? EMB_DRAFT0 : EMB_DRAFTS, 0, 0, st, d);
     // step 0 may carry catch-up rows; later steps have one row
-    if (e == hipSuccess) e = enqueue_layers(c, m, s, st == 0 ? kMaxRows : 1, c->profiling);
+    if (e == hipSuccess) e = enqueue_layers(c, m, s, st == 0 ? kMaxRows : 1, st == 0 ? 0 : 1, c->profiling);
     float* drow = Dp + (size_t)st * m.V;
-    if (e == hipSuccess) e = enqueue_head(c, m, s, 1, 1, c->logits, drow);
+    if (e == hipSuccess) e = enqueue_head(c, m, s, 1, 1, st == 0 ? 0 : 1, c->logits, drow);
     if (e == hipSuccess) {
       ArArgs ar{};
       ar.T = drow; ar.D = nullptr; ar.d = d; ar.B = 1; ar.K = 0; ar.V = m.V;
@@ -526,8 +533,8 @@ hipError_t enqueue_verify(spec_ctx* c, hipStream_t s, int K, uint64_t seed, cons
   float* Tb = Tdst ? Tdst : c->Tbuf;
   float* Lb = Ldst ? Ldst : c->logits;
   hipError_t e = enqueue_embed(c, m, s, EMB_VERIFY, K + 1, 0, 0, d);
-  if (e == hipSuccess) e = enqueue_layers(c, m, s, K + 1, c->profiling, c->profiling);
-  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, K + 1, Lb, Tb, c->profiling);
+  if (e == hipSuccess) e = enqueue_layers(c, m, s, K + 1, K + 1, c->profiling, c->profiling);
+  if (e == hipSuccess) e = enqueue_head(c, m, s, 0, K + 1, K + 1, Lb, Tb, c->profiling);
   if (e == hipSuccess) {
     ArArgs ar{};
     ar.T = Tb; ar.D = Dp; ar.d = d; ar.B = 1; ar.K = K; ar.V = m.V;
@@ -628,7 +635,7 @@ int prefill(spec_ctx* c, const Model& m, int pos0, int n) {
   for (int p = pos0; p < pos0 + n; p += kMaxRows) {
     const int cnt = std::min(kMaxRows, pos0 + n - p);
     HIPTRY(c, enqueue_embed(c, m, c->stream, EMB_PREFILL, cnt, p, 0, nullptr));
-    HIPTRY(c, enqueue_layers(c, m, c->stream, kMaxRows, false));
+    HIPTRY(c, enqueue_layers(c, m, c->stream, kMaxRows, 0, false));
   }
   return SPEC_OK;
 }
