@@ -27,8 +27,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 # HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE) of this script, with the hash of the kernel sources
-# they were taken with; used only while the sources still hash the same.
+# (FETCH_SIZE, WRITE_SIZE) of the native driver spec_run on the 8B-shaped pair
+# at K = 4, with the hash of the kernel sources they were taken with; used only
+# for that workload and while the sources still hash the same.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_8b_k4_traffic.txt")
 KERNEL_SOURCES = ("k_gemm.hip", "k_gemm.h", "common.h")  # the GEMM kernels and their launch plans
 COPY_CALIB_BYTES = 1 << 30
@@ -281,7 +282,10 @@ def main():
         avg_bytes = (b_d + b_t) / n_l
         avg_ms = float((kt_d.sum() + kt_t.sum()) / n_l)
         ach = avg_bytes / (avg_ms / 1e3) / 1e9
-        traffic, traffic_note = measured_traffic(target_only=len(kt_d) == 0)
+        if args.pair == "8b" and (K == 4 or len(kt_d) == 0):
+            traffic, traffic_note = measured_traffic(target_only=len(kt_d) == 0)
+        else:  # the counters were taken on the 8B-shaped pair's K = 4 launch mix
+            traffic, traffic_note = None, "counters cover the 8B-shaped pair at K = 4 only"
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "traffic_note": traffic_note,
