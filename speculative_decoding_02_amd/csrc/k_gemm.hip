@@ -177,11 +177,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const PassRows* rows, cons
   // that is faster, see kPeel).
   uint4 av0[U], wv0[U][NB];
   // Issuing the first batch ahead of the prologue was measured per instance
-  // (rocprofv3, same box, graph-replayed rounds): it shortens the half-block,
-  // the four-and-more-block and the one-block QKV launches by 0.15-0.5 us and
-  // lengthens the whole-block residual launches with one block (8B-shaped O
-  // and down, +2.2 us) and the two-block QKV (+0.4 us), which therefore issue
-  // it in the loop as before.
+  // (rocprofv3 kernel traces of graph-replayed rounds): it shortens the
+  // half-block, the four-and-more-block and the one-block QKV launches by
+  // 0.15-0.5 us and lengthens the whole-block residual launches with one block
+  // (8B-shaped O and down, +2.2 us) and the two-block QKV (+0.4 us), which
+  // therefore issue it in the loop as before.
   constexpr bool kPeel = HALF || NB >= 4 || (EPI == EPI_QKV && NB == 1);
   const bool peel = kPeel && kb0 + U <= kb1;  // wave-uniform
   if (peel) load_batch(std::integral_constant<int, U>{}, kb0, av0, wv0);
