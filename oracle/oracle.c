@@ -11,8 +11,11 @@
  *
  * Parity status of each part is stated at its definition:
  *   Philox, fix, sample_icdf, argmax_low, accept, verify_* -- pinned.
- *   Model forward -- parity unpinned against the pages (the pages give no
- *   model equations); checked only by invariants and special cases.
+ *   Model forward -- the pages give no model equations, so it is pinned by
+ *   the mathematics: invariants (causality, row invariance, GQA as MHA with
+ *   repeated KV heads) and special cases of the whole pass computed another
+ *   way (RoPE as complex rotation, scipy softmax and expit), which sixteen
+ *   planted mistakes each fail.
  */
 #include "oracle.h"
 
@@ -297,11 +300,12 @@ uint64_t orc_accept_count(float T, float D) {
 }
 
 /* ======================================================================= */
-/* Model forward (fp64).  Parity unpinned against the pages: they name a     */
-/* "forward pass" that yields a next-token distribution at every position   */
-/* ([en] Floor 3) but give no equations.  The decoder below is the standard */
-/* Llama-style pre-norm block: RMSNorm, rotate-half RoPE, causal GQA         */
-/* attention, SwiGLU FFN, final RMSNorm, untied LM head, softmax at T = 1.   */
+/* Model forward (fp64).  The pages name a "forward pass" that yields a     */
+/* next-token distribution at every position ([en] Floor 3) but give no     */
+/* equations.  The decoder below is the standard Llama-style pre-norm       */
+/* block: RMSNorm, rotate-half RoPE, causal GQA attention, SwiGLU FFN,      */
+/* final RMSNorm, untied LM head, softmax at T = 1; its pins are those of   */
+/* the mathematics (header above).                                          */
 /* ======================================================================= */
 static double bf16_to_f64(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;

@@ -1,7 +1,7 @@
-"""Pins for the oracle's model forward.  The pages give no model equations
-(parity against them is unpinned), so the forward is held to invariants and
-to special cases that reduce to library routines (numpy matmul, scipy
-softmax/expit):
+"""Pins for the oracle's model forward.  The pages give no model equations,
+so the forward is held to invariants and to special cases that reduce to
+library routines (numpy matmul, scipy softmax/expit); the whole-pass special
+cases and the planted mistakes are in test_oracle_forward_pins.py:
   - RoPE: identity at position 0, a rotation (norm-preserving, composes
     additively in position), scores depend only on relative position;
   - RMSNorm: closed form on constant vectors, scale invariance;
