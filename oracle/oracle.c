@@ -15,7 +15,8 @@
  *   the mathematics: invariants (causality, row invariance, GQA as MHA with
  *   repeated KV heads) and special cases of the whole pass computed another
  *   way (RoPE as complex rotation, scipy softmax and expit), which sixteen
- *   planted mistakes each fail.
+ *   planted mistakes each fail (as fifteen planted in the rule, the sampler
+ *   and Philox each fail their pins).
  */
 #include "oracle.h"
 

@@ -1,4 +1,4 @@
-"""Model-level pins of the oracle's forward pass, and planted mistakes.
+"""Model-level pins of the oracle's forward pass.
 
 The pages name a forward pass that gives a next-token distribution at every
 position ([en] Floor 3) but print no model equations, so the oracle's
@@ -9,16 +9,9 @@ scaled dot-product attention with scipy's softmax, SiLU through scipy's
 expit -- with norm gains and query/key scales drawn at random so that a
 gain on the wrong vector or a flat softmax cannot hide a mistake.
 
-The last test plants plausible mistakes in copies of oracle/oracle.c (the
-attention scale, RoPE on the wrong vector or position, the causal window,
-the GQA head mapping, each residual, the SiLU operand, the RMSNorm epsilon
-and gains, the LM head's input, ...) and checks that each mutant fails at
-least one of the model pins (this file and test_oracle_model.py)."""
-import concurrent.futures
-import os
-import subprocess
-import sys
-
+test_oracle_planted_mistakes.py plants plausible mistakes in copies of the
+oracle and checks that each fails one of these pins or those of
+test_oracle_model.py."""
 import numpy as np
 import pytest
 from scipy import special
@@ -26,7 +19,6 @@ from scipy import special
 import oracle
 import synth
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CFG1 = synth.ModelConfig("fwd-pin-1L", 1, 64, 4, 2, 16, 96, 40, rope_theta=10000.0)
 CFG2 = synth.ModelConfig("fwd-pin-2L", 2, 64, 4, 2, 16, 96, 40, rope_theta=500.0)
 
@@ -121,72 +113,3 @@ def test_attention_is_not_flat():
     toks = synth.prompt(CFG1.vocab, 5, seed=31)
     flat = _forward_numpy(CFG1, dict(w, wq=np.zeros_like(w["wq"])), toks, ffn=False)
     assert np.abs(_forward_numpy(CFG1, w, toks, ffn=False) - flat).max() > 1e-3
-
-
-# (pattern, replacement, occurrence) -- applied to a copy of oracle.c
-_ROPE_Q = ("for (int32_t hh = 0; hh < H; hh++) rope_head(q + (size_t)r * qd + (size_t)hh * hd, hd, "
-           "pos, m->rope_theta);")
-_ROPE_K = ("for (int32_t hh = 0; hh < Hkv; hh++) rope_head(k + (size_t)r * kvd + (size_t)hh * hd, "
-           "hd, pos, m->rope_theta);")
-_RESID = "for (size_t i = 0; i < (size_t)n * d; i++) x[i] += y[i];"
-MUTANTS = {
-    "attention scale 1/hd": ("const double scale = 1.0 / sqrt((double)hd);",
-                             "const double scale = 1.0 / (double)hd;", 0),
-    "attention weights unnormalised": ("const double p = sc[t] / den;", "const double p = sc[t];", 0),
-    "values read from the keys": ("const double* vt = vbase", "const double* vt = kbase", 0),
-    "no RoPE on keys": (_ROPE_K, "", 0),
-    "RoPE on values too": (_ROPE_K, _ROPE_K + _ROPE_K.replace("rope_head(k", "rope_head(v"), 0),
-    "queries rotated one position late": (_ROPE_Q, _ROPE_Q.replace("hd, pos,", "hd, pos + 1,"), 0),
-    "RoPE exponent -j/hd": ("pow(theta, -2.0 * (double)j / (double)hd)",
-                            "pow(theta, -(double)j / (double)hd)", 0),
-    "non-causal window": ("(size_t)Hkv * hd, pos + 1, hd,", "(size_t)Hkv * hd, pos0 + n, hd,", 0),
-    "GQA head mapping hh % Hkv": ("const int32_t kh = (int32_t)(((int64_t)hh * Hkv) / H);",
-                                  "const int32_t kh = hh % Hkv;", 0),
-    "attention residual dropped": (_RESID, _RESID.replace("x[i] += y[i]", "x[i] = y[i]"), 0),
-    "feed-forward residual dropped": (_RESID, _RESID.replace("x[i] += y[i]", "x[i] = y[i]"), 1),
-    "SiLU on the up projection": ("g[i] = silu(g[i]) * u[i];", "g[i] = g[i] * silu(u[i]);", 0),
-    "RMSNorm epsilon outside the root": ("double inv = 1.0 / sqrt(ss / (double)d + eps);",
-                                         "double inv = 1.0 / (sqrt(ss / (double)d) + eps);", 0),
-    "RMSNorm gain dropped": ("h[k] = x[k] * inv * bf16_to_f64(g[k]);", "h[k] = x[k] * inv;", 0),
-    "final norm with the attention gains": ("rmsnorm_row(x + (size_t)r * d, d, m->final_norm,",
-                                            "rmsnorm_row(x + (size_t)r * d, d, m->attn_norm,", 0),
-    "LM head on the un-normed state": ("if (logits) matmul_rows(h, n, d, m->lm_head, V, logits);",
-                                       "if (logits) matmul_rows(x, n, d, m->lm_head, V, logits);", 0),
-}
-
-
-def _mutate(src, pattern, repl, occurrence):
-    parts = src.split(pattern)
-    assert len(parts) > occurrence + 1, f"pattern not found (occurrence {occurrence}): {pattern}"
-    return pattern.join(parts[:occurrence + 1]) + repl + pattern.join(parts[occurrence + 1:])
-
-
-def _build_and_run(name, src, tmp):
-    path = os.path.join(tmp, name.replace(" ", "_").replace("/", "_"))
-    os.makedirs(path, exist_ok=True)
-    c_file, so = os.path.join(path, "oracle.c"), os.path.join(path, "liboracle.so")
-    with open(c_file, "w") as fh:
-        fh.write(src)
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-                    "-fPIC", "-shared", "-I", os.path.join(ROOT, "oracle"), c_file, "-o", so, "-lm"],
-                   check=True, capture_output=True)
-    env = dict(os.environ, SPEC_ORACLE_LIB=so, OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "-m", "not gpu", "-k", "not planted",
-                        os.path.join(ROOT, "tests", "test_oracle_model.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_forward_pins.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    return r.returncode
-
-
-def test_planted_mistakes_fail_a_pin(tmp_path):
-    with open(os.path.join(ROOT, "oracle", "oracle.c")) as fh:
-        src = fh.read()
-    mutants = {name: _mutate(src, *spec) for name, spec in MUTANTS.items()}
-    assert all(m != src for m in mutants.values())
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        futs = {name: ex.submit(_build_and_run, name, m, str(tmp_path)) for name, m in mutants.items()}
-        rcs = {name: f.result() for name, f in futs.items()}
-    survivors = [name for name, rc in rcs.items() if rc == 0]
-    assert not survivors, f"planted mistakes no pin catches: {survivors}"
-    assert all(rc == 1 for rc in rcs.values()), rcs  # failed tests, not a crash or usage error
